@@ -1,0 +1,262 @@
+#!/usr/bin/env python3
+"""Benchmark of the block-scaled FP8 linear-layer path on one MI355X.
+
+One step = the whole hot path of a training-step linear layer (Qwen3-8B
+down_proj shape, X [8192 x 12288], W [4096 x 12288], dY [8192 x 4096], all
+bf16, seeded synthetic data) on the GPU:
+    128x128 weight quantization (+ transposed codes)        R2
+    dual 1x128 quantization of X  (row-wise + token-axis)   R1 + R3
+    FProp  Y  = X W^T                                        R4
+    dual 1x128 quantization of dY (row-wise + token-axis)   R1 + R3
+    DGrad  dX = dY W                                         R5
+    WGrad  dW = dY^T X                                       R6
+value = 3 * 2*N*D*C FLOP / step time (TFLOP/s), inputs resident in HBM.
+Two copies of every input alternate between steps so nothing is reused
+from the 256 MB Infinity Cache across steps.
+
+Printed JSON line: the contract fields, a per-kernel breakdown (HIP-event
+time per launch on the launch stream, TFLOP/s or GB/s, fraction of the
+MI355X peak), the roofline of the dominant kernel, a bf16 hipBLASLt
+baseline on the same GEMM shapes, and the CPU oracle timed on a bounded
+sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_FP8_TFLOPS = 5000.0      # MI355X dense FP8 MFMA
+PEAK_BF16_TFLOPS = 2500.0     # MI355X dense BF16 MFMA
+PEAK_HBM_GBS = 8000.0         # MI355X HBM3E
+
+METRIC = "block-scaled FP8 GEMM TFLOPS (FProp/DGrad/WGrad) + quantize GB/s, % of peak"
+N, C, D = 8192, 12288, 4096
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0,
+                    help="rough CPU budget of the oracle baseline sample")
+    return ap.parse_args()
+
+
+def src_sha(*names):
+    h = hashlib.sha256()
+    for n in names:
+        with open(os.path.join(ROOT, "block_scaled_fp8_02_amd", "csrc", n), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def algorithmic_bytes():
+    """Bytes each kernel must move at minimum (inputs once, outputs once)."""
+    g = (C + 127) // 128
+    gd = (D + 127) // 128
+    gn = (N + 127) // 128
+    return {
+        "quant_weight": D * C * 2 + D * C * 2 + gd * g * 4,            # bf16 in, q + qT, scales
+        "quant_dual_X": N * C * 2 + 2 * N * C + N * g * 4 + C * gn * 4,
+        "quant_dual_dY": N * D * 2 + 2 * N * D + N * gd * 4 + D * gn * 4,
+        "fprop": N * C + D * C + N * g * 4 + gd * g * 4 + N * D * 2,
+        "dgrad": N * D + C * D + N * gd * 4 + gd * g * 4 + N * C * 2,
+        "wgrad": D * N + C * N + D * gn * 4 + C * gn * 4 + D * C * 2,
+    }
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
+              f"(this build runs on a single MI355X).", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import block_scaled_fp8_02_amd as fb
+    from block_scaled_fp8_02_amd import workloads as wl
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    t0 = time.time()
+    w = wl.train(args.seed)
+    print(f"[bench] inputs drawn in {time.time() - t0:.1f}s", file=sys.stderr, flush=True)
+
+    def to_dev(bits):
+        return torch.from_numpy(bits).view(torch.bfloat16).to(dev)
+
+    copies = []
+    for k in range(2):
+        Xd, Wd, Gd = to_dev(w["X"]), to_dev(w["W"]), to_dev(w["dY"])
+        copies.append((Xd, Wd, Gd))
+    # preallocated outputs (allocation is outside the timed region)
+    cdiv = lambda a, b: (a + b - 1) // b
+    u8 = dict(dtype=torch.uint8, device=dev)
+    f32 = dict(dtype=torch.float32, device=dev)
+    bufs = dict(
+        wq=torch.empty((D, C), **u8), ws=torch.empty((cdiv(D, 128), cdiv(C, 128)), **f32),
+        wqT=torch.empty((C, D), **u8),
+        xq=torch.empty((N, C), **u8), xs=torch.empty((N, cdiv(C, 128)), **f32),
+        xqT=torch.empty((C, N), **u8), xsT=torch.empty((C, cdiv(N, 128)), **f32),
+        gq=torch.empty((N, D), **u8), gs=torch.empty((N, cdiv(D, 128)), **f32),
+        gqT=torch.empty((D, N), **u8), gsT=torch.empty((D, cdiv(N, 128)), **f32),
+        y=torch.empty((N, D), dtype=torch.bfloat16, device=dev),
+        dx=torch.empty((N, C), dtype=torch.bfloat16, device=dev),
+        dw=torch.empty((D, C), dtype=torch.bfloat16, device=dev),
+    )
+    b = bufs
+    names = ["quant_weight", "quant_dual_X", "fprop", "quant_dual_dY", "dgrad", "wgrad"]
+    events = {n: [] for n in names}
+
+    def step(i, record):
+        Xd, Wd, Gd = copies[i % 2]
+        ev = []
+
+        def mark():
+            if record:
+                e = torch.cuda.Event(enable_timing=True)
+                e.record()
+                ev.append(e)
+        mark()
+        fb.fp8_quantize_weight_128x128(Wd, transpose=True, q=b["wq"], s=b["ws"], qT=b["wqT"])
+        mark()
+        fb.fp8_quantize_transposed(Xd, rowwise=True, qT=b["xqT"], sT=b["xsT"], q=b["xq"], s=b["xs"])
+        mark()
+        fb.fp8_gemm_fprop(b["xq"], b["xs"], b["wq"], b["ws"], N, D, C, y=b["y"])
+        mark()
+        fb.fp8_quantize_transposed(Gd, rowwise=True, qT=b["gqT"], sT=b["gsT"], q=b["gq"], s=b["gs"])
+        mark()
+        fb.fp8_gemm_dgrad(b["gq"], b["gs"], b["wqT"], b["ws"], N, D, C, dx=b["dx"])
+        mark()
+        fb.fp8_gemm_wgrad(b["gqT"], b["gsT"], b["xqT"], b["xsT"], N, D, C, dw=b["dw"])
+        mark()
+        return ev
+
+    for i in range(args.warmup):
+        step(i, False)
+    torch.cuda.synchronize()
+    all_ev = []
+    t_start = time.perf_counter()
+    for i in range(args.steps):
+        all_ev.append(step(i, True))
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t_start
+    for ev in all_ev:
+        for k, n in enumerate(names):
+            events[n].append(ev[k].elapsed_time(ev[k + 1]) * 1e-3)   # seconds
+
+    flops_gemm = 2.0 * N * D * C
+    abytes = algorithmic_bytes()
+    kernels = {}
+    for n in names:
+        t = float(np.mean(events[n]))
+        ent = {"us": round(t * 1e6, 2), "us_min": round(float(np.min(events[n])) * 1e6, 2)}
+        if n in ("fprop", "dgrad", "wgrad"):
+            tf = flops_gemm / t / 1e12
+            ent.update(tflops=round(tf, 1), frac_fp8_peak=round(tf / PEAK_FP8_TFLOPS, 4))
+        gbs = abytes[n] / t / 1e9
+        ent.update(alg_bytes=abytes[n], gbs=round(gbs, 1), frac_hbm=round(gbs / PEAK_HBM_GBS, 4))
+        kernels[n] = ent
+    step_s = elapsed / args.steps
+    value = 3 * flops_gemm / step_s / 1e12
+
+    dom = max(("fprop", "dgrad", "wgrad"), key=lambda n: kernels[n]["us"])
+    t_dom = kernels[dom]["us"] * 1e-6
+    achieved = flops_gemm / t_dom / 1e12
+    traffic = None
+    tfile = os.path.join(ROOT, "profiles", "traffic_gemm_train.json")
+    if os.path.exists(tfile):
+        tj = json.load(open(tfile))
+        if tj.get("src_sha") == src_sha("gemm.hip") and dom in tj.get("kernels", {}):
+            traffic = tj["kernels"][dom]["bytes_per_launch"]
+    roofline = {"bound": "mfma", "kernel": dom, "achieved": round(achieved, 1),
+                "peak": PEAK_FP8_TFLOPS, "unit": "TFLOP/s", "frac": round(achieved / PEAK_FP8_TFLOPS, 4),
+                "traffic": traffic, "alg_bytes": abytes[dom]}
+
+    # bf16 hipBLASLt baseline on the same three GEMM shapes
+    Xd, Wd, Gd = copies[0]
+    bf = {}
+    for name, fn in (("fprop", lambda: torch.matmul(Xd, Wd.t())),
+                     ("dgrad", lambda: torch.matmul(Gd, Wd)),
+                     ("wgrad", lambda: torch.matmul(Gd.t(), Xd))):
+        for _ in range(3):
+            fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        reps = 10
+        e0.record()
+        for _ in range(reps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        t = e0.elapsed_time(e1) * 1e-3 / reps
+        tf = flops_gemm / t / 1e12
+        bf[name] = {"us": round(t * 1e6, 1), "tflops": round(tf, 1), "frac_bf16_peak": round(tf / PEAK_BF16_TFLOPS, 4)}
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(w, args.cpu_seconds)
+
+    out = {
+        "metric": METRIC, "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(step_s * 1e3, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "fp8e4m3 (fp32 accumulate)", "data": "synthetic",
+        "config": {"workload": "training-step linear layer, Qwen3-8B down_proj shape: X bf16 [8192x12288] "
+                               "(1% outlier channels x50), W bf16 [4096x12288], dY bf16 [8192x4096]; "
+                               "1x128 act/grad + 128x128 weight FP8 path, FProp+DGrad+WGrad",
+                   "N": N, "C": C, "D": D, "seed": args.seed, "inputs_resident_in_hbm": True},
+        "kernels": kernels, "roofline": roofline, "bf16_baseline": bf, "cpu_baseline": cpu,
+    }
+    print(json.dumps(out), flush=True)
+
+
+def cpu_baseline(w, budget_s: float):
+    """The oracle as it stands (plain C, fp32 quantizers, fp64 GEMMs) on a
+    bounded sample of the same workload: all of W quantized 128x128, then
+    `rows` sampled token rows through the 1x128 quantizer and FProp/DGrad,
+    and `rows` sampled dW rows through the token-axis quantizer and WGrad.
+    Reported in TFLOP/s of GEMM work per second of the sampled pipeline."""
+    import oracle
+    threads = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
+    rng = np.random.default_rng(99)
+    rows = 16
+    t0 = time.perf_counter()
+    while True:
+        ridx = np.sort(rng.choice(N, rows, replace=False))
+        didx = np.sort(rng.choice(D, rows, replace=False))
+        ts = time.perf_counter()
+        wq, ws, _ = oracle.quant_128x128(w["W"], with_transpose=False)
+        xq, xs = oracle.quant_1x128(w["X"][ridx])
+        oracle.fprop(xq, xs, wq, ws, C)
+        gq, gs = oracle.quant_1x128(w["dY"][ridx])
+        oracle.dgrad(gq, gs, wq, ws, D, C)
+        gqT, gsT = oracle.quant_colwise(np.ascontiguousarray(w["dY"][:, didx]))
+        xqT, xsT = oracle.quant_colwise(w["X"])
+        oracle.wgrad(gqT, gsT, xqT, xsT, N)
+        dt = time.perf_counter() - ts
+        if dt > budget_s / 3 or time.perf_counter() - t0 > budget_s or rows >= 256:
+            break
+        rows *= 2
+    flops = 2.0 * rows * D * C + 2.0 * rows * C * D + 2.0 * rows * C * N
+    return {"value": round(flops / dt / 1e12, 6), "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+            "seconds": round(dt, 2),
+            "sample": f"W quantized 128x128 in full; {rows} token rows of X and dY through 1x128 "
+                      f"quantization and FProp/DGrad; X and {rows} columns of dY through token-axis "
+                      f"quantization and {rows} rows of WGrad (fp64 GEMMs)"}
+
+
+if __name__ == "__main__":
+    main()

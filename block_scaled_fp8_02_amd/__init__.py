@@ -1,0 +1,330 @@
+"""Python binding of libfp8blk.so (the block-scaled FP8 linear-layer path
+on MI355X / gfx950).
+
+Argument marshalling only: every function has the name of the C entry
+point it wraps (see include/fp8blk.h), takes torch tensors that already
+live on the GPU, allocates missing outputs with torch, and launches on the
+current torch stream.  All arithmetic happens in the HIP kernels.  There is
+no fallback: if the library is not built or a call fails, an exception is
+raised.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libfp8blk.so")
+
+FP8B_F32 = 0
+FP8B_BF16 = 1
+_STATUS = {0: "ok", 1: "invalid argument", 2: "invalid shape", 3: "misaligned",
+           4: "unsupported", 5: "HIP launch error"}
+
+_i64 = ctypes.c_int64
+_i32 = ctypes.c_int
+_p = ctypes.c_void_p
+_lib = None
+
+
+class Fp8bError(RuntimeError):
+    def __init__(self, fn: str, status: int, hip_err: int = 0):
+        msg = f"{fn} failed: {_STATUS.get(status, status)} (status {status})"
+        if status == 5:
+            msg += f", hip error {hip_err}"
+        super().__init__(msg)
+        self.status = status
+
+
+_SIGS = {
+    "fp8_quantize_act_1x128": [_p, _i32, _i64, _i64, _i64, _p, _i64, _p, _i64, _p],
+    "fp8_quantize_weight_128x128": [_p, _i32, _i64, _i64, _i64, _p, _i64, _p, _i64, _p, _i64, _p],
+    "fp8_quantize_transposed": [_p, _i32, _i64, _i64, _i64, _p, _i64, _p, _i64, _p, _i64, _p, _i64, _p],
+    "fp8_quantize_transposed_grouped": [_p, _i32, _i64, _i64, _i64, _p, _i64, _p, _i64, _p, _i64,
+                                        _p, _i64, _p, _i64, _p],
+    "fp8_gemm_fprop": [_p, _i64, _p, _i64, _p, _i64, _p, _i64, _p, _i32, _i64, _i64, _i64, _i64, _p],
+    "fp8_gemm_dgrad": [_p, _i64, _p, _i64, _p, _i64, _p, _i64, _p, _i32, _i64, _i64, _i64, _i64, _p],
+    "fp8_gemm_wgrad": [_p, _i64, _p, _i64, _p, _i64, _p, _i64, _p, _i32, _i64, _i32, _i64, _i64, _i64, _p],
+    "fp8_gemm_fprop_grouped": [_p, _i64, _p, _i64, _p, _i64, _i64, _p, _i64, _i64, _p, _i32, _i64,
+                               _p, _i64, _i64, _i64, _i64, _p],
+    "fp8_gemm_dgrad_grouped": [_p, _i64, _p, _i64, _p, _i64, _i64, _p, _i64, _i64, _p, _i32, _i64,
+                               _p, _i64, _i64, _i64, _i64, _p],
+    "fp8_gemm_wgrad_grouped": [_p, _i64, _p, _i64, _p, _i64, _p, _i64, _p, _i32, _i64, _i64, _i32,
+                               _p, _i64, _i64, _i64, _i64, _p],
+    "fp8_mx_quantize_1x32": [_p, _i32, _i64, _i64, _i64, _p, _i64, _p, _i64, _p, _i64, _p, _i64, _p],
+    "fp8_mx_gemm_fprop": [_p, _i64, _p, _i64, _p, _i64, _p, _i64, _p, _i32, _i64, _i64, _i64, _i64, _p],
+    "fp8_mx_gemm_dgrad": [_p, _i64, _p, _i64, _p, _i64, _p, _i64, _p, _i32, _i64, _i64, _i64, _i64, _p],
+    "fp8_mx_gemm_wgrad": [_p, _i64, _p, _i64, _p, _i64, _p, _i64, _p, _i32, _i64, _i32, _i64, _i64, _i64, _p],
+    "fp8b_e4m3_encode": [_p, _p, _i64, _p, _p],
+    "fp8b_validate_gemm": [_i32, _p, _i64, _p, _i64, _p, _i64, _p, _i64, _p, _i32, _i64, _i32,
+                           _i64, _i64, _i64],
+    "fp8b_abi_version": [],
+    "fp8b_status_string": [_i32],
+    "fp8b_last_hip_error": [],
+}
+EXPORTS = tuple(_SIGS)
+
+
+def lib():
+    """Load libfp8blk.so (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with "
+                               f"`python -m block_scaled_fp8_02_amd.build` (hipcc, gfx950)")
+        L = ctypes.CDLL(LIB_PATH)
+        for name, args in _SIGS.items():
+            fn = getattr(L, name)
+            fn.argtypes = args
+            fn.restype = ctypes.c_char_p if name == "fp8b_status_string" else ctypes.c_int
+        _lib = L
+    return _lib
+
+
+def _call(name: str, *args):
+    st = getattr(lib(), name)(*args)
+    if st != 0:
+        raise Fp8bError(name, st, lib().fp8b_last_hip_error())
+
+
+def _rup(n: int, m: int = 128) -> int:
+    return (n + m - 1) // m * m
+
+
+def _cdiv(n: int, m: int) -> int:
+    return (n + m - 1) // m
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(dev):
+    return ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.bfloat16:
+        return FP8B_BF16
+    if t.dtype == torch.float32:
+        return FP8B_F32
+    raise TypeError(f"unsupported dtype {t.dtype}; expected bfloat16 or float32")
+
+
+def _out_dtype_code(dt: torch.dtype) -> int:
+    return FP8B_BF16 if dt == torch.bfloat16 else FP8B_F32
+
+
+def _check_2d(t, name):
+    if t.dim() != 2 or (t.shape[1] > 1 and t.stride(1) != 1):
+        raise ValueError(f"{name} must be a row-major 2-D tensor")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor")
+
+
+def _ld(t):
+    return t.stride(0) if t.shape[0] > 0 else max(t.shape[1], 1)
+
+
+def _new(shape, dtype, dev):
+    return torch.empty(shape, dtype=dtype, device=dev)
+
+
+def _new_out(rows: int, cols: int, dtype, dev):
+    """Output matrix whose row stride is a multiple of 16 bytes (the
+    kernels store 8- and 16-byte vectors)."""
+    per16 = 16 // torch.tensor([], dtype=dtype).element_size()
+    ld = max(_rup(cols, per16), per16)
+    return torch.empty((rows, ld), dtype=dtype, device=dev)[:, :cols]
+
+
+# ----------------------------------------------------------- quantizers
+def fp8_quantize_act_1x128(x, q=None, s=None):
+    """1x128 quantization along the last axis -> (q uint8 [rows, rup(cols)],
+    s float32 [rows, ceil(cols/128)])."""
+    _check_2d(x, "x")
+    rows, cols = x.shape
+    q = _new((rows, _rup(cols)), torch.uint8, x.device) if q is None else q
+    s = _new((rows, _cdiv(cols, 128)), torch.float32, x.device) if s is None else s
+    _call("fp8_quantize_act_1x128", _ptr(x), _dtype_code(x), rows, cols, _ld(x),
+          _ptr(q), _ld(q), _ptr(s), _ld(s), _stream(x.device))
+    return q, s
+
+
+def fp8_quantize_weight_128x128(w, transpose: bool = True, q=None, s=None, qT=None):
+    """128x128 block quantization -> (q [D, rup(C)], s [ceil(D/128),
+    ceil(C/128)], qT [C, rup(D)] or None)."""
+    _check_2d(w, "w")
+    D, C = w.shape
+    q = _new((D, _rup(C)), torch.uint8, w.device) if q is None else q
+    s = _new((_cdiv(D, 128), _cdiv(C, 128)), torch.float32, w.device) if s is None else s
+    if transpose and qT is None:
+        qT = _new((C, _rup(D)), torch.uint8, w.device)
+    _call("fp8_quantize_weight_128x128", _ptr(w), _dtype_code(w), D, C, _ld(w),
+          _ptr(q), _ld(q), _ptr(s), _ld(s), _ptr(qT), _ld(qT) if qT is not None else 0,
+          _stream(w.device))
+    return q, s, qT
+
+
+def fp8_quantize_transposed(x, rowwise: bool = False, qT=None, sT=None, q=None, s=None):
+    """1x128 along the token axis, transposed -> (qT [cols, rup(rows)],
+    sT [cols, ceil(rows/128)], q, s) with q, s the row-wise copy or None."""
+    _check_2d(x, "x")
+    rows, cols = x.shape
+    qT = _new((cols, _rup(rows)), torch.uint8, x.device) if qT is None else qT
+    sT = _new((cols, _cdiv(rows, 128)), torch.float32, x.device) if sT is None else sT
+    if rowwise and q is None:
+        q = _new((rows, _rup(cols)), torch.uint8, x.device)
+        s = _new((rows, _cdiv(cols, 128)), torch.float32, x.device)
+    _call("fp8_quantize_transposed", _ptr(x), _dtype_code(x), rows, cols, _ld(x),
+          _ptr(qT), _ld(qT), _ptr(sT), _ld(sT),
+          _ptr(q), _ld(q) if q is not None else 0, _ptr(s), _ld(s) if s is not None else 0,
+          _stream(x.device))
+    return qT, sT, q, s
+
+
+def grouped_token_capacity(rows: int, E: int) -> int:
+    """Row length of the grouped transposed layout: round_up(rows + 128*E)."""
+    return _rup(rows + 128 * E)
+
+
+def fp8_quantize_transposed_grouped(x, offsets, rowwise: bool = False, qT=None, sT=None, q=None, s=None):
+    """Grouped (MoE) transposed quantization; offsets is a device int32
+    tensor [E+1].  qT is [cols, round_up(rows + 128E)] (columns past each
+    expert's padded span are not written)."""
+    _check_2d(x, "x")
+    rows, cols = x.shape
+    E = offsets.numel() - 1
+    P = grouped_token_capacity(rows, E)
+    qT = _new((cols, P), torch.uint8, x.device) if qT is None else qT
+    sT = _new((cols, P // 128), torch.float32, x.device) if sT is None else sT
+    if rowwise and q is None:
+        q = _new((rows, _rup(cols)), torch.uint8, x.device)
+        s = _new((rows, _cdiv(cols, 128)), torch.float32, x.device)
+    _call("fp8_quantize_transposed_grouped", _ptr(x), _dtype_code(x), rows, cols, _ld(x),
+          _ptr(offsets), E, _ptr(qT), _ld(qT), _ptr(sT), _ld(sT),
+          _ptr(q), _ld(q) if q is not None else 0, _ptr(s), _ld(s) if s is not None else 0,
+          _stream(x.device))
+    return qT, sT, q, s
+
+
+# ---------------------------------------------------------------- GEMMs
+def fp8_gemm_fprop(xq, xs, wq, ws, N, D, C, y=None, out_dtype=torch.bfloat16):
+    y = _new_out(N, D, out_dtype, xq.device) if y is None else y
+    _call("fp8_gemm_fprop", _ptr(xq), _ld(xq), _ptr(xs), _ld(xs), _ptr(wq), _ld(wq), _ptr(ws), _ld(ws),
+          _ptr(y), _out_dtype_code(y.dtype), _ld(y), N, D, C, _stream(xq.device))
+    return y
+
+
+def fp8_gemm_dgrad(gq, gs, wqT, ws, N, D, C, dx=None, out_dtype=torch.bfloat16):
+    dx = _new_out(N, C, out_dtype, gq.device) if dx is None else dx
+    _call("fp8_gemm_dgrad", _ptr(gq), _ld(gq), _ptr(gs), _ld(gs), _ptr(wqT), _ld(wqT), _ptr(ws), _ld(ws),
+          _ptr(dx), _out_dtype_code(dx.dtype), _ld(dx), N, D, C, _stream(gq.device))
+    return dx
+
+
+def fp8_gemm_wgrad(gqT, gsT, xqT, xsT, N, D, C, dw=None, out_dtype=torch.bfloat16, beta: int = 0):
+    dw = _new_out(D, C, out_dtype, gqT.device) if dw is None else dw
+    _call("fp8_gemm_wgrad", _ptr(gqT), _ld(gqT), _ptr(gsT), _ld(gsT), _ptr(xqT), _ld(xqT),
+          _ptr(xsT), _ld(xsT), _ptr(dw), _out_dtype_code(dw.dtype), _ld(dw), beta, N, D, C,
+          _stream(gqT.device))
+    return dw
+
+
+def fp8_gemm_fprop_grouped(xq, xs, wq, wq_estride, ws, ws_estride, offsets, N, D, C, y=None,
+                           out_dtype=torch.bfloat16, ldwq=None, ldws=None):
+    """wq/ws hold all experts (e.g. stacked [E*D, C] from one R2 call);
+    ldwq/ldws default to their row strides."""
+    y = _new_out(N, D, out_dtype, xq.device) if y is None else y
+    E = offsets.numel() - 1
+    _call("fp8_gemm_fprop_grouped", _ptr(xq), _ld(xq), _ptr(xs), _ld(xs),
+          _ptr(wq), ldwq or _ld(wq), wq_estride, _ptr(ws), ldws or _ld(ws), ws_estride,
+          _ptr(y), _out_dtype_code(y.dtype), _ld(y), _ptr(offsets), E, N, D, C, _stream(xq.device))
+    return y
+
+
+def fp8_gemm_dgrad_grouped(gq, gs, wqT, wqT_estride, ws, ws_estride, offsets, N, D, C, dx=None,
+                           out_dtype=torch.bfloat16, ldwqT=None, ldws=None):
+    dx = _new_out(N, C, out_dtype, gq.device) if dx is None else dx
+    E = offsets.numel() - 1
+    _call("fp8_gemm_dgrad_grouped", _ptr(gq), _ld(gq), _ptr(gs), _ld(gs),
+          _ptr(wqT), ldwqT or _ld(wqT), wqT_estride, _ptr(ws), ldws or _ld(ws), ws_estride,
+          _ptr(dx), _out_dtype_code(dx.dtype), _ld(dx), _ptr(offsets), E, N, D, C, _stream(gq.device))
+    return dx
+
+
+def fp8_gemm_wgrad_grouped(gqT, gsT, xqT, xsT, offsets, N, D, C, dw=None, out_dtype=torch.bfloat16,
+                           beta: int = 0):
+    """dW for every expert -> dw [E, D, C]."""
+    E = offsets.numel() - 1
+    if dw is None:
+        per16 = 16 // (2 if out_dtype == torch.bfloat16 else 4)
+        dw = torch.empty((E, D, max(_rup(C, per16), per16)), dtype=out_dtype, device=gqT.device)[:, :, :C]
+    _call("fp8_gemm_wgrad_grouped", _ptr(gqT), _ld(gqT), _ptr(gsT), _ld(gsT), _ptr(xqT), _ld(xqT),
+          _ptr(xsT), _ld(xsT), _ptr(dw), _out_dtype_code(dw.dtype), dw.stride(1), dw.stride(0), beta,
+          _ptr(offsets), E, N, D, C, _stream(gqT.device))
+    return dw
+
+
+# ---------------------------------------------------------------- MXFP8
+def fp8_mx_quantize_1x32(x, rowwise: bool = True, colwise: bool = True):
+    """-> (q [rows, rup(cols)], e [rows, rup(cols)/32], qT [cols, rup(rows)],
+    eT [cols, rup(rows)/32]); unrequested outputs are None."""
+    _check_2d(x, "x")
+    rows, cols = x.shape
+    q = e = qT = eT = None
+    if rowwise:
+        q = _new((rows, _rup(cols)), torch.uint8, x.device)
+        e = _new((rows, _rup(cols) // 32), torch.uint8, x.device)
+    if colwise:
+        qT = _new((cols, _rup(rows)), torch.uint8, x.device)
+        eT = _new((cols, _rup(rows) // 32), torch.uint8, x.device)
+    _call("fp8_mx_quantize_1x32", _ptr(x), _dtype_code(x), rows, cols, _ld(x),
+          _ptr(q), _ld(q) if q is not None else 0, _ptr(e), _ld(e) if e is not None else 0,
+          _ptr(qT), _ld(qT) if qT is not None else 0, _ptr(eT), _ld(eT) if eT is not None else 0,
+          _stream(x.device))
+    return q, e, qT, eT
+
+
+def fp8_mx_gemm_fprop(xq, xe, wq, we, N, D, C, y=None, out_dtype=torch.bfloat16):
+    y = _new_out(N, D, out_dtype, xq.device) if y is None else y
+    _call("fp8_mx_gemm_fprop", _ptr(xq), _ld(xq), _ptr(xe), _ld(xe), _ptr(wq), _ld(wq), _ptr(we), _ld(we),
+          _ptr(y), _out_dtype_code(y.dtype), _ld(y), N, D, C, _stream(xq.device))
+    return y
+
+
+def fp8_mx_gemm_dgrad(gq, ge, wqT, weT, N, D, C, dx=None, out_dtype=torch.bfloat16):
+    dx = _new_out(N, C, out_dtype, gq.device) if dx is None else dx
+    _call("fp8_mx_gemm_dgrad", _ptr(gq), _ld(gq), _ptr(ge), _ld(ge), _ptr(wqT), _ld(wqT), _ptr(weT),
+          _ld(weT), _ptr(dx), _out_dtype_code(dx.dtype), _ld(dx), N, D, C, _stream(gq.device))
+    return dx
+
+
+def fp8_mx_gemm_wgrad(gqT, geT, xqT, xeT, N, D, C, dw=None, out_dtype=torch.bfloat16, beta: int = 0):
+    dw = _new_out(D, C, out_dtype, gqT.device) if dw is None else dw
+    _call("fp8_mx_gemm_wgrad", _ptr(gqT), _ld(gqT), _ptr(geT), _ld(geT), _ptr(xqT), _ld(xqT), _ptr(xeT),
+          _ld(xeT), _ptr(dw), _out_dtype_code(dw.dtype), _ld(dw), beta, N, D, C, _stream(gqT.device))
+    return dw
+
+
+# ----------------------------------------------------------------- misc
+def fp8b_e4m3_encode(x, s=None, out=None):
+    out = _new(x.shape, torch.uint8, x.device) if out is None else out
+    _call("fp8b_e4m3_encode", _ptr(x), _ptr(s), x.numel(), _ptr(out), _stream(x.device))
+    return out
+
+
+def fp8b_validate_gemm(op, a, lda, sa, ldsa, b, ldb, sb, ldsb, out, out_dtype, ldo, beta, N, D, C) -> int:
+    """Host-only argument check (pointers are plain integers here)."""
+    return lib().fp8b_validate_gemm(op, a, lda, sa, ldsa, b, ldb, sb, ldsb, out, out_dtype, ldo, beta,
+                                    N, D, C)
+
+
+def fp8b_abi_version() -> int:
+    return lib().fp8b_abi_version()
+
+
+def fp8b_status_string(status: int) -> str:
+    return lib().fp8b_status_string(status).decode()

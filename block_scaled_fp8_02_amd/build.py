@@ -1,0 +1,62 @@
+"""Build the gfx950 HIP library libfp8blk.so in-tree with hipcc.
+
+Flags:
+  --offload-arch=gfx950          CDNA4 only
+  -Xclang -target-feature -Xclang -packed-fp32-ops
+                                 no packed fp32 VALU ops are generated
+  -fno-gpu-flush-denormals-to-zero
+                                 IEEE denormals on the device (the
+                                 quantizer's scale and quotient must keep them)
+  -ffp-contract=off              no implicit FMA contraction; the kernels
+                                 write every FMA they use explicitly
+"""
+import glob
+import os
+import subprocess
+import sys
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+CSRC = os.path.join(HERE, "csrc")
+LIB = os.path.join(HERE, "libfp8blk.so")
+HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
+
+FLAGS = [
+    "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",
+    "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    "-fno-gpu-flush-denormals-to-zero", "-ffp-contract=off",
+    "-fvisibility=hidden", "-Wall", "-Wno-unused-function",
+]
+
+
+def sources():
+    return sorted(glob.glob(os.path.join(CSRC, "*.hip")))
+
+
+def build(verbose: bool = False, extra=None) -> str:
+    """Compile every HIP source for gfx950 into one shared library.  Always
+    recompiles (this is the 'does it build' check)."""
+    objs = []
+    bdir = os.path.join(HERE, "_build")
+    os.makedirs(bdir, exist_ok=True)
+    procs = []
+    for src in sources():
+        obj = os.path.join(bdir, os.path.basename(src) + ".o")
+        cmd = [HIPCC] + [f for f in FLAGS if f != "-shared"] + ["-c", src, "-o", obj] + list(extra or [])
+        if verbose:
+            print(" ".join(cmd), flush=True)
+        procs.append((subprocess.Popen(cmd), src))
+        objs.append(obj)
+    failed = [src for p, src in procs if p.wait() != 0]
+    if failed:
+        raise RuntimeError(f"hipcc failed for {failed}")
+    tmp = LIB + ".tmp"
+    cmd = [HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp] + objs
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    subprocess.run(cmd, check=True)
+    os.replace(tmp, LIB)
+    return LIB
+
+
+if __name__ == "__main__":
+    build(verbose=True, extra=sys.argv[1:])

@@ -1,0 +1,342 @@
+// api.hip -- the C ABI declared in include/fp8blk.h: host-side argument
+// validation, then one stream-ordered launch per call.  No allocation, no
+// synchronization, no exceptions across the boundary.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/fp8blk.h"
+#include "kernels.hpp"
+
+using namespace fp8blk;
+
+namespace {
+
+thread_local int g_last_hip_error = 0;
+
+inline int64_t rup128(int64_t n) { return (n + 127) / 128 * 128; }
+inline int64_t cdiv(int64_t n, int64_t m) { return (n + m - 1) / m; }
+inline bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+inline int esize(int dt) { return dt == FP8B_BF16 ? 2 : 4; }
+inline bool dtype_ok(int dt) { return dt == FP8B_F32 || dt == FP8B_BF16; }
+
+inline int hip_status(hipError_t e) {
+    if (e == hipSuccess) return FP8B_OK;
+    g_last_hip_error = (int)e;
+    return FP8B_EHIP;
+}
+
+// Input tensor: rows x cols of dtype dt with row stride ld (elements).
+int check_input(const void* x, int dt, int64_t rows, int64_t cols, int64_t ld) {
+    if (!dtype_ok(dt)) return FP8B_EINVAL;
+    if (rows < 0 || cols < 0 || ld < cols) return FP8B_ESHAPE;
+    if (rows == 0 || cols == 0) return FP8B_OK;          // nothing is read
+    if (x == nullptr) return FP8B_EINVAL;
+    if (!aligned(x, 16) || (ld * esize(dt)) % 16 != 0) return FP8B_EALIGN;
+    return FP8B_OK;
+}
+
+// FP8 code buffer: rows x ld bytes holding a padded contraction axis K.
+int check_codes(const void* q, int64_t rows, int64_t K, int64_t ld) {
+    if (rows < 0 || K < 0 || ld < rup128(K)) return FP8B_ESHAPE;
+    if (rows == 0 || K == 0) return FP8B_OK;             // nothing is touched
+    if (q == nullptr) return FP8B_EINVAL;
+    if (!aligned(q, 16) || ld % 16 != 0) return FP8B_EALIGN;
+    return FP8B_OK;
+}
+
+int check_scales(const void* s, int64_t rows, int64_t ncols, int64_t ld, uintptr_t align) {
+    if (rows < 0 || ncols < 0 || ld < ncols) return FP8B_ESHAPE;
+    if (rows == 0 || ncols == 0) return FP8B_OK;
+    if (s == nullptr) return FP8B_EINVAL;
+    if (!aligned(s, align)) return FP8B_EALIGN;
+    return FP8B_OK;
+}
+
+int check_output(const void* o, int dt, int64_t rows, int64_t cols, int64_t ld, int beta) {
+    if (!dtype_ok(dt)) return FP8B_EINVAL;
+    if (beta != 0 && beta != 1) return FP8B_EINVAL;
+    if (beta == 1 && dt != FP8B_F32) return FP8B_EUNSUPPORTED;
+    if (rows < 0 || cols < 0 || ld < cols) return FP8B_ESHAPE;
+    if (rows == 0 || cols == 0) return FP8B_OK;
+    if (o == nullptr) return FP8B_EINVAL;
+    if (!aligned(o, 16) || (ld * esize(dt)) % 16 != 0) return FP8B_EALIGN;
+    return FP8B_OK;
+}
+
+#define FP8B_TRY(expr)                  \
+    do {                                \
+        const int _st = (expr);         \
+        if (_st != FP8B_OK) return _st; \
+    } while (0)
+
+// Shared validation of the dense GEMM family.
+//   op 0 FProp: a = xq [N x C], b = wq [D x C], sb = ws [D/128 x C/128]  -> [N x D]
+//   op 1 DGrad: a = gq [N x D], b = wqT [C x D], sb = ws [D/128 x C/128] -> [N x C]
+//   op 2 WGrad: a = gqT [D x N], b = xqT [C x N], per-row scales          -> [D x C]
+//   op 3..5: the MX forms of the same, with E8M0 scales per 32.
+int validate_gemm(int op, const void* a, int64_t lda, const void* sa, int64_t ldsa,
+                  const void* b, int64_t ldb, const void* sb, int64_t ldsb,
+                  const void* out, int odt, int64_t ldo, int beta, int64_t N, int64_t D, int64_t C) {
+    if (op < 0 || op > 5) return FP8B_EINVAL;
+    if (N < 0 || D < 0 || C < 0) return FP8B_ESHAPE;
+    const bool mx = op >= 3;
+    const int base = op % 3;
+    int64_t M, Nn, K;
+    if (base == 0) { M = N; Nn = D; K = C; }
+    else if (base == 1) { M = N; Nn = C; K = D; }
+    else { M = D; Nn = C; K = N; }
+    if (base != 2 && beta != 0) return FP8B_EINVAL;
+    FP8B_TRY(check_codes(a, M, K, lda));
+    FP8B_TRY(check_codes(b, Nn, K, ldb));
+    const int64_t kb = mx ? rup128(K) / 32 : cdiv(K, 128);
+    const uintptr_t sal = mx ? 1 : 4;
+    FP8B_TRY(check_scales(sa, M, kb, ldsa, sal));
+    if (!mx && base != 2) {
+        // 128x128 weight scale grid [ceil(D/128) x ceil(C/128)], row stride ldsb
+        FP8B_TRY(check_scales(sb, cdiv(D, 128), cdiv(C, 128), ldsb, 4));
+    } else {
+        FP8B_TRY(check_scales(sb, Nn, kb, ldsb, sal));
+    }
+    FP8B_TRY(check_output(out, odt, M, Nn, ldo, beta));
+    return FP8B_OK;
+}
+
+GemmArgs dense_args(int op, const void* a, int64_t lda, const void* sa, int64_t ldsa,
+                    const void* b, int64_t ldb, const void* sb, int64_t ldsb,
+                    void* out, int odt, int64_t ldo, int beta, int64_t N, int64_t D, int64_t C) {
+    GemmArgs g{};
+    const int base = op % 3;
+    g.P = static_cast<const uint8_t*>(a); g.ldp = lda;
+    g.sP = sa; g.ldsp = ldsa;
+    g.Q = static_cast<const uint8_t*>(b); g.ldq = ldb;
+    g.sQ = sb;
+    g.O = out; g.ldo = ldo; g.out_f32 = odt == FP8B_F32; g.beta = beta;
+    if (base == 0) { g.M = N; g.Nn = D; g.K = C; }
+    else if (base == 1) { g.M = N; g.Nn = C; g.K = D; }
+    else { g.M = D; g.Nn = C; g.K = N; }
+    if (op >= 3) {
+        g.scale_mode = SCALE_MX; g.sq_rs = ldsb; g.sq_ks = 1;
+    } else if (base == 0) {
+        g.scale_mode = SCALE_Q_BLOCK; g.sq_rs = ldsb; g.sq_ks = 1;       // ws[d/128][kb]
+    } else if (base == 1) {
+        g.scale_mode = SCALE_Q_BLOCK; g.sq_rs = 1; g.sq_ks = ldsb;       // ws[kb][c/128]
+    } else {
+        g.scale_mode = SCALE_Q_ROW; g.sq_rs = ldsb; g.sq_ks = 1;         // xsT[c][kb]
+    }
+    g.group_mode = GROUP_NONE;
+    return g;
+}
+
+int check_offsets(const int32_t* offsets, int64_t E) {
+    if (E < 1 || E > 65535) return FP8B_ESHAPE;
+    if (offsets == nullptr) return FP8B_EINVAL;
+    if (!aligned(offsets, 4)) return FP8B_EALIGN;
+    return FP8B_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int fp8b_abi_version(void) { return 1; }
+
+const char* fp8b_status_string(int status) {
+    switch (status) {
+        case FP8B_OK: return "ok";
+        case FP8B_EINVAL: return "invalid argument (null pointer or bad enum)";
+        case FP8B_ESHAPE: return "invalid shape or leading dimension";
+        case FP8B_EALIGN: return "pointer or leading dimension not 16-byte aligned";
+        case FP8B_EUNSUPPORTED: return "unsupported combination";
+        case FP8B_EHIP: return "HIP launch error";
+        default: return "unknown status";
+    }
+}
+
+int fp8b_last_hip_error(void) { return g_last_hip_error; }
+
+int fp8_quantize_act_1x128(const void* x, int xt, int64_t rows, int64_t cols, int64_t ldx,
+                           uint8_t* q, int64_t ldq, float* s, int64_t lds, void* stream) {
+    FP8B_TRY(check_input(x, xt, rows, cols, ldx));
+    FP8B_TRY(check_codes(q, rows, cols, ldq));
+    FP8B_TRY(check_scales(s, rows, cdiv(cols, 128), lds, 4));
+    return hip_status(launch_quant_rows(x, xt == FP8B_BF16, rows, cols, ldx, q, ldq, s, lds,
+                                        static_cast<hipStream_t>(stream)));
+}
+
+int fp8_quantize_weight_128x128(const void* w, int wt, int64_t D, int64_t C, int64_t ldw,
+                                uint8_t* q, int64_t ldq, float* s, int64_t lds,
+                                uint8_t* qT, int64_t ldqT, void* stream) {
+    FP8B_TRY(check_input(w, wt, D, C, ldw));
+    FP8B_TRY(check_codes(q, D, C, ldq));
+    FP8B_TRY(check_scales(s, cdiv(D, 128), cdiv(C, 128), lds, 4));
+    if (qT != nullptr) FP8B_TRY(check_codes(qT, C, D, ldqT));
+    return hip_status(launch_quant_weight(w, wt == FP8B_BF16, D, C, ldw, q, ldq, s, lds, qT, ldqT,
+                                          static_cast<hipStream_t>(stream)));
+}
+
+static int quantize_transposed_impl(const void* x, int xt, int64_t rows, int64_t cols, int64_t ldx,
+                                    const int32_t* offsets, int64_t E,
+                                    uint8_t* qT, int64_t ldqT, float* sT, int64_t ldsT,
+                                    uint8_t* q, int64_t ldq, float* s, int64_t lds, void* stream) {
+    FP8B_TRY(check_input(x, xt, rows, cols, ldx));
+    const int64_t P = offsets ? rows + 128 * E : rows;    // upper bound of the padded token axis
+    FP8B_TRY(check_codes(qT, cols, P, ldqT));
+    FP8B_TRY(check_scales(sT, cols, cdiv(P, 128), ldsT, 4));
+    if ((q == nullptr) != (s == nullptr)) return FP8B_EINVAL;
+    if (q != nullptr) {
+        FP8B_TRY(check_codes(q, rows, cols, ldq));
+        FP8B_TRY(check_scales(s, rows, cdiv(cols, 128), lds, 4));
+    }
+    return hip_status(launch_quant_cols(x, xt == FP8B_BF16, rows, cols, ldx, offsets, E, qT, ldqT, sT, ldsT,
+                                        q, ldq, s, lds, static_cast<hipStream_t>(stream)));
+}
+
+int fp8_quantize_transposed(const void* x, int xt, int64_t rows, int64_t cols, int64_t ldx,
+                            uint8_t* qT, int64_t ldqT, float* sT, int64_t ldsT,
+                            uint8_t* q, int64_t ldq, float* s, int64_t lds, void* stream) {
+    return quantize_transposed_impl(x, xt, rows, cols, ldx, nullptr, 0, qT, ldqT, sT, ldsT, q, ldq, s, lds, stream);
+}
+
+int fp8_quantize_transposed_grouped(const void* x, int xt, int64_t rows, int64_t cols, int64_t ldx,
+                                    const int32_t* offsets, int64_t E,
+                                    uint8_t* qT, int64_t ldqT, float* sT, int64_t ldsT,
+                                    uint8_t* q, int64_t ldq, float* s, int64_t lds, void* stream) {
+    FP8B_TRY(check_offsets(offsets, E));
+    return quantize_transposed_impl(x, xt, rows, cols, ldx, offsets, E, qT, ldqT, sT, ldsT, q, ldq, s, lds, stream);
+}
+
+int fp8b_validate_gemm(int op, const void* a, int64_t lda, const void* sa, int64_t ldsa,
+                       const void* b, int64_t ldb, const void* sb, int64_t ldsb,
+                       const void* out, int out_dtype, int64_t ldo, int beta,
+                       int64_t N, int64_t D, int64_t C) {
+    return validate_gemm(op, a, lda, sa, ldsa, b, ldb, sb, ldsb, out, out_dtype, ldo, beta, N, D, C);
+}
+
+static int gemm_dense(int op, const void* a, int64_t lda, const void* sa, int64_t ldsa,
+                      const void* b, int64_t ldb, const void* sb, int64_t ldsb,
+                      void* out, int odt, int64_t ldo, int beta, int64_t N, int64_t D, int64_t C,
+                      void* stream) {
+    FP8B_TRY(validate_gemm(op, a, lda, sa, ldsa, b, ldb, sb, ldsb, out, odt, ldo, beta, N, D, C));
+    const GemmArgs g = dense_args(op, a, lda, sa, ldsa, b, ldb, sb, ldsb, out, odt, ldo, beta, N, D, C);
+    return hip_status(launch_gemm(g, static_cast<hipStream_t>(stream)));
+}
+
+int fp8_gemm_fprop(const uint8_t* xq, int64_t ldxq, const float* xs, int64_t ldxs,
+                   const uint8_t* wq, int64_t ldwq, const float* ws, int64_t ldws,
+                   void* y, int yt, int64_t ldy, int64_t N, int64_t D, int64_t C, void* stream) {
+    return gemm_dense(0, xq, ldxq, xs, ldxs, wq, ldwq, ws, ldws, y, yt, ldy, 0, N, D, C, stream);
+}
+
+int fp8_gemm_dgrad(const uint8_t* gq, int64_t ldgq, const float* gs, int64_t ldgs,
+                   const uint8_t* wqT, int64_t ldwqT, const float* ws, int64_t ldws,
+                   void* dx, int dxt, int64_t lddx, int64_t N, int64_t D, int64_t C, void* stream) {
+    return gemm_dense(1, gq, ldgq, gs, ldgs, wqT, ldwqT, ws, ldws, dx, dxt, lddx, 0, N, D, C, stream);
+}
+
+int fp8_gemm_wgrad(const uint8_t* gqT, int64_t ldgqT, const float* gsT, int64_t ldgsT,
+                   const uint8_t* xqT, int64_t ldxqT, const float* xsT, int64_t ldxsT,
+                   void* dw, int dwt, int64_t lddw, int beta,
+                   int64_t N, int64_t D, int64_t C, void* stream) {
+    return gemm_dense(2, gqT, ldgqT, gsT, ldgsT, xqT, ldxqT, xsT, ldxsT, dw, dwt, lddw, beta, N, D, C, stream);
+}
+
+// Grouped FProp / DGrad: per-expert weights; rows follow the offsets.
+static int gemm_grouped_rows(int op, const uint8_t* a, int64_t lda, const float* sa, int64_t ldsa,
+                             const uint8_t* b, int64_t ldb, int64_t b_estride,
+                             const float* sb, int64_t ldsb, int64_t sb_estride,
+                             void* out, int odt, int64_t ldo,
+                             const int32_t* offsets, int64_t E, int64_t N, int64_t D, int64_t C, void* stream) {
+    FP8B_TRY(check_offsets(offsets, E));
+    if (b_estride < 0 || sb_estride < 0) return FP8B_ESHAPE;
+    // per-expert validation with the expert's D x C weight
+    FP8B_TRY(validate_gemm(op, a, lda, sa, ldsa, b, ldb, sb, ldsb, out, odt, ldo, 0, N, D, C));
+    if (b_estride % 16 != 0) return FP8B_EALIGN;
+    GemmArgs g = dense_args(op, a, lda, sa, ldsa, b, ldb, sb, ldsb, out, odt, ldo, 0, N, D, C);
+    g.group_mode = GROUP_ROWS;
+    g.offsets = offsets; g.E = E;
+    g.q_estride = b_estride; g.sq_estride = sb_estride;
+    return hip_status(launch_gemm(g, static_cast<hipStream_t>(stream)));
+}
+
+int fp8_gemm_fprop_grouped(const uint8_t* xq, int64_t ldxq, const float* xs, int64_t ldxs,
+                           const uint8_t* wq, int64_t ldwq, int64_t wq_estride,
+                           const float* ws, int64_t ldws, int64_t ws_estride,
+                           void* y, int yt, int64_t ldy,
+                           const int32_t* offsets, int64_t E, int64_t N, int64_t D, int64_t C,
+                           void* stream) {
+    return gemm_grouped_rows(0, xq, ldxq, xs, ldxs, wq, ldwq, wq_estride, ws, ldws, ws_estride, y, yt, ldy,
+                             offsets, E, N, D, C, stream);
+}
+
+int fp8_gemm_dgrad_grouped(const uint8_t* gq, int64_t ldgq, const float* gs, int64_t ldgs,
+                           const uint8_t* wqT, int64_t ldwqT, int64_t wqT_estride,
+                           const float* ws, int64_t ldws, int64_t ws_estride,
+                           void* dx, int dxt, int64_t lddx,
+                           const int32_t* offsets, int64_t E, int64_t N, int64_t D, int64_t C,
+                           void* stream) {
+    return gemm_grouped_rows(1, gq, ldgq, gs, ldgs, wqT, ldwqT, wqT_estride, ws, ldws, ws_estride, dx, dxt, lddx,
+                             offsets, E, N, D, C, stream);
+}
+
+int fp8_gemm_wgrad_grouped(const uint8_t* gqT, int64_t ldgqT, const float* gsT, int64_t ldgsT,
+                           const uint8_t* xqT, int64_t ldxqT, const float* xsT, int64_t ldxsT,
+                           void* dw, int dwt, int64_t lddw, int64_t dw_estride, int beta,
+                           const int32_t* offsets, int64_t E, int64_t N, int64_t D, int64_t C,
+                           void* stream) {
+    FP8B_TRY(check_offsets(offsets, E));
+    // the padded token axis is bounded by N + 128*E
+    const int64_t P = N + 128 * E;
+    FP8B_TRY(validate_gemm(2, gqT, ldgqT, gsT, ldgsT, xqT, ldxqT, xsT, ldxsT, dw, dwt, lddw, beta, P, D, C));
+    if (dw_estride < (int64_t)D * lddw) return FP8B_ESHAPE;
+    if ((dw_estride * esize(dwt)) % 16 != 0) return FP8B_EALIGN;
+    GemmArgs g = dense_args(2, gqT, ldgqT, gsT, ldgsT, xqT, ldxqT, xsT, ldxsT, dw, dwt, lddw, beta, P, D, C);
+    g.group_mode = GROUP_K;
+    g.offsets = offsets; g.E = E;
+    g.o_estride = dw_estride;
+    return hip_status(launch_gemm(g, static_cast<hipStream_t>(stream)));
+}
+
+int fp8_mx_quantize_1x32(const void* x, int xt, int64_t rows, int64_t cols, int64_t ldx,
+                         uint8_t* q, int64_t ldq, uint8_t* e, int64_t lde,
+                         uint8_t* qT, int64_t ldqT, uint8_t* eT, int64_t ldeT, void* stream) {
+    FP8B_TRY(check_input(x, xt, rows, cols, ldx));
+    if ((q == nullptr) != (e == nullptr) || (qT == nullptr) != (eT == nullptr)) return FP8B_EINVAL;
+    if (q == nullptr && qT == nullptr) return FP8B_EINVAL;
+    if (q != nullptr) {
+        FP8B_TRY(check_codes(q, rows, cols, ldq));
+        FP8B_TRY(check_scales(e, rows, rup128(cols) / 32, lde, 1));
+    }
+    if (qT != nullptr) {
+        FP8B_TRY(check_codes(qT, cols, rows, ldqT));
+        FP8B_TRY(check_scales(eT, cols, rup128(rows) / 32, ldeT, 1));
+    }
+    return hip_status(launch_mx_quant(x, xt == FP8B_BF16, rows, cols, ldx, q, ldq, e, lde, qT, ldqT, eT, ldeT,
+                                      static_cast<hipStream_t>(stream)));
+}
+
+int fp8_mx_gemm_fprop(const uint8_t* xq, int64_t ldxq, const uint8_t* xe, int64_t ldxe,
+                      const uint8_t* wq, int64_t ldwq, const uint8_t* we, int64_t ldwe,
+                      void* y, int yt, int64_t ldy, int64_t N, int64_t D, int64_t C, void* stream) {
+    return gemm_dense(3, xq, ldxq, xe, ldxe, wq, ldwq, we, ldwe, y, yt, ldy, 0, N, D, C, stream);
+}
+
+int fp8_mx_gemm_dgrad(const uint8_t* gq, int64_t ldgq, const uint8_t* ge, int64_t ldge,
+                      const uint8_t* wqT, int64_t ldwqT, const uint8_t* weT, int64_t ldweT,
+                      void* dx, int dxt, int64_t lddx, int64_t N, int64_t D, int64_t C, void* stream) {
+    return gemm_dense(4, gq, ldgq, ge, ldge, wqT, ldwqT, weT, ldweT, dx, dxt, lddx, 0, N, D, C, stream);
+}
+
+int fp8_mx_gemm_wgrad(const uint8_t* gqT, int64_t ldgqT, const uint8_t* geT, int64_t ldgeT,
+                      const uint8_t* xqT, int64_t ldxqT, const uint8_t* xeT, int64_t ldxeT,
+                      void* dw, int dwt, int64_t lddw, int beta,
+                      int64_t N, int64_t D, int64_t C, void* stream) {
+    return gemm_dense(5, gqT, ldgqT, geT, ldgeT, xqT, ldxqT, xeT, ldxeT, dw, dwt, lddw, beta, N, D, C, stream);
+}
+
+int fp8b_e4m3_encode(const float* x, const float* s, int64_t n, uint8_t* out, void* stream) {
+    if (n < 0) return FP8B_ESHAPE;
+    if (n > 0 && (x == nullptr || out == nullptr)) return FP8B_EINVAL;
+    return hip_status(launch_encode(x, s, n, out, static_cast<hipStream_t>(stream)));
+}
+
+}  // extern "C"

@@ -1,0 +1,155 @@
+// device_common.hpp -- device helpers shared by the gfx950 kernels:
+// bf16 conversion, the exact E4M3 quotient and encoder, wave reductions.
+//
+// The quantizer Q of the Jet-RL notes (section 2.1) is
+//     S = max|X| / 448,   Xhat = E4M3(X / S)
+// with the quotient formed in fp32 and rounded to the nearest E4M3 value
+// (ties to even, saturating at +-448).  The code below reproduces that
+// bit for bit without the long IEEE fp32 division sequence per element.
+//
+// Lane layout of v_mfma_f32_16x16x128_f8f6f4 (checked on the device): lane
+// l supplies row l%16 of an operand; its first 16 bytes are K positions
+// 16*(l/16) .. +15 and its last 16 bytes K positions 64 + 16*(l/16) .. +15.
+// The scaled form takes the E8M0 scale of row l%16, K block l/16 (32 wide)
+// from lane l.  The 4 results of lane l are rows 4*(l/16)+r, column l%16.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace fp8blk {
+
+typedef int v8i __attribute__((ext_vector_type(8)));
+typedef float v4f __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ float bf16_to_f32(uint32_t bits16) {
+    return __uint_as_float(bits16 << 16);
+}
+
+// Nearest-even fp32 -> bf16 (finite inputs).
+__device__ __forceinline__ uint32_t f32_to_bf16(float f) {
+    uint32_t u = __float_as_uint(f);
+    u += 0x7FFFu + ((u >> 16) & 1u);
+    return u >> 16;
+}
+
+// Group scale S = fl32(amax / 448).  The binary64 quotient rounded to
+// binary32 equals the correctly rounded binary32 quotient (double rounding
+// through 53 bits is innocuous for a division of 24-bit operands, since
+// 53 >= 2*24 + 2).
+__device__ __forceinline__ float group_scale(float amax) {
+    return (float)((double)amax / 448.0);
+}
+
+// R = 1/S rounded to binary64; 0 when S == 0, so that x * R is the signed
+// zero of x (an all-zero group, or one whose scale underflowed).
+__device__ __forceinline__ double quotient_recip(float S) {
+    return S == 0.0f ? 0.0 : 1.0 / (double)S;
+}
+
+// fl32(x / S) from R = RN64(1/S).  x * R carries a relative error below
+// 2^-52, while a quotient of two binary32 numbers is either exactly
+// representable or at least 2^-49 (relative) away from every binary32
+// rounding boundary and never exactly on one; so rounding x * R to binary32
+// gives exactly the correctly rounded fp32 quotient.
+__device__ __forceinline__ float exact_quotient(float x, double R) {
+    return (float)((double)x * R);
+}
+
+// E4M3 code of a finite fp32 value: nearest, ties to even, |y| >= 448
+// saturates to 0x7E/0xFE, the sign of zero is kept.  The value is clamped
+// to [-448, 448] (saturation: nothing beyond 448 is representable, and
+// values in (448, 464) would round to 448 anyway), then converted by the
+// gfx950 OCP-E4M3 conversion, which rounds to nearest-even and keeps
+// subnormals; the device test suite checks this conversion against the
+// reference encoder on every finite fp32 bit pattern.
+__device__ __forceinline__ float sat448(float y) {
+    return fminf(fmaxf(y, -448.0f), 448.0f);
+}
+
+// Two codes in the low 16 bits (first argument in the low byte).
+__device__ __forceinline__ uint32_t e4m3_encode2(float a, float b) {
+    return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(sat448(a), sat448(b), 0, false) & 0xFFFFu;
+}
+
+__device__ __forceinline__ uint32_t e4m3_encode(float y) {
+    return e4m3_encode2(y, y) & 0xFFu;
+}
+
+// Four codes in one little-endian word.
+__device__ __forceinline__ uint32_t e4m3_pack4(float a, float b, float c, float d) {
+    const int lo = __builtin_amdgcn_cvt_pk_fp8_f32(sat448(a), sat448(b), 0, false);
+    return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(sat448(c), sat448(d), lo, true);
+}
+
+// Encode four quotients x / S (R = 1/S as above) into one word.
+__device__ __forceinline__ uint32_t encode4(float a, float b, float c, float d, double R) {
+    return e4m3_pack4(exact_quotient(a, R), exact_quotient(b, R), exact_quotient(c, R), exact_quotient(d, R));
+}
+
+// Max over the 16 lanes of an aligned 16-lane group.
+__device__ __forceinline__ float max16(float v) {
+    v = fmaxf(v, __shfl_xor(v, 1));
+    v = fmaxf(v, __shfl_xor(v, 2));
+    v = fmaxf(v, __shfl_xor(v, 4));
+    v = fmaxf(v, __shfl_xor(v, 8));
+    return v;
+}
+
+// Max over the whole wavefront (64 lanes).
+__device__ __forceinline__ float max64(float v) {
+    v = max16(v);
+    v = fmaxf(v, __shfl_xor(v, 16));
+    v = fmaxf(v, __shfl_xor(v, 32));
+    return v;
+}
+
+// Load 8 consecutive elements (bf16 or fp32) as fp32; `valid` (0..8) of
+// them are in bounds, the rest read as +0.  A full 8-element run is one
+// (bf16) or two (fp32) 16-byte loads; 16-byte alignment is a precondition
+// checked on the host.
+__device__ __forceinline__ void load8(const uint16_t* p, int valid, float v[8]) {
+    if (valid == 8) {
+        uint4 w = *reinterpret_cast<const uint4*>(p);
+        v[0] = bf16_to_f32(w.x & 0xFFFFu); v[1] = bf16_to_f32(w.x >> 16);
+        v[2] = bf16_to_f32(w.y & 0xFFFFu); v[3] = bf16_to_f32(w.y >> 16);
+        v[4] = bf16_to_f32(w.z & 0xFFFFu); v[5] = bf16_to_f32(w.z >> 16);
+        v[6] = bf16_to_f32(w.w & 0xFFFFu); v[7] = bf16_to_f32(w.w >> 16);
+    } else {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) v[i] = i < valid ? bf16_to_f32(p[i]) : 0.0f;
+    }
+}
+
+__device__ __forceinline__ void load8(const float* p, int valid, float v[8]) {
+    if (valid == 8) {
+        float4 a = *reinterpret_cast<const float4*>(p);
+        float4 b = *reinterpret_cast<const float4*>(p + 4);
+        v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
+        v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+    } else {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) v[i] = i < valid ? p[i] : 0.0f;
+    }
+}
+
+__device__ __forceinline__ int clamp_valid(int64_t remaining) {
+    return remaining >= 8 ? 8 : (remaining <= 0 ? 0 : (int)remaining);
+}
+
+// Transpose an 8x8 byte block held as rows (lo = bytes 0..3, hi = 4..7):
+// column j of the input becomes row j of the output.
+__device__ __forceinline__ void transpose8x8(const uint32_t lo[8], const uint32_t hi[8],
+                                             uint32_t tlo[8], uint32_t thi[8]) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+        const uint32_t* src = j < 4 ? lo : hi;
+        const int sh = 8 * (j & 3);
+        tlo[j] = ((src[0] >> sh) & 0xFFu) | (((src[1] >> sh) & 0xFFu) << 8) |
+                 (((src[2] >> sh) & 0xFFu) << 16) | (((src[3] >> sh) & 0xFFu) << 24);
+        thi[j] = ((src[4] >> sh) & 0xFFu) | (((src[5] >> sh) & 0xFFu) << 8) |
+                 (((src[6] >> sh) & 0xFFu) << 16) | (((src[7] >> sh) & 0xFFu) << 24);
+    }
+}
+
+}  // namespace fp8blk

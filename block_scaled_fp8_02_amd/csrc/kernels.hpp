@@ -1,0 +1,65 @@
+// kernels.hpp -- internal launch interface between the C ABI layer
+// (api.hip) and the kernel translation units.  Arguments are validated by
+// the caller; these functions only launch and report hipGetLastError().
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace fp8blk {
+
+// Row-wise 1x128 quantization (in_bf16: bf16 input, else fp32).
+hipError_t launch_quant_rows(const void* x, bool in_bf16, int64_t rows, int64_t cols, int64_t ldx,
+                             uint8_t* q, int64_t ldq, float* s, int64_t lds, hipStream_t st);
+
+// 128x128 weight quantization with optional transposed copy.
+hipError_t launch_quant_weight(const void* w, bool in_bf16, int64_t D, int64_t C, int64_t ldw,
+                               uint8_t* q, int64_t ldq, float* s, int64_t lds,
+                               uint8_t* qT, int64_t ldqT, hipStream_t st);
+
+// Token-axis 1x128 quantization written transposed, optionally also the
+// row-wise copy; offsets == nullptr means one segment of all rows.
+hipError_t launch_quant_cols(const void* x, bool in_bf16, int64_t rows, int64_t cols, int64_t ldx,
+                             const int32_t* offsets, int64_t E,
+                             uint8_t* qT, int64_t ldqT, float* sT, int64_t ldsT,
+                             uint8_t* q, int64_t ldq, float* s, int64_t lds, hipStream_t st);
+
+// Elementwise codec access.
+hipError_t launch_encode(const float* x, const float* s, int64_t n, uint8_t* out, hipStream_t st);
+
+// Generic block-scaled / MX GEMM:
+//   O[i][j] (+)= sum_k P[i][k] Q[j][k] * scales
+// P: M x K codes (row stride ldp), Q: Nn x K codes (row stride ldq), both
+// padded with zero codes to a multiple of 128 along K.
+enum ScaleMode {
+    SCALE_Q_BLOCK = 0,   // sQ per 128-row block of Q: sQ[(j/128)*sq_rs + kb*sq_ks]
+    SCALE_Q_ROW = 1,     // sQ per row of Q:           sQ[j*sq_rs + kb*sq_ks]
+    SCALE_MX = 2         // E8M0 bytes per 32-block:   eP[i*ldsp + k/32], eQ[j*sq_rs + k/32]
+};
+enum GroupMode {
+    GROUP_NONE = 0,
+    GROUP_ROWS = 1,      // expert e owns P/O rows [off[e], off[e+1]) and Q_e = Q + e*q_estride
+    GROUP_K = 2          // expert e owns K range [P_e, P_e + round_up(n_e,128)), O_e = O + e*o_estride
+};
+
+struct GemmArgs {
+    const uint8_t* P; int64_t ldp;
+    const void* sP; int64_t ldsp;
+    const uint8_t* Q; int64_t ldq;
+    const void* sQ; int64_t sq_rs; int64_t sq_ks;
+    void* O; int64_t ldo; bool out_f32; int beta;
+    int64_t M, Nn, K;
+    int scale_mode;
+    int group_mode;
+    const int32_t* offsets; int64_t E;
+    int64_t q_estride, sq_estride, o_estride;
+};
+
+hipError_t launch_gemm(const GemmArgs& a, hipStream_t st);
+
+// MXFP8 1x32 quantization (row-wise and/or column-wise).
+hipError_t launch_mx_quant(const void* x, bool in_bf16, int64_t rows, int64_t cols, int64_t ldx,
+                           uint8_t* q, int64_t ldq, uint8_t* e, int64_t lde,
+                           uint8_t* qT, int64_t ldqT, uint8_t* eT, int64_t ldeT, hipStream_t st);
+
+}  // namespace fp8blk

@@ -1,0 +1,142 @@
+// mx.hip -- MXFP8 quantizer for gfx950 (Miles MXFP8/NVFP4 blog, MXFP8
+// paragraphs): 32 consecutive values share one E8M0 power-of-two scale
+// 2^k, k the smallest integer with max|block| <= 448 * 2^k (rounded up so
+// the block maximum does not clip), and the codes are E4M3(x * 2^-k).  The
+// row-wise (1x32) and column-wise (32x1) copies are both quantized from the
+// full-precision input, in one pass over a 128x128 tile.
+//
+// The MX GEMMs themselves run through the generic kernel in gemm.hip with
+// the E8M0 scales handed to the scaled MFMA.
+#include "device_common.hpp"
+#include "kernels.hpp"
+
+namespace fp8blk {
+
+// Smallest k with amax <= 448 * 2^k, clamped to [-127, 127]; -127 for 0.
+// With amax = m * 2^e, m in [0.5, 1): 448 = 0.875 * 2^9, so k = e - 9 when
+// m <= 0.875 and k = e - 8 otherwise.
+__device__ __forceinline__ int mx_exponent(float amax) {
+    if (amax == 0.0f) return -127;
+    int e;
+    const float m = frexpf(amax, &e);
+    int k = e - 9 + (m > 0.875f ? 1 : 0);
+    return k < -127 ? -127 : (k > 127 ? 127 : k);
+}
+
+__device__ __forceinline__ uint32_t mx_encode4(const float* v, int k) {
+    return e4m3_pack4(ldexpf(v[0], -k), ldexpf(v[1], -k), ldexpf(v[2], -k), ldexpf(v[3], -k));
+}
+
+// Tile 128 rows x 128 cols; thread t holds rows 8*(t/16)..+7, cols
+// 8*(t%16)..+7.  A 32-column row block spans 4 consecutive lanes; a 32-row
+// column block spans the 4 row-slices of one wavefront.
+template <typename T>
+__global__ __launch_bounds__(256) void k_mx_quant(const T* __restrict__ x, int64_t rows, int64_t cols, int64_t ldx,
+                                                  uint8_t* __restrict__ q, int64_t ldq,
+                                                  uint8_t* __restrict__ e, int64_t lde,
+                                                  uint8_t* __restrict__ qT, int64_t ldqT,
+                                                  uint8_t* __restrict__ eT, int64_t ldeT) {
+    __shared__ __attribute__((aligned(16))) uint8_t tileT[128 * 128];
+    const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+    const int rg = t >> 4, cg = t & 15;
+    const int64_t rb = (int64_t)blockIdx.x * 128, cb = (int64_t)blockIdx.y * 128;
+    const int64_t r0 = rb + rg * 8, c0 = cb + cg * 8;
+    const int cvalid = clamp_valid(cols - c0);
+
+    float v[8][8];
+#pragma unroll
+    for (int p = 0; p < 8; ++p) {
+        const int64_t r = r0 + p;
+        const bool in = r < rows;
+        load8(x + (in ? r : 0) * ldx + c0, in ? cvalid : 0, v[p]);
+    }
+
+    if (q != nullptr) {
+        // row-wise 1x32: lanes 4n..4n+3 of a 16-lane row slice share a block
+#pragma unroll
+        for (int p = 0; p < 8; ++p) {
+            float m = 0.0f;
+#pragma unroll
+            for (int j = 0; j < 8; ++j) m = fmaxf(m, fabsf(v[p][j]));
+            m = fmaxf(m, __shfl_xor(m, 1));
+            m = fmaxf(m, __shfl_xor(m, 2));
+            const int k = mx_exponent(m);
+            const int64_t r = r0 + p;
+            if (r < rows) {
+                *reinterpret_cast<uint2*>(q + r * ldq + c0) = make_uint2(mx_encode4(&v[p][0], k), mx_encode4(&v[p][4], k));
+                if ((cg & 3) == 0) {
+                    const int64_t blk = c0 / 32;
+                    e[r * lde + blk] = (uint8_t)(c0 < cols ? k + 127 : 127);
+                }
+            }
+        }
+    }
+    if (qT == nullptr) return;                                       // uniform
+
+    // column-wise 32x1: reduce 8 rows in-thread, then lanes l, l^16, l^32, l^48
+    int kc[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+        float m = 0.0f;
+#pragma unroll
+        for (int p = 0; p < 8; ++p) m = fmaxf(m, fabsf(v[p][j]));
+        m = fmaxf(m, __shfl_xor(m, 16));
+        m = fmaxf(m, __shfl_xor(m, 32));
+        kc[j] = mx_exponent(m);
+    }
+    if (lane < 16) {                                                  // one writer per (column, wave)
+        const int64_t rblk = rb / 32 + wave;
+        const bool padblk = rb + 32 * wave >= rows;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            const int64_t c = c0 + j;
+            if (c < cols) eT[c * ldeT + rblk] = (uint8_t)(padblk ? 127 : kc[j] + 127);
+        }
+    }
+    uint32_t lo[8], hi[8];
+#pragma unroll
+    for (int p = 0; p < 8; ++p) {
+        lo[p] = e4m3_pack4(ldexpf(v[p][0], -kc[0]), ldexpf(v[p][1], -kc[1]), ldexpf(v[p][2], -kc[2]),
+                           ldexpf(v[p][3], -kc[3]));
+        hi[p] = e4m3_pack4(ldexpf(v[p][4], -kc[4]), ldexpf(v[p][5], -kc[5]), ldexpf(v[p][6], -kc[6]),
+                           ldexpf(v[p][7], -kc[7]));
+    }
+    uint32_t tlo[8], thi[8];
+    transpose8x8(lo, hi, tlo, thi);
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+        *reinterpret_cast<uint2*>(tileT + (cg * 8 + j) * 128 + ((rg ^ cg) << 3)) = make_uint2(tlo[j], thi[j]);
+    __syncthreads();
+    const int crow = t >> 1, h = t & 1;
+    const int64_t c = cb + crow;
+    if (c < cols) {
+        uint32_t wv[16];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const int phys = (8 * h + i) ^ (crow >> 3);
+            const uint2 u = *reinterpret_cast<const uint2*>(tileT + crow * 128 + (phys << 3));
+            wv[2 * i] = u.x;
+            wv[2 * i + 1] = u.y;
+        }
+        uint8_t* dst = qT + c * ldqT + rb + 64 * h;
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            *reinterpret_cast<uint4*>(dst + 16 * i) = make_uint4(wv[4 * i], wv[4 * i + 1], wv[4 * i + 2], wv[4 * i + 3]);
+    }
+}
+
+hipError_t launch_mx_quant(const void* x, bool in_bf16, int64_t rows, int64_t cols, int64_t ldx,
+                           uint8_t* q, int64_t ldq, uint8_t* e, int64_t lde,
+                           uint8_t* qT, int64_t ldqT, uint8_t* eT, int64_t ldeT, hipStream_t st) {
+    if (rows == 0 || cols == 0) return hipSuccess;
+    const int64_t rt = (rows + 127) / 128, ct = (cols + 127) / 128;
+    if (rt > 0x7FFFFFFF || ct > 65535) return hipErrorInvalidValue;
+    const dim3 grid((unsigned)rt, (unsigned)ct);
+    if (in_bf16)
+        k_mx_quant<uint16_t><<<grid, 256, 0, st>>>(static_cast<const uint16_t*>(x), rows, cols, ldx, q, ldq, e, lde, qT, ldqT, eT, ldeT);
+    else
+        k_mx_quant<float><<<grid, 256, 0, st>>>(static_cast<const float*>(x), rows, cols, ldx, q, ldq, e, lde, qT, ldqT, eT, ldeT);
+    return hipGetLastError();
+}
+
+}  // namespace fp8blk

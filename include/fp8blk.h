@@ -1,0 +1,255 @@
+/*
+ * fp8blk.h -- C ABI of the block-scaled FP8 linear-layer library for
+ * AMD Instinct MI355X (gfx950).
+ *
+ * The library implements the unified FP8 precision flow for linear layers
+ * described on the Jet-RL pages:
+ *   - quantizer Q: S = max|X| / 448, Xhat = X / S rounded to the nearest
+ *     OCP E4M3 value (Jet-RL notes, section 2.1, definition of Q);
+ *   - activations and gradients quantized per 1x128 group along the
+ *     contraction axis, weights per 128x128 block (Jet-RL notes, section
+ *     4.2; summary page, "Weight quantization" and "Activation and gradient
+ *     quantization");
+ *   - FProp Y = X W^T, DGrad dX = dY W, WGrad dW = dY^T X as block-scaled
+ *     FP8 GEMMs with fp32 accumulation (Jet-RL notes, section 2.2 and 4.2);
+ *   - an MXFP8 variant with 1x32 E4M3 blocks sharing an E8M0 power-of-two
+ *     scale rounded up so nothing clips (Miles MXFP8/NVFP4 blog, MXFP8
+ *     paragraphs).
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * - All pointers are DEVICE pointers (except where stated) owned by the
+ *   caller.  The library never allocates or frees device memory and keeps
+ *   no state between calls apart from lazily loaded code objects.
+ * - Every call is asynchronous on `stream` (a hipStream_t passed as void*;
+ *   NULL is the default stream).  Buffers must stay valid until the stream
+ *   reaches the operation.
+ * - Layouts are row-major with explicit leading dimensions counted in
+ *   ELEMENTS of the buffer's type (bytes for FP8/E8M0 buffers).
+ * - FP8 code buffers pad the contraction axis to a multiple of 128: the
+ *   quantizers write 0x00 into the padding, and the GEMMs read the whole
+ *   padded length.  The pad therefore contributes exactly zero.
+ * - Return value: 0 (FP8B_OK) on success.  Argument errors are detected on
+ *   the host before anything is launched and return a nonzero status; a
+ *   failed launch returns FP8B_EHIP with the HIP error code retrievable by
+ *   fp8b_last_hip_error() (thread-local).  Nothing aborts the process and
+ *   no C++ exception crosses this boundary.
+ * - Inputs must be finite; this is not checked on the device.
+ * - Results are deterministic, and every GEMM row depends only on its own
+ *   input row: the reduction order of an output element does not depend on
+ *   the number of rows in the call (unified rollout/training forward).
+ */
+#ifndef FP8BLK_H
+#define FP8BLK_H
+
+#include <stdint.h>
+
+#if defined(__GNUC__) || defined(__clang__)
+#define FP8B_API __attribute__((visibility("default")))
+#else
+#define FP8B_API
+#endif
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum fp8b_status_code {
+    FP8B_OK = 0,
+    FP8B_EINVAL = 1,       /* null pointer where one is required, bad enum value */
+    FP8B_ESHAPE = 2,       /* dimension < 0, leading dimension too small, bad group count */
+    FP8B_EALIGN = 3,       /* pointer or leading dimension not 16-byte aligned */
+    FP8B_EUNSUPPORTED = 4, /* valid request this build does not implement */
+    FP8B_EHIP = 5          /* HIP launch error; see fp8b_last_hip_error() */
+};
+
+enum fp8b_dtype {
+    FP8B_F32 = 0,          /* IEEE binary32 */
+    FP8B_BF16 = 1          /* bfloat16 (upper half of binary32), stored as uint16 */
+};
+
+/* Version of this ABI (incremented on any incompatible change). */
+FP8B_API int fp8b_abi_version(void);
+
+/* Static, human-readable text for a status code. */
+FP8B_API const char* fp8b_status_string(int status);
+
+/* HIP error code of the last FP8B_EHIP returned on the calling thread. */
+FP8B_API int fp8b_last_hip_error(void);
+
+/* ------------------------------------------------------------------ */
+/* Quantizers                                                          */
+/* ------------------------------------------------------------------ */
+
+/* R1. 1x128 per-group quantization along the contiguous axis
+ * (Jet-RL summary, "Activation and gradient quantization: 1x128 per-group";
+ * used for X in FProp and for dY along D in DGrad).
+ *   x  : rows x cols of dtype xt, row stride ldx >= cols.
+ *   q  : rows x ldq bytes, ldq >= round_up(cols,128), ldq % 16 == 0;
+ *        columns [cols, round_up(cols,128)) are written 0x00.
+ *   s  : rows x lds fp32, lds >= ceil(cols/128); s[r][g] = max|x[r][128g..]|/448.
+ * Codes are E4M3(fl32(x / s)), nearest-even, saturating at +-448; a group
+ * with s == 0 stores the signed zero of each input. */
+FP8B_API int fp8_quantize_act_1x128(const void* x, int xt, int64_t rows, int64_t cols, int64_t ldx,
+                           uint8_t* q, int64_t ldq, float* s, int64_t lds, void* stream);
+
+/* R2. 128x128 per-block weight quantization (Jet-RL summary, "Weight
+ * quantization: 128x128 per-block"; redone after every optimizer step).
+ *   w  : D x C of dtype wt, row stride ldw >= C.
+ *   q  : D x ldq bytes, ldq >= round_up(C,128), ldq % 16 == 0; pad 0x00.
+ *   s  : ceil(D/128) x lds fp32, lds >= ceil(C/128).
+ *   qT : optional (NULL to skip): the same codes transposed, C x ldqT bytes,
+ *        ldqT >= round_up(D,128), ldqT % 16 == 0; columns [D, round_up(D,128))
+ *        written 0x00.  DGrad reads W through this copy with the same scale
+ *        grid read transposed (the block scales are symmetric in D and C).
+ * Several weights of equal C may be stacked along D (e.g. the E experts of a
+ * MoE layer as one (E*D) x C matrix) when D is a multiple of 128. */
+FP8B_API int fp8_quantize_weight_128x128(const void* w, int wt, int64_t D, int64_t C, int64_t ldw,
+                                uint8_t* q, int64_t ldq, float* s, int64_t lds,
+                                uint8_t* qT, int64_t ldqT, void* stream);
+
+/* R3. 1x128 groups along the token (row) axis, written transposed: the
+ * WGrad operands dY^T and X^T (Jet-RL notes, section 4.2: WGrad groups its
+ * operands along the token axis).  Reads x once and can also emit the R1
+ * row-wise quantization of the same tensor from the same read.
+ *   x   : rows x cols of dtype xt, row stride ldx.
+ *   qT  : cols x ldqT bytes, ldqT >= round_up(rows,128), ldqT % 16 == 0;
+ *         qT[c][r] is the code of x[r][c]; pad positions 0x00.
+ *   sT  : cols x ldsT fp32, ldsT >= ceil(rows/128).
+ *   q, s: optional (both NULL or both set) R1 output with ldq/lds as in R1. */
+FP8B_API int fp8_quantize_transposed(const void* x, int xt, int64_t rows, int64_t cols, int64_t ldx,
+                            uint8_t* qT, int64_t ldqT, float* sT, int64_t ldsT,
+                            uint8_t* q, int64_t ldq, float* s, int64_t lds, void* stream);
+
+/* R3, grouped (MoE).  offsets: DEVICE int32[E+1], non-decreasing, offsets[0]
+ * = 0, offsets[E] = rows; rows [offsets[e], offsets[e+1]) belong to expert
+ * e and token groups restart at every offsets[e].  Expert e occupies qT
+ * columns [P_e, P_e + round_up(n_e,128)) with n_e = offsets[e+1]-offsets[e]
+ * and P_e = sum_{e'<e} round_up(n_e',128), and sT columns [P_e/128,
+ * P_e/128 + ceil(n_e/128)).  The caller sizes ldqT >= round_up(rows +
+ * 128*E, 128) (a bound of P_E) and ldsT >= ldqT/128.  The optional row-wise
+ * output does not depend on the grouping.  offsets are read on the device
+ * and are not validated there: they must describe a partition of the rows. */
+FP8B_API int fp8_quantize_transposed_grouped(const void* x, int xt, int64_t rows, int64_t cols, int64_t ldx,
+                                    const int32_t* offsets, int64_t E,
+                                    uint8_t* qT, int64_t ldqT, float* sT, int64_t ldsT,
+                                    uint8_t* q, int64_t ldq, float* s, int64_t lds, void* stream);
+
+/* ------------------------------------------------------------------ */
+/* Block-scaled FP8 GEMMs (fp32 accumulation; each 128-wide K block's    */
+/* partial product is scaled by s_a * s_b before it is added)           */
+/* ------------------------------------------------------------------ */
+
+/* R4. FProp Y[N x D] = X W^T (Jet-RL notes, section 2.2 FProp; 4.2: the
+ * activation 1x128 and the weight 128x128).
+ *   xq [N x ldxq] codes, xs [N x ldxs] fp32 (from R1 on X [N x C]);
+ *   wq [D x ldwq] codes, ws [ceil(D/128) x ldws] fp32 (from R2);
+ *   y  [N x ldy] of dtype yt (FP8B_BF16: round-to-nearest-even; FP8B_F32). */
+FP8B_API int fp8_gemm_fprop(const uint8_t* xq, int64_t ldxq, const float* xs, int64_t ldxs,
+                   const uint8_t* wq, int64_t ldwq, const float* ws, int64_t ldws,
+                   void* y, int yt, int64_t ldy, int64_t N, int64_t D, int64_t C, void* stream);
+
+/* R5. DGrad dX[N x C] = dY W (Jet-RL notes, section 2.2 DGrad; 4.2: same
+ * kernel configuration as FProp, the weight only transposed).
+ *   gq [N x ldgq] codes, gs [N x ldgs] fp32 (R1 on dY [N x D], groups along D);
+ *   wqT [C x ldwqT] codes (R2's transposed copy), ws [ceil(D/128) x ldws]. */
+FP8B_API int fp8_gemm_dgrad(const uint8_t* gq, int64_t ldgq, const float* gs, int64_t ldgs,
+                   const uint8_t* wqT, int64_t ldwqT, const float* ws, int64_t ldws,
+                   void* dx, int dxt, int64_t lddx, int64_t N, int64_t D, int64_t C, void* stream);
+
+/* R6. WGrad dW[D x C] = dY^T X (Jet-RL notes, section 2.2 WGrad; 4.2: both
+ * operands grouped along the token axis).
+ *   gqT [D x ldgqT], gsT [D x ldgsT] (R3 on dY); xqT [C x ldxqT], xsT [C x ldxsT]
+ *   (R3 on X); contraction length N (tokens).
+ *   beta = 0: dw = result; beta = 1: dw += result (dwt must be FP8B_F32). */
+FP8B_API int fp8_gemm_wgrad(const uint8_t* gqT, int64_t ldgqT, const float* gsT, int64_t ldgsT,
+                   const uint8_t* xqT, int64_t ldxqT, const float* xsT, int64_t ldxsT,
+                   void* dw, int dwt, int64_t lddw, int beta,
+                   int64_t N, int64_t D, int64_t C, void* stream);
+
+/* R7. Grouped (MoE) forms.  offsets: DEVICE int32[E+1] as for the grouped
+ * quantizer.  Expert e's weight codes start at w + e*w_estride (bytes) and
+ * its scales at ws + e*ws_estride (floats); stacking the experts as one
+ * (E*D) x C matrix quantized by R2 gives w_estride = D*ldwq and
+ * ws_estride = (D/128)*ldws, and for the transposed copy qT [C x E*D]
+ * w_estride = D.
+ * FProp: rows of expert e of xq times W_e^T -> rows of y.
+ * DGrad: rows of expert e of gq times W_e   -> rows of dx. */
+FP8B_API int fp8_gemm_fprop_grouped(const uint8_t* xq, int64_t ldxq, const float* xs, int64_t ldxs,
+                           const uint8_t* wq, int64_t ldwq, int64_t wq_estride,
+                           const float* ws, int64_t ldws, int64_t ws_estride,
+                           void* y, int yt, int64_t ldy,
+                           const int32_t* offsets, int64_t E, int64_t N, int64_t D, int64_t C,
+                           void* stream);
+FP8B_API int fp8_gemm_dgrad_grouped(const uint8_t* gq, int64_t ldgq, const float* gs, int64_t ldgs,
+                           const uint8_t* wqT, int64_t ldwqT, int64_t wqT_estride,
+                           const float* ws, int64_t ldws, int64_t ws_estride,
+                           void* dx, int dxt, int64_t lddx,
+                           const int32_t* offsets, int64_t E, int64_t N, int64_t D, int64_t C,
+                           void* stream);
+/* WGrad per expert: dW_e = dY_e^T X_e from the grouped transposed operands
+ * (R3 grouped); dW_e is written at dw + e*dw_estride (elements).  An expert
+ * with no rows gets dW_e = 0 (beta = 0) or is left unchanged (beta = 1). */
+FP8B_API int fp8_gemm_wgrad_grouped(const uint8_t* gqT, int64_t ldgqT, const float* gsT, int64_t ldgsT,
+                           const uint8_t* xqT, int64_t ldxqT, const float* xsT, int64_t ldxsT,
+                           void* dw, int dwt, int64_t lddw, int64_t dw_estride, int beta,
+                           const int32_t* offsets, int64_t E, int64_t N, int64_t D, int64_t C,
+                           void* stream);
+
+/* ------------------------------------------------------------------ */
+/* MXFP8 (Miles MXFP8/NVFP4 blog, MXFP8 paragraphs)                    */
+/* ------------------------------------------------------------------ */
+
+/* R9. 1x32 blocks, scale 2^k stored as the E8M0 byte k+127, k the smallest
+ * integer with max|block| <= 448*2^k, clamped to [-127,127] (all-zero block:
+ * k = -127); codes E4M3(x * 2^-k).  Either output pair may be NULL:
+ *   q  [rows x ldq], e [rows x lde]: row-wise (blocks along cols);
+ *   qT [cols x ldqT], eT [cols x ldeT]: column-wise (blocks along rows),
+ *   each quantized from x itself (never from the other copy).
+ * Code buffers pad the block axis to a multiple of 128 with 0x00
+ * (ldq >= round_up(cols,128), ldqT >= round_up(rows,128), multiples of 16);
+ * E8M0 buffers hold round_up(K,128)/32 entries per row, pad entries 127. */
+FP8B_API int fp8_mx_quantize_1x32(const void* x, int xt, int64_t rows, int64_t cols, int64_t ldx,
+                         uint8_t* q, int64_t ldq, uint8_t* e, int64_t lde,
+                         uint8_t* qT, int64_t ldqT, uint8_t* eT, int64_t ldeT, void* stream);
+
+/* R10. MX GEMMs on gfx950 scaled MFMA.  All three are
+ *   out[i][j] = sum_k (a[i][k] 2^(ea[i][k/32]-127)) (b[j][k] 2^(eb[j][k/32]-127))
+ * with both operands K-contiguous:
+ *   FProp: a = X row-wise [N x C], b = W row-wise [D x C]          -> y [N x D]
+ *   DGrad: a = dY row-wise [N x D], b = W column-wise [C x D]      -> dx [N x C]
+ *   WGrad: a = dY column-wise [D x N], b = X column-wise [C x N]   -> dw [D x C] */
+FP8B_API int fp8_mx_gemm_fprop(const uint8_t* xq, int64_t ldxq, const uint8_t* xe, int64_t ldxe,
+                      const uint8_t* wq, int64_t ldwq, const uint8_t* we, int64_t ldwe,
+                      void* y, int yt, int64_t ldy, int64_t N, int64_t D, int64_t C, void* stream);
+FP8B_API int fp8_mx_gemm_dgrad(const uint8_t* gq, int64_t ldgq, const uint8_t* ge, int64_t ldge,
+                      const uint8_t* wqT, int64_t ldwqT, const uint8_t* weT, int64_t ldweT,
+                      void* dx, int dxt, int64_t lddx, int64_t N, int64_t D, int64_t C, void* stream);
+FP8B_API int fp8_mx_gemm_wgrad(const uint8_t* gqT, int64_t ldgqT, const uint8_t* geT, int64_t ldgeT,
+                      const uint8_t* xqT, int64_t ldxqT, const uint8_t* xeT, int64_t ldxeT,
+                      void* dw, int dwt, int64_t lddw, int beta,
+                      int64_t N, int64_t D, int64_t C, void* stream);
+
+/* ------------------------------------------------------------------ */
+/* Codec access (for exhaustive checks of the device codec)            */
+/* ------------------------------------------------------------------ */
+
+/* out[i] = E4M3 code of x[i] / s[i] exactly as the quantizers compute it:
+ * fp32 quotient, nearest-even E4M3, saturating; s[i] == 0 gives the signed
+ * zero of x[i].  If s is NULL the divisor is 1 (plain encode of x). */
+FP8B_API int fp8b_e4m3_encode(const float* x, const float* s, int64_t n, uint8_t* out, void* stream);
+
+/* Host-only argument check of the GEMM entry points: runs exactly the
+ * validation the launch would run and returns its status, launching
+ * nothing.  op: 0 FProp, 1 DGrad, 2 WGrad, 3 MX FProp, 4 MX DGrad,
+ * 5 MX WGrad.  Pointers are only tested for NULL and alignment. */
+FP8B_API int fp8b_validate_gemm(int op, const void* a, int64_t lda, const void* sa, int64_t ldsa,
+                       const void* b, int64_t ldb, const void* sb, int64_t ldsb,
+                       const void* out, int out_dtype, int64_t ldo, int beta,
+                       int64_t N, int64_t D, int64_t C);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FP8BLK_H */

@@ -1,0 +1,299 @@
+"""GPU parity of the block-scaled GEMMs (FProp, DGrad, WGrad, grouped MoE)
+against the oracle.  Both sides start from the same seeded inputs; each
+side quantizes with its own code and computes its own GEMMs.  Bar:
+max |y - y_oracle| / ||y_oracle row||_2 <= 2e-3 (the bf16 output rounding
+alone can reach 2^-9 of the row norm); fp32 outputs must in addition sit
+within 2^-12 * sum_k |a_k b_k| of the oracle (the accumulation error scale
+of the fp8 MFMA dot product), a bound that stays meaningful for short or
+cancelling rows.
+
+Full-size launches use exactly the kernels and tile configurations the
+benchmark times; where the oracle cannot cover a full-size output in
+seconds, it computes a seeded sample of rows.
+"""
+import numpy as np
+import pytest
+import torch
+
+import block_scaled_fp8_02_amd as fb
+import oracle
+from block_scaled_fp8_02_amd import workloads as wl
+from gpu_util import TOL, banner, dev, dev_strided, host
+
+pytestmark = pytest.mark.gpu
+
+
+def gpu_layer(X, W, dY, out_dtype=torch.bfloat16):
+    N, C = X.shape
+    D = W.shape[0]
+    xd, wd, gd = dev_strided(X), dev_strided(W), dev_strided(dY)
+    xq, xs = fb.fp8_quantize_act_1x128(xd)
+    wq, ws, wqT = fb.fp8_quantize_weight_128x128(wd)
+    gq, gs = fb.fp8_quantize_act_1x128(gd)
+    gqT, gsT, _, _ = fb.fp8_quantize_transposed(gd)
+    xqT, xsT, _, _ = fb.fp8_quantize_transposed(xd)
+    y = fb.fp8_gemm_fprop(xq, xs, wq, ws, N, D, C, out_dtype=out_dtype)
+    dx = fb.fp8_gemm_dgrad(gq, gs, wqT, ws, N, D, C, out_dtype=out_dtype)
+    dw = fb.fp8_gemm_wgrad(gqT, gsT, xqT, xsT, N, D, C, out_dtype=out_dtype)
+    return host(y), host(dx), host(dw)
+
+
+def oracle_layer(X, W, dY):
+    N, C = X.shape
+    D = W.shape[0]
+    xq, xs = oracle.quant_1x128(X)
+    wq, ws, _ = oracle.quant_128x128(W, with_transpose=False)
+    gq, gs = oracle.quant_1x128(dY)
+    gqT, gsT = oracle.quant_colwise(dY)
+    xqT, xsT = oracle.quant_colwise(X)
+    y = oracle.fprop(xq, xs, wq, ws, C)
+    dx = oracle.dgrad(gq, gs, wq, ws, D, C)
+    dw = oracle.wgrad(gqT, gsT, xqT, xsT, gqT.shape[1])
+    return y, dx, dw
+
+
+def check(got, want, tol, what):
+    err = oracle.rel_row_error(got, want)
+    banner(f"{what}: rel row error {err:.3e} (tol {tol:.0e})")
+    assert err <= tol, f"{what}: {err}"
+
+
+# Accumulation bound for fp32 outputs: |error| <= 2^-12 * sum_k |a_k b_k|.
+# The fp8 MFMA forms each 128-wide block's dot product with a narrower
+# internal sum than fp32 (measured: up to ~1e-4 of sum |a_k b_k| on one
+# block); promoting every block's partial sum into an fp32 accumulator with
+# its scales, as the pages' GEMMs do, keeps the error at that level instead
+# of letting it grow with K.
+ACC_BOUND = 2.0 ** -12
+
+
+def abs_products(X, W, dY):
+    """sum_k |a_k b_k| for every output of the three GEMMs (fp64, oracle
+    dequantization): the scale of the rounding error of any fp32 sum."""
+    N, C = X.shape
+    D = W.shape[0]
+    xq, xs = oracle.quant_1x128(X)
+    wq, ws, _ = oracle.quant_128x128(W, with_transpose=False)
+    gq, gs = oracle.quant_1x128(dY)
+    gqT, gsT = oracle.quant_colwise(dY)
+    xqT, xsT = oracle.quant_colwise(X)
+    K = gqT.shape[1]
+    Xa = np.abs(oracle.deq_rowgroups(xq, xs, C))
+    Wa = np.abs(oracle.deq_128x128(wq, ws, D, C))
+    Ga = np.abs(oracle.deq_rowgroups(gq, gs, D))
+    GTa = np.abs(oracle.deq_rowgroups(gqT, gsT, K))
+    XTa = np.abs(oracle.deq_rowgroups(xqT, xsT, K))
+    return (oracle.matmul_f64(Xa, Wa.T), oracle.matmul_f64(Ga, Wa), oracle.matmul_f64(GTa, XTa.T))
+
+
+def check_f32(got, want, mag, what):
+    """fp32 output: the benchmark spec row-norm metric, and every element within
+    the fp32 accumulation bound of the oracle."""
+    err = oracle.rel_row_error(got, want)
+    ratio = float(np.max(np.abs(got - want) / np.maximum(mag, 1e-300)))
+    banner(f"{what}: rel row error {err:.3e}, |err|/sum|ab| {ratio:.3e} (bound {ACC_BOUND:.1e})")
+    assert err <= TOL, f"{what}: {err}"
+    assert ratio <= ACC_BOUND, f"{what}: {ratio}"
+
+
+def test_tiny_workload_layer():
+    w = wl.tiny(0)
+    banner("tiny layer: FProp/DGrad/WGrad")
+    ref = oracle_layer(w["X"], w["W"], w["dY"])
+    got = gpu_layer(w["X"], w["W"], w["dY"], out_dtype=torch.bfloat16)
+    for g, r, name in zip(got, ref, ("fprop", "dgrad", "wgrad")):
+        check(g, r, TOL, f"tiny {name} bf16")
+    mags = abs_products(w["X"], w["W"], w["dY"])
+    got = gpu_layer(w["X"], w["W"], w["dY"], out_dtype=torch.float32)
+    for g, r, m, name in zip(got, ref, mags, ("fprop", "dgrad", "wgrad")):
+        check_f32(g, r, m, f"tiny {name} f32")
+
+
+@pytest.mark.parametrize("N,D,C", [(1, 16, 1), (3, 130, 300), (200, 300, 260), (320, 400, 640),
+                                   (129, 1, 129), (64, 256, 8), (257, 384, 1024)])
+def test_ragged_layers(N, D, C):
+    banner(f"ragged layer N={N} D={D} C={C}")
+    rng = np.random.default_rng(N * 7 + D * 3 + C)
+    X = (rng.standard_normal((N, C)) * np.exp(rng.uniform(-3, 3, (N, 1)))).astype(np.float32)
+    W = (rng.standard_normal((D, C)) * 0.02).astype(np.float32)
+    dY = (rng.standard_normal((N, D)) * 1e-3).astype(np.float32)
+    ref = oracle_layer(X, W, dY)
+    mags = abs_products(X, W, dY)
+    got = gpu_layer(X, W, dY, out_dtype=torch.float32)
+    for g, r, m, name in zip(got, ref, mags, ("fprop", "dgrad", "wgrad")):
+        check_f32(g, r, m, f"ragged {name}")
+
+
+def test_zero_contraction_gives_zero():
+    """C = 0: every output is an empty sum."""
+    xq = torch.zeros((5, 16), dtype=torch.uint8, device="cuda")[:, :0]
+    xs = torch.zeros((5, 4), dtype=torch.float32, device="cuda")[:, :0]
+    wq = torch.zeros((7, 16), dtype=torch.uint8, device="cuda")[:, :0]
+    ws = torch.zeros((1, 4), dtype=torch.float32, device="cuda")[:, :0]
+    y = torch.full((5, 8), 3.0, dtype=torch.float32, device="cuda")[:, :7]
+    fb.fp8_gemm_fprop(xq, xs, wq, ws, 5, 7, 0, y=y)
+    torch.cuda.synchronize()
+    assert torch.all(y == 0)
+
+
+def test_decode_fprop_full():
+    w = wl.decode(0)
+    banner("decode FProp 64x24576x4096 (full, oracle full)")
+    X, W = w["X"], w["W"]
+    xq, xs = fb.fp8_quantize_act_1x128(dev(X))
+    wq, ws, _ = fb.fp8_quantize_weight_128x128(dev(W), transpose=False)
+    y = host(fb.fp8_gemm_fprop(xq, xs, wq, ws, 64, 24576, 4096))
+    oxq, oxs = oracle.quant_1x128(X)
+    owq, ows, _ = oracle.quant_128x128(W, with_transpose=False)
+    check(y, oracle.fprop(oxq, oxs, owq, ows, 4096), TOL, "decode fprop")
+
+
+def test_train_layer_full_size_sampled():
+    """The three training GEMMs at full size (8192 x 4096 x 12288), checked
+    on seeded samples of output rows against the oracle."""
+    w = wl.train(0)
+    X, W, dY = w["X"], w["W"], w["dY"]
+    N, C, D = 8192, 12288, 4096
+    banner("train: GPU quantize + FProp/DGrad/WGrad at full size")
+    xd, wd, gd = dev(X), dev(W), dev(dY)
+    xqT, xsT, xq, xs = fb.fp8_quantize_transposed(xd, rowwise=True)
+    gqT, gsT, gq, gs = fb.fp8_quantize_transposed(gd, rowwise=True)
+    wq, ws, wqT = fb.fp8_quantize_weight_128x128(wd)
+    y = fb.fp8_gemm_fprop(xq, xs, wq, ws, N, D, C)
+    dx = fb.fp8_gemm_dgrad(gq, gs, wqT, ws, N, D, C)
+    dw = fb.fp8_gemm_wgrad(gqT, gsT, xqT, xsT, N, D, C)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(2024)
+    rows = np.sort(rng.choice(N, 48, replace=False))
+    drows = np.sort(rng.choice(D, 24, replace=False))
+    banner("train: oracle on sampled rows")
+    owq, ows, _ = oracle.quant_128x128(W, with_transpose=False)
+    oxq, oxs = oracle.quant_1x128(X[rows])
+    check(host(y)[rows], oracle.fprop(oxq, oxs, owq, ows, C), TOL, "train fprop (sampled rows)")
+    ogq, ogs = oracle.quant_1x128(dY[rows])
+    check(host(dx)[rows], oracle.dgrad(ogq, ogs, owq, ows, D, C), TOL, "train dgrad (sampled rows)")
+    ogqT, ogsT = oracle.quant_colwise(np.ascontiguousarray(dY[:, drows]))
+    oxqT, oxsT = oracle.quant_colwise(X)
+    check(host(dw)[drows], oracle.wgrad(ogqT, ogsT, oxqT, oxsT, N), TOL, "train wgrad (sampled rows)")
+
+
+def test_unified_forward_is_batch_invariant():
+    """Rollout FProp of 64 tokens equals rows 0..63 of the training-size
+    FProp bit for bit, with the decode weight (Jet-RL: the inference graph
+    is a subgraph of the training forward graph)."""
+    w = wl.decode(0)
+    rng = wl.rng_for(7)
+    X = wl.normal(rng, (8192, 4096), 1.0)
+    wl.add_outlier_channels(rng, X)
+    X = wl.f32_to_bf16_bits(X)
+    banner("batch invariance 64 vs 8192 rows")
+    wq, ws, _ = fb.fp8_quantize_weight_128x128(dev(w["W"]), transpose=False)
+    xq, xs = fb.fp8_quantize_act_1x128(dev(X))
+    y_big = fb.fp8_gemm_fprop(xq, xs, wq, ws, 8192, 24576, 4096)
+    xq64, xs64 = fb.fp8_quantize_act_1x128(dev(X[:64]))
+    y_small = fb.fp8_gemm_fprop(xq64, xs64, wq, ws, 64, 24576, 4096)
+    for m in (1, 17, 100, 256):
+        xqm, xsm = fb.fp8_quantize_act_1x128(dev(X[:m]))
+        ym = fb.fp8_gemm_fprop(xqm, xsm, wq, ws, m, 24576, 4096)
+        assert torch.equal(ym, y_big[:m]), m
+    assert torch.equal(y_small, y_big[:64])
+    y_again = fb.fp8_gemm_fprop(xq, xs, wq, ws, 8192, 24576, 4096)
+    assert torch.equal(y_again, y_big)
+
+
+def test_wgrad_accumulate_fp32():
+    rng = np.random.default_rng(5)
+    N, D, C = 384, 256, 512
+    X = rng.standard_normal((N, C)).astype(np.float32)
+    dY = (rng.standard_normal((N, D)) * 1e-3).astype(np.float32)
+    gqT, gsT, _, _ = fb.fp8_quantize_transposed(dev(dY))
+    xqT, xsT, _, _ = fb.fp8_quantize_transposed(dev(X))
+    base = torch.from_numpy(rng.standard_normal((D, C)).astype(np.float32)).cuda()
+    acc = base.clone()
+    fb.fp8_gemm_wgrad(gqT, gsT, xqT, xsT, N, D, C, dw=acc, beta=1)
+    plain = fb.fp8_gemm_wgrad(gqT, gsT, xqT, xsT, N, D, C, out_dtype=torch.float32)
+    assert torch.equal(acc, base + plain)
+
+
+# ----------------------------------------------------------------- MoE
+def moe_gpu(w):
+    """Grouped FProp/DGrad/WGrad for gate/up and down on the GPU."""
+    offs = w["offsets"]
+    E, I2, H = w["W_gu"].shape
+    I = w["inter"]
+    R = int(offs[-1])
+    offs_d = dev(offs.astype(np.int32))
+    out = {}
+    Wgu = dev(w["W_gu"].reshape(E * I2, H))
+    Wd = dev(w["W_d"].reshape(E * H, I))
+    gu_q, gu_s, gu_qT = fb.fp8_quantize_weight_128x128(Wgu)
+    d_q, d_s, d_qT = fb.fp8_quantize_weight_128x128(Wd)
+    Xd, Ad, dHd, dYd = dev(w["X_perm"]), dev(w["A"]), dev(w["dH"]), dev(w["dY_d"])
+    xqT, xsT, xq, xs = fb.fp8_quantize_transposed_grouped(Xd, offs_d, rowwise=True)
+    aqT, asT, aq, as_ = fb.fp8_quantize_transposed_grouped(Ad, offs_d, rowwise=True)
+    hqT, hsT, hq, hs = fb.fp8_quantize_transposed_grouped(dHd, offs_d, rowwise=True)
+    yqT, ysT, yq, ys = fb.fp8_quantize_transposed_grouped(dYd, offs_d, rowwise=True)
+    # gate/up: H -> 2I
+    out["gu_fprop"] = fb.fp8_gemm_fprop_grouped(xq, xs, gu_q, I2 * gu_q.stride(0), gu_s,
+                                                (I2 // 128) * gu_s.stride(0), offs_d, R, I2, H)
+    out["gu_dgrad"] = fb.fp8_gemm_dgrad_grouped(hq, hs, gu_qT, I2, gu_s, (I2 // 128) * gu_s.stride(0),
+                                                offs_d, R, I2, H)
+    out["gu_wgrad"] = fb.fp8_gemm_wgrad_grouped(hqT, hsT, xqT, xsT, offs_d, R, I2, H)
+    # down: I -> H
+    out["d_fprop"] = fb.fp8_gemm_fprop_grouped(aq, as_, d_q, H * d_q.stride(0), d_s,
+                                               (H // 128) * d_s.stride(0), offs_d, R, H, I)
+    out["d_dgrad"] = fb.fp8_gemm_dgrad_grouped(yq, ys, d_qT, H, d_s, (H // 128) * d_s.stride(0),
+                                               offs_d, R, H, I)
+    out["d_wgrad"] = fb.fp8_gemm_wgrad_grouped(yqT, ysT, aqT, asT, offs_d, R, H, I)
+    torch.cuda.synchronize()
+    return {k: host(v) for k, v in out.items()}
+
+
+def test_moe_grouped_full_launch_sampled_experts():
+    w = wl.moe(0)
+    banner("moe: grouped GEMMs at full size")
+    got = moe_gpu(w)
+    offs = w["offsets"]
+    counts = np.diff(offs)
+    experts = sorted({int(np.argmin(counts)), int(np.argmax(counts)), 0, 63, 127})
+    I = w["inter"]
+    banner(f"moe: oracle on experts {experts}")
+    for e in experts:
+        a, b = int(offs[e]), int(offs[e + 1])
+        n = b - a
+        Wgu, Wd = w["W_gu"][e], w["W_d"][e]
+        for (Xn, Wn, dYn, pre, Dn, Cn) in ((w["X_perm"][a:b], Wgu, w["dH"][a:b], "gu", 2 * I, w["hidden"]),
+                                           (w["A"][a:b], Wd, w["dY_d"][a:b], "d", w["hidden"], I)):
+            y, dx, dw = oracle_layer(Xn, Wn, dYn)
+            check(got[f"{pre}_fprop"][a:b], y, TOL, f"moe e{e} ({n} rows) {pre} fprop")
+            check(got[f"{pre}_dgrad"][a:b], dx, TOL, f"moe e{e} {pre} dgrad")
+            check(got[f"{pre}_wgrad"][e], dw, TOL, f"moe e{e} {pre} wgrad")
+
+
+def test_moe_grouped_edge_segments():
+    banner("grouped GEMMs with empty and tiny experts")
+    rng = np.random.default_rng(11)
+    offs = np.array([0, 0, 1, 129, 129, 400, 700, 700], dtype=np.int32)
+    E, R, H, Dn = 7, 700, 256, 128
+    X = rng.standard_normal((R, H)).astype(np.float32)
+    dY = (rng.standard_normal((R, Dn)) * 1e-3).astype(np.float32)
+    Ws = (rng.standard_normal((E, Dn, H)) * 0.02).astype(np.float32)
+    offs_d = dev(offs)
+    wq, ws, wqT = fb.fp8_quantize_weight_128x128(dev(Ws.reshape(E * Dn, H)))
+    xqT, xsT, xq, xs = fb.fp8_quantize_transposed_grouped(dev(X), offs_d, rowwise=True)
+    gqT, gsT, gq, gs = fb.fp8_quantize_transposed_grouped(dev(dY), offs_d, rowwise=True)
+    y = host(fb.fp8_gemm_fprop_grouped(xq, xs, wq, Dn * wq.stride(0), ws, ws.stride(0), offs_d, R, Dn, H,
+                                       out_dtype=torch.float32))
+    dx = host(fb.fp8_gemm_dgrad_grouped(gq, gs, wqT, Dn, ws, ws.stride(0), offs_d, R, Dn, H,
+                                        out_dtype=torch.float32))
+    dw = host(fb.fp8_gemm_wgrad_grouped(gqT, gsT, xqT, xsT, offs_d, R, Dn, H, out_dtype=torch.float32))
+    for e in range(E):
+        a, b = int(offs[e]), int(offs[e + 1])
+        if b == a:
+            assert np.all(dw[e] == 0)
+            continue
+        ry, rdx, rdw = oracle_layer(X[a:b], Ws[e], dY[a:b])
+        my, mdx, mdw = abs_products(X[a:b], Ws[e], dY[a:b])
+        check_f32(y[a:b], ry, my, f"edge e{e} fprop")
+        check_f32(dx[a:b], rdx, mdx, f"edge e{e} dgrad")
+        check_f32(dw[e], rdw, mdw, f"edge e{e} wgrad")

@@ -1,0 +1,113 @@
+"""GPU parity of the MXFP8 path (Miles blog, MXFP8 paragraphs) against the
+oracle: E4M3 codes and E8M0 bytes bit-exact in both orientations, MX GEMMs
+within the 2e-3 row-norm tolerance, on the decode-shaped MX workload and on
+ragged shapes."""
+import numpy as np
+import pytest
+import torch
+
+import block_scaled_fp8_02_amd as fb
+import oracle
+from block_scaled_fp8_02_amd import workloads as wl
+from gpu_util import TOL, assert_bytes_equal, banner, dev, dev_strided, host
+
+pytestmark = pytest.mark.gpu
+
+
+def check_mx_quant(x_host):
+    q, e, qT, eT = fb.fp8_mx_quantize_1x32(dev_strided(x_host))
+    oq, oe = oracle.mx_quant_rows(x_host)
+    oqT, oeT = oracle.mx_quant_cols(x_host)
+    assert_bytes_equal(host(q), oq, "mx row codes")
+    assert_bytes_equal(host(e), oe, "mx row scales")
+    assert_bytes_equal(host(qT), oqT, "mx col codes")
+    assert_bytes_equal(host(eT), oeT, "mx col scales")
+
+
+@pytest.mark.parametrize("shape", [(1, 1), (3, 300), (129, 257), (64, 4096), (300, 33)])
+def test_mx_quant_ragged(shape):
+    banner(f"mx quant {shape}")
+    rng = np.random.default_rng(sum(shape) + 1)
+    x = (rng.standard_normal(shape) * np.exp(rng.uniform(-20, 20, shape))).astype(np.float32)
+    x[0, :min(32, shape[1])] = 0.0
+    check_mx_quant(x)
+    check_mx_quant(wl.f32_to_bf16_bits(x))
+
+
+def test_mx_quant_classes():
+    x = np.zeros((64, 256), np.float32)
+    x[1] = np.finfo(np.float32).max
+    x[2] = np.uint32(1).view(np.float32)
+    x[3] = -0.0
+    x[4, ::3] = 448.0 * 2.0 ** -130
+    x[5] = np.linspace(-3, 3, 256).astype(np.float32)
+    check_mx_quant(x)
+
+
+def test_mx_workload_full():
+    w = wl.mx(0)
+    banner("mx workload: quantize X, W, dY in both orientations; FProp/DGrad/WGrad")
+    X, W, dY = w["X"], w["W"], w["dY"]
+    N, C, D = 64, 4096, 24576
+    xq, xe, xqT, xeT = fb.fp8_mx_quantize_1x32(dev(X))
+    wq, we, wqT, weT = fb.fp8_mx_quantize_1x32(dev(W))
+    gq, ge, gqT, geT = fb.fp8_mx_quantize_1x32(dev(dY))
+    y = host(fb.fp8_mx_gemm_fprop(xq, xe, wq, we, N, D, C))
+    dx = host(fb.fp8_mx_gemm_dgrad(gq, ge, wqT, weT, N, D, C))
+    dw = fb.fp8_mx_gemm_wgrad(gqT, geT, xqT, xeT, N, D, C)
+    torch.cuda.synchronize()
+    banner("mx workload: oracle")
+    oxq, oxe = oracle.mx_quant_rows(X)
+    owq, owe = oracle.mx_quant_rows(W)
+    assert_bytes_equal(host(wq), owq, "mx W row codes")
+    assert_bytes_equal(host(we), owe, "mx W row scales")
+    owqT, oweT = oracle.mx_quant_cols(W)
+    assert_bytes_equal(host(wqT), owqT, "mx W col codes")
+    assert_bytes_equal(host(weT), oweT, "mx W col scales")
+    ogq, oge = oracle.mx_quant_rows(dY)
+    y_ref = oracle.mx_gemm(oxq, oxe, owq, owe, C)
+    err = oracle.rel_row_error(y, y_ref)
+    banner(f"mx fprop err {err:.3e}")
+    assert err <= TOL
+    dx_ref = oracle.mx_gemm(ogq, oge, owqT, oweT, D)
+    err = oracle.rel_row_error(dx, dx_ref)
+    banner(f"mx dgrad err {err:.3e}")
+    assert err <= TOL
+    rows = np.sort(np.random.default_rng(3).choice(D, 256, replace=False))
+    ogqT, ogeT = oracle.mx_quant_cols(np.ascontiguousarray(dY[:, rows]))
+    oxqT, oxeT = oracle.mx_quant_cols(X)
+    dw_ref = oracle.mx_gemm(ogqT, ogeT, oxqT, oxeT, N)
+    err = oracle.rel_row_error(host(dw)[rows], dw_ref)
+    banner(f"mx wgrad err (sampled rows) {err:.3e}")
+    assert err <= TOL
+
+
+@pytest.mark.parametrize("N,D,C", [(1, 16, 32), (3, 130, 300), (200, 300, 260), (257, 384, 1024)])
+def test_mx_gemm_ragged(N, D, C):
+    rng = np.random.default_rng(N + D + C)
+    X = (rng.standard_normal((N, C)) * np.exp(rng.uniform(-3, 3, (N, C)))).astype(np.float32)
+    W = (rng.standard_normal((D, C)) * 0.02).astype(np.float32)
+    dY = (rng.standard_normal((N, D)) * 1e-3).astype(np.float32)
+    xq, xe, xqT, xeT = fb.fp8_mx_quantize_1x32(dev_strided(X))
+    wq, we, wqT, weT = fb.fp8_mx_quantize_1x32(dev_strided(W))
+    gq, ge, gqT, geT = fb.fp8_mx_quantize_1x32(dev_strided(dY))
+    y = host(fb.fp8_mx_gemm_fprop(xq, xe, wq, we, N, D, C, out_dtype=torch.float32))
+    dx = host(fb.fp8_mx_gemm_dgrad(gq, ge, wqT, weT, N, D, C, out_dtype=torch.float32))
+    dw = host(fb.fp8_mx_gemm_wgrad(gqT, geT, xqT, xeT, N, D, C, out_dtype=torch.float32))
+    oxq, oxe = oracle.mx_quant_rows(X)
+    owq, owe = oracle.mx_quant_rows(W)
+    owqT, oweT = oracle.mx_quant_cols(W)
+    ogq, oge = oracle.mx_quant_rows(dY)
+    ogqT, ogeT = oracle.mx_quant_cols(dY)
+    oxqT, oxeT = oracle.mx_quant_cols(X)
+    mag = {"fprop": oracle.matmul_f64(np.abs(oracle.deq_mx(oxq, oxe, C)), np.abs(oracle.deq_mx(owq, owe, C)).T),
+           "dgrad": oracle.matmul_f64(np.abs(oracle.deq_mx(ogq, oge, D)), np.abs(oracle.deq_mx(owqT, oweT, D)).T),
+           "wgrad": oracle.matmul_f64(np.abs(oracle.deq_mx(ogqT, ogeT, N)), np.abs(oracle.deq_mx(oxqT, oxeT, N)).T)}
+    for got, ref, name in ((y, oracle.mx_gemm(oxq, oxe, owq, owe, C), "fprop"),
+                           (dx, oracle.mx_gemm(ogq, oge, owqT, oweT, D), "dgrad"),
+                           (dw, oracle.mx_gemm(ogqT, ogeT, oxqT, oxeT, N), "wgrad")):
+        err = oracle.rel_row_error(got, ref)
+        ratio = float(np.max(np.abs(got - ref) / np.maximum(mag[name], 1e-300)))
+        banner(f"mx ragged {name} N={N} D={D} C={C}: {err:.3e}, |err|/sum|ab| {ratio:.3e}")
+        assert err <= TOL
+        assert ratio <= 2.0 ** -12          # fp8 MFMA dot-product accumulation scale

@@ -1,8 +1,8 @@
 """Pins for the oracle's block-scaled GEMMs (CPU only).
 
 * Exact rational brute force (fractions.Fraction over the decoded codes and
-  the fp32 scales) on 2x128x128 and 2x128x256 problems for FProp, DGrad and
-  WGrad, with scales that differ from block to block so a wrong scale index
+  the fp32 scales) on two-row problems with one or two 128-wide blocks on
+  the other axes, for FProp, DGrad and WGrad, with scales that differ from block to block so a wrong scale index
   or a transposed operand fails.  The oracle's fp64 sums must sit within the
   standard fp64 summation bound of the exact values.
 * The lossless case reduces to a plain fp64 matrix product of the original
