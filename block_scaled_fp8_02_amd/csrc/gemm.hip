@@ -19,43 +19,26 @@
 //     lane's four results share one P row (one token) and, for the
 //     128x128-scaled weight, one Q block: the combined scale is a single
 //     value per lane and P sub-tile;
-//   * 128-row tiles of P and Q are staged through LDS, double-buffered with
-//     one barrier per K block; 16-byte chunks are XOR-swizzled by row so
-//     the MFMA fragment reads are conflict-free;
+//   * P and Q tiles of one K block go global -> LDS by direct DMA
+//     (global_load_lds_dwordx4, no register staging), double-buffered with
+//     one barrier per K block; the next block's DMA and scale loads are in
+//     flight while the current one is multiplied.  16-byte chunks are
+//     XOR-swizzled by row (the DMA lane picks the source chunk that belongs
+//     in its LDS slot), so the MFMA fragment reads are conflict-free;
+//   * blocks are renumbered so that the tiles resident on one XCD (one L2)
+//     at a time form a compact patch of the output and share operands;
 //   * the MX variant feeds the E8M0 block scales to the scaled MFMA and
 //     accumulates across all K blocks in the matrix core.
 //
 // The reduction order of an output element is fixed: ascending K blocks,
-// one MFMA per block, one FMA per block.  It does not depend on the tile
-// shape or on M, which makes row i of the output a function of row i of P
-// alone (rollout and training forward agree bit for bit).
+// one MFMA per block, one FMA per block (one scaled MFMA per block for MX).
+// It does not depend on the tile shape or on M, which makes row i of the
+// output a function of row i of P alone (rollout and training forward
+// agree bit for bit).
 #include "device_common.hpp"
 #include "kernels.hpp"
 
 namespace fp8blk {
-
-struct TileInfo {
-    int64_t i0, ihi;        // P/O rows [i0, ihi) of this tile (ihi clipped to the segment)
-    int64_t kbase, KB;      // first K block and number of K blocks
-    int64_t e;              // expert (grouped modes), else 0
-};
-
-__device__ __forceinline__ void find_row_tile(const int32_t* off, int64_t E, int64_t tile, int64_t BI,
-                                              TileInfo& ti) {
-    int64_t acc = 0;
-    for (int64_t e = 0; e < E; ++e) {
-        const int64_t a = off[e], b = off[e + 1];
-        const int64_t tiles = (b - a + BI - 1) / BI;
-        if (tile < acc + tiles) {
-            ti.i0 = a + (tile - acc) * BI;
-            ti.ihi = ti.i0 + BI < b ? ti.i0 + BI : b;
-            ti.e = e;
-            return;
-        }
-        acc += tiles;
-    }
-    ti.i0 = 0; ti.ihi = 0; ti.e = -1;
-}
 
 // MFMA operand fragment of one row: lane group g = lane/16 takes the 16-byte
 // chunks g and g+4 of the row's 128 K bytes, which is the K order of the
@@ -71,92 +54,170 @@ __device__ __forceinline__ v8i lds_frag(const uint8_t* base, int row, int lane) 
     return r;
 }
 
-// BI x BJ block tile, 4 waves, wave tile (16*TI) x (16*TJ).
-template <int BI, int BJ, int TI, int TJ, int SM>
-__global__ __launch_bounds__(256, 2) void k_gemm(GemmArgs g) {
+// Tile index -> (tile row, tile col) with groups of GM tile rows walked
+// column by column, so consecutive indices form GM x k patches.
+__device__ __forceinline__ void grouped_tile(int64_t t, int64_t nbi, int64_t nbj, int64_t GM,
+                                             int64_t& ti, int64_t& tj) {
+    const int64_t per_group = GM * nbj;
+    const int64_t group = t / per_group;
+    const int64_t first = group * GM;
+    const int64_t rows = nbi - first < GM ? nbi - first : GM;
+    const int64_t r = t - group * per_group;
+    ti = first + r % rows;
+    tj = r / rows;
+}
+
+// Consecutive block ids are dealt round-robin to the 8 XCDs; renumber so
+// that each XCD works on a contiguous range of logical tiles.
+__device__ __forceinline__ int64_t xcd_remap(int64_t b, int64_t total) {
+    if (total % 8 != 0) return b;
+    return (b % 8) * (total / 8) + b / 8;
+}
+
+// Row tile `tile` of the grouped (MoE) row enumeration -> rows [i0, ihi) of expert e.
+__device__ __forceinline__ void find_row_tile(const int32_t* off, int64_t E, int64_t tile, int64_t BI,
+                                              int64_t& i0, int64_t& ihi, int64_t& e_out) {
+    int64_t acc = 0;
+    for (int64_t e = 0; e < E; ++e) {
+        const int64_t a = off[e], b = off[e + 1];
+        const int64_t tiles = (b - a + BI - 1) / BI;
+        if (tile < acc + tiles) {
+            i0 = a + (tile - acc) * BI;
+            ihi = i0 + BI < b ? i0 + BI : b;
+            e_out = e;
+            return;
+        }
+        acc += tiles;
+    }
+    i0 = 0; ihi = 0; e_out = -1;
+}
+
+// BI x BJ block tile, NW waves, wave tile (16*TI) x (16*TJ).
+template <int BI, int BJ, int TI, int TJ, int NW, int SM>
+__global__ __launch_bounds__(64 * NW, 1) void k_gemm(GemmArgs g) {
+    constexpr int NT = 64 * NW;
     constexpr int WI = 16 * TI, WJ = 16 * TJ;
     constexpr int NWI = BI / WI, NWJ = BJ / WJ;
-    static_assert(NWI * NWJ == 4, "four waves per block");
+    static_assert(NWI * NWJ == NW, "wave grid must cover the block tile");
     static_assert(SM != SCALE_Q_BLOCK || (128 % WJ == 0), "a wave's Q rows must sit in one 128-row block");
-    constexpr int PCH = BI * 8 / 256, QCH = BJ * 8 / 256;   // 16-byte chunks per thread per K block
-    static_assert(PCH >= 1 && QCH >= 1, "tile too small for 256 loaders");
     constexpr int STAGE = (BI + BJ) * 128;
+    constexpr int NCH = (BI + BJ) * 8 / NT;                 // 16-byte DMA chunks per thread per stage
+    static_assert(NCH * NT == (BI + BJ) * 8, "DMA chunks must divide evenly");
+    static_assert(BI + BJ <= NT, "one scale loader per tile row");
 
     __shared__ __attribute__((aligned(16))) uint8_t smem[2 * STAGE];
+    // Per K block, one 32-bit scale word per tile row (P rows, then Q rows):
+    // the fp32 group/block scale, or for MX the four E8M0 bytes of the row's
+    // four 32-wide sub-blocks.
+    __shared__ __attribute__((aligned(16))) uint32_t sscale[2][NT];
     __shared__ int64_t tinfo[4];
 
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int wi = wave % NWI, wj = wave / NWI;
 
     // ---------------------------------------------------- tile setup
-    TileInfo ti;
     const uint8_t* Q = g.Q;
     const char* sQ = static_cast<const char*>(g.sQ);
     char* O = static_cast<char*>(g.O);
-    const int64_t j0 = (int64_t)blockIdx.x * BJ;
-    const int64_t KBall = (g.K + 127) / 128;
     const size_t sq_elem = SM == SCALE_MX ? 1 : 4;
     const size_t o_elem = g.out_f32 ? 4 : 2;
+    const int64_t nbj = (g.Nn + BJ - 1) / BJ;
+    int64_t i0, ihi, j0, kbase = 0, KB = (g.K + 127) / 128;
     if (g.group_mode == GROUP_ROWS) {
         if (tid == 0) {
-            TileInfo t0;
-            find_row_tile(g.offsets, g.E, blockIdx.y, BI, t0);
-            tinfo[0] = t0.i0; tinfo[1] = t0.ihi; tinfo[2] = t0.e;
+            int64_t a, b, e;
+            find_row_tile(g.offsets, g.E, blockIdx.y, BI, a, b, e);
+            tinfo[0] = a; tinfo[1] = b; tinfo[2] = e;
         }
         __syncthreads();
-        ti.i0 = tinfo[0]; ti.ihi = tinfo[1]; ti.e = tinfo[2];
-        if (ti.e < 0) return;                                        // whole block
-        ti.kbase = 0; ti.KB = KBall;
-        Q += ti.e * g.q_estride;
-        sQ += ti.e * g.sq_estride * sq_elem;
-    } else if (g.group_mode == GROUP_K) {
-        if (tid == 0) {
-            int64_t P = 0;
-            for (int64_t e = 0; e < (int64_t)blockIdx.z; ++e)
-                P += (g.offsets[e + 1] - g.offsets[e] + 127) / 128 * 128;
-            tinfo[0] = P / 128;
-            tinfo[1] = (g.offsets[blockIdx.z + 1] - g.offsets[blockIdx.z] + 127) / 128;
-        }
-        __syncthreads();
-        ti.kbase = tinfo[0]; ti.KB = tinfo[1];
-        ti.i0 = (int64_t)blockIdx.y * BI;
-        ti.ihi = ti.i0 + BI < g.M ? ti.i0 + BI : g.M;
-        ti.e = blockIdx.z;
-        O += ti.e * g.o_estride * o_elem;
+        i0 = tinfo[0]; ihi = tinfo[1];
+        const int64_t e = tinfo[2];
+        if (e < 0) return;                                         // whole block
+        j0 = (int64_t)blockIdx.x * BJ;
+        Q += e * g.q_estride;
+        sQ += e * g.sq_estride * sq_elem;
     } else {
-        ti.i0 = (int64_t)blockIdx.y * BI;
-        ti.ihi = ti.i0 + BI < g.M ? ti.i0 + BI : g.M;
-        ti.kbase = 0; ti.KB = KBall; ti.e = 0;
+        const int64_t nbi = (g.M + BI - 1) / BI;
+        int64_t ti, tj;
+        grouped_tile(xcd_remap(blockIdx.x, nbi * nbj), nbi, nbj, 4, ti, tj);
+        i0 = ti * BI;
+        ihi = i0 + BI < g.M ? i0 + BI : g.M;
+        j0 = tj * BJ;
+        if (g.group_mode == GROUP_K) {
+            const int64_t e = blockIdx.y;
+            if (tid == 0) {
+                int64_t P = 0;
+                for (int64_t x = 0; x < e; ++x) P += (g.offsets[x + 1] - g.offsets[x] + 127) / 128 * 128;
+                tinfo[0] = P / 128;
+                tinfo[1] = (g.offsets[e + 1] - g.offsets[e] + 127) / 128;
+            }
+            __syncthreads();
+            kbase = tinfo[0];
+            KB = tinfo[1];
+            O += e * g.o_estride * o_elem;
+        }
     }
     const int64_t jhi = j0 + BJ < g.Nn ? j0 + BJ : g.Nn;
 
-    // ---------------------------------------------------- global -> LDS staging
-    uint4 rp[PCH], rq[QCH];
-    const uint8_t* gp[PCH];
-    const uint8_t* gq[QCH];
+    // ---------------------------------------------------- DMA addressing
+    // Chunk q = c*NT + tid of a stage lands at LDS byte 16*q: row q/8,
+    // physical chunk q%8, which holds logical chunk (q%8) ^ (row&7).
+    const uint8_t* src[NCH];
 #pragma unroll
-    for (int c = 0; c < PCH; ++c) {
-        const int idx = tid + 256 * c, row = idx >> 3, ch = idx & 7;
-        int64_t r = ti.i0 + row;
-        r = r < ti.ihi ? r : ti.ihi - 1;                            // clamp: rows past the edge are never stored
-        gp[c] = g.P + r * g.ldp + ti.kbase * 128 + ch * 16;
+    for (int c = 0; c < NCH; ++c) {
+        const int q = c * NT + tid, row = q >> 3, lch = (q & 7) ^ (row & 7);
+        if (row < BI) {
+            int64_t r = i0 + row;
+            r = r < ihi ? r : ihi - 1;                             // clamp: rows past the edge are never stored
+            src[c] = g.P + r * g.ldp + kbase * 128 + lch * 16;
+        } else {
+            int64_t r = j0 + row - BI;
+            r = r < jhi ? r : jhi - 1;
+            src[c] = Q + r * g.ldq + kbase * 128 + lch * 16;
+        }
     }
-#pragma unroll
-    for (int c = 0; c < QCH; ++c) {
-        const int idx = tid + 256 * c, row = idx >> 3, ch = idx & 7;
-        int64_t r = j0 + row;
+
+    // ---------------------------------------------------- scale loader
+    // Thread t < BI+BJ fetches the scale word of tile row t for each K block
+    // (the others fetch a valid word they never use, which keeps the K loop
+    // free of branches).
+    const char* sbase;
+    int64_t sstep;                                                  // bytes per K block
+    if (tid < BI) {
+        int64_t r = i0 + tid;
+        r = r < ihi ? r : ihi - 1;
+        sbase = static_cast<const char*>(g.sP) + (r * g.ldsp + (SM == SCALE_MX ? kbase * 4 : kbase)) * sq_elem;
+        sstep = SM == SCALE_MX ? 4 : 4;
+    } else {
+        int64_t r = j0 + (tid < BI + BJ ? tid - BI : 0);
         r = r < jhi ? r : jhi - 1;
-        gq[c] = Q + r * g.ldq + ti.kbase * 128 + ch * 16;
+        const int64_t rr = SM == SCALE_Q_BLOCK ? r / 128 : r;
+        sbase = sQ + (rr * g.sq_rs + (SM == SCALE_MX ? kbase * 4 : kbase * g.sq_ks)) * sq_elem;
+        sstep = SM == SCALE_MX ? 4 : 4 * g.sq_ks;
     }
-    // ---------------------------------------------------- scale addressing
-    // P rows of this lane's B fragments, Q rows of its A fragments.
-    int64_t prow[TI];
-#pragma unroll
-    for (int t = 0; t < TI; ++t) {
-        int64_t r = ti.i0 + wi * WI + t * 16 + (lane & 15);
-        prow[t] = r < ti.ihi ? r : ti.ihi - 1;
-    }
-    const int64_t jw = j0 + wj * WJ;                               // first Q row of this wave
+    auto load_scale = [&](int64_t kb) -> uint32_t {
+        return *reinterpret_cast<const uint32_t*>(sbase + kb * sstep);
+    };
+
+    // global_load_lds_dwordx4 writes lane l's 16 bytes to LDS at m0 + 16*l.
+    // It is issued from inline assembly so that the compiler, which cannot
+    // tell the stage being filled from the stage being read, does not stall
+    // the fragment reads on it; completion is awaited explicitly before the
+    // barrier that ends each K step.
+    const uint32_t lds_base = (uint32_t)(uintptr_t)smem;
+#define FP8B_DMA(kb_, buf_)                                                                         \
+    do {                                                                                            \
+        _Pragma("unroll") for (int c = 0; c < NCH; ++c) {                                           \
+            const uint32_t la = __builtin_amdgcn_readfirstlane(                                     \
+                lds_base + (uint32_t)((buf_) * STAGE + (c * NT + wave * 64) * 16));                 \
+            const uint8_t* ga = src[c] + (kb_) * 128;                                               \
+            uint32_t m0save;                                                                        \
+            asm volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %1\n\t"                                \
+                         "global_load_lds_dwordx4 %2, off\n\ts_mov_b32 m0, %0"                      \
+                         : "=&s"(m0save) : "s"(la), "v"(ga) : "memory");                           \
+        }                                                                                           \
+    } while (0)
 
     v4f acc[TJ][TI];
 #pragma unroll
@@ -164,123 +225,95 @@ __global__ __launch_bounds__(256, 2) void k_gemm(GemmArgs g) {
 #pragma unroll
         for (int b = 0; b < TI; ++b) acc[a][b] = v4f{0.f, 0.f, 0.f, 0.f};
 
-#define FP8B_GLOAD(kb_)                                                                    \
-    do {                                                                                   \
-        _Pragma("unroll") for (int c = 0; c < PCH; ++c)                                    \
-            rp[c] = *reinterpret_cast<const uint4*>(gp[c] + (kb_) * 128);                  \
-        _Pragma("unroll") for (int c = 0; c < QCH; ++c)                                    \
-            rq[c] = *reinterpret_cast<const uint4*>(gq[c] + (kb_) * 128);                  \
-    } while (0)
-#define FP8B_SSTORE(buf_)                                                                  \
-    do {                                                                                   \
-        uint8_t* sb_ = smem + (buf_) * STAGE;                                              \
-        _Pragma("unroll") for (int c = 0; c < PCH; ++c) {                                  \
-            const int idx = tid + 256 * c, row = idx >> 3, ch = idx & 7;                   \
-            *reinterpret_cast<uint4*>(sb_ + row * 128 + ((ch ^ (row & 7)) << 4)) = rp[c];  \
-        }                                                                                  \
-        _Pragma("unroll") for (int c = 0; c < QCH; ++c) {                                  \
-            const int idx = tid + 256 * c, row = BI + (idx >> 3), ch = idx & 7;            \
-            *reinterpret_cast<uint4*>(sb_ + row * 128 + ((ch ^ (row & 7)) << 4)) = rq[c];  \
-        }                                                                                  \
-    } while (0)
-
-    if (ti.KB > 0) {
-        FP8B_GLOAD(0);
-        FP8B_SSTORE(0);
+    if (KB > 0) {
+        FP8B_DMA(0, 0);
+        sscale[0][tid] = load_scale(0);
     }
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
 
-    for (int64_t kb = 0; kb < ti.KB; ++kb) {
+    const int prow_l = wi * WI + (lane & 15);                        // tile row of this lane's first P fragment
+    const int qrow_l = BI + wj * WJ;                                 // tile row of this wave's first Q row
+    for (int64_t kb = 0; kb < KB; ++kb) {
         const int buf = (int)(kb & 1);
-        // unconditional prefetch (the last iteration re-reads its own block)
-        // keeps the staging registers out of scratch memory
-        FP8B_GLOAD(kb + 1 < ti.KB ? kb + 1 : kb);
-        const int64_t kg = ti.kbase + kb;                          // global K-block index
-
+        const int64_t kn = kb + 1 < KB ? kb + 1 : kb;             // the last block reloads itself into
+        FP8B_DMA(kn, buf ^ 1);                                     // the idle stage: no branch in the loop
+        const uint32_t snext = load_scale(kn);
         const uint8_t* base = smem + buf * STAGE;
-        v8i af[TJ], bf[TI];
-#pragma unroll
-        for (int t = 0; t < TJ; ++t) af[t] = lds_frag(base, BI + wj * WJ + t * 16 + (lane & 15), lane);
-#pragma unroll
-        for (int t = 0; t < TI; ++t) bf[t] = lds_frag(base, wi * WI + t * 16 + (lane & 15), lane);
+        const uint32_t* sc = sscale[buf];
 
-        if constexpr (SM == SCALE_MX) {
-            const uint8_t* eP = static_cast<const uint8_t*>(g.sP);
-            const uint8_t* eQ = reinterpret_cast<const uint8_t*>(sQ);
-            const int kq = (int)(kg * 4 + (lane >> 4));
-            int sa[TJ], sb[TI];
+        // P fragments and P-side scales for the whole K block; Q fragments
+        // stream through a two-deep register pipeline (the next Q sub-tile's
+        // LDS reads are in flight while the current one is multiplied).
+        const int sh = 8 * (lane >> 4);
+        v8i bf[TI];
+        float sp[TI];
+        int eb[TI];
 #pragma unroll
-            for (int t = 0; t < TJ; ++t) {
-                int64_t r = jw + t * 16 + (lane & 15);
-                r = r < jhi ? r : jhi - 1;
-                sa[t] = eQ[r * g.sq_rs + kq];
-            }
-#pragma unroll
-            for (int t = 0; t < TI; ++t) sb[t] = eP[prow[t] * g.ldsp + kq];
-#pragma unroll
-            for (int a = 0; a < TJ; ++a)
-#pragma unroll
-                for (int b = 0; b < TI; ++b)
-                    acc[a][b] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(af[a], bf[b], acc[a][b],
-                                                                                  0, 0, 0, sa[a], 0, sb[b]);
-        } else {
-            const float* sPf = static_cast<const float*>(g.sP);
-            const float* sQf = reinterpret_cast<const float*>(sQ);
-            float sp[TI];
-#pragma unroll
-            for (int t = 0; t < TI; ++t) sp[t] = sPf[prow[t] * g.ldsp + kg];
-            if constexpr (SM == SCALE_Q_BLOCK) {
-                const float sq = sQf[(jw / 128) * g.sq_rs + kg * g.sq_ks];
-                float cmb[TI];
-#pragma unroll
-                for (int t = 0; t < TI; ++t) cmb[t] = sp[t] * sq;
-#pragma unroll
-                for (int a = 0; a < TJ; ++a)
-#pragma unroll
-                    for (int b = 0; b < TI; ++b) {
-                        const v4f pr = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
-                            af[a], bf[b], v4f{0.f, 0.f, 0.f, 0.f}, 0, 0, 0, 0, 0, 0);
-#pragma unroll
-                        for (int r = 0; r < 4; ++r) acc[a][b][r] = __builtin_fmaf(pr[r], cmb[b], acc[a][b][r]);
-                    }
-            } else {
-                float sq[TJ][4];
-#pragma unroll
-                for (int a = 0; a < TJ; ++a)
-#pragma unroll
-                    for (int r = 0; r < 4; ++r) {
-                        int64_t j = jw + a * 16 + 4 * (lane >> 4) + r;
-                        j = j < jhi ? j : jhi - 1;
-                        sq[a][r] = sQf[j * g.sq_rs + kg * g.sq_ks];
-                    }
-#pragma unroll
-                for (int a = 0; a < TJ; ++a)
-#pragma unroll
-                    for (int b = 0; b < TI; ++b) {
-                        const v4f pr = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
-                            af[a], bf[b], v4f{0.f, 0.f, 0.f, 0.f}, 0, 0, 0, 0, 0, 0);
-#pragma unroll
-                        for (int r = 0; r < 4; ++r)
-                            acc[a][b][r] = __builtin_fmaf(pr[r], sp[b] * sq[a][r], acc[a][b][r]);
-                    }
-            }
+        for (int t = 0; t < TI; ++t) {
+            bf[t] = lds_frag(base, prow_l + t * 16, lane);
+            const uint32_t w = sc[prow_l + t * 16];
+            sp[t] = __uint_as_float(w);
+            eb[t] = (int)((w >> sh) & 0xFFu);
         }
-
-        if (kb + 1 < ti.KB) FP8B_SSTORE(buf ^ 1);
+        if constexpr (SM == SCALE_Q_BLOCK) {
+            const float sq = __uint_as_float(sc[qrow_l]);
+#pragma unroll
+            for (int t = 0; t < TI; ++t) sp[t] *= sq;                 // combined scale per P sub-tile
+        }
+        v8i af = lds_frag(base, qrow_l + (lane & 15), lane);
+        uint4 sqa = *reinterpret_cast<const uint4*>(&sc[qrow_l + 4 * (lane >> 4)]);
+        uint32_t eaw = sc[qrow_l + (lane & 15)];
+#pragma unroll
+        for (int a = 0; a < TJ; ++a) {
+            v8i af_n = af;
+            uint4 sqa_n = sqa;
+            uint32_t eaw_n = eaw;
+            if (a + 1 < TJ) {
+                const int qr = qrow_l + (a + 1) * 16;
+                af_n = lds_frag(base, qr + (lane & 15), lane);
+                if constexpr (SM == SCALE_Q_ROW) sqa_n = *reinterpret_cast<const uint4*>(&sc[qr + 4 * (lane >> 4)]);
+                if constexpr (SM == SCALE_MX) eaw_n = sc[qr + (lane & 15)];
+            }
+#pragma unroll
+            for (int b = 0; b < TI; ++b) {
+                if constexpr (SM == SCALE_MX) {
+                    acc[a][b] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+                        af, bf[b], acc[a][b], 0, 0, 0, (int)((eaw >> sh) & 0xFFu), 0, eb[b]);
+                } else {
+                    const v4f pr = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+                        af, bf[b], v4f{0.f, 0.f, 0.f, 0.f}, 0, 0, 0, 0, 0, 0);
+                    if constexpr (SM == SCALE_Q_BLOCK) {
+#pragma unroll
+                        for (int r = 0; r < 4; ++r) acc[a][b][r] = __builtin_fmaf(pr[r], sp[b], acc[a][b][r]);
+                    } else {
+                        acc[a][b][0] = __builtin_fmaf(pr[0], sp[b] * __uint_as_float(sqa.x), acc[a][b][0]);
+                        acc[a][b][1] = __builtin_fmaf(pr[1], sp[b] * __uint_as_float(sqa.y), acc[a][b][1]);
+                        acc[a][b][2] = __builtin_fmaf(pr[2], sp[b] * __uint_as_float(sqa.z), acc[a][b][2]);
+                        acc[a][b][3] = __builtin_fmaf(pr[3], sp[b] * __uint_as_float(sqa.w), acc[a][b][3]);
+                    }
+                }
+            }
+            af = af_n;
+            sqa = sqa_n;
+            eaw = eaw_n;
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        sscale[buf ^ 1][tid] = snext;
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");           // next stage's DMA has landed
         __syncthreads();
     }
-
-#undef FP8B_GLOAD
-#undef FP8B_SSTORE
+#undef FP8B_DMA
 
     // ---------------------------------------------------- epilogue
+    const int64_t jw = j0 + wj * WJ;
 #pragma unroll
     for (int a = 0; a < TJ; ++a) {
         const int64_t j = jw + a * 16 + 4 * (lane >> 4);
 #pragma unroll
         for (int b = 0; b < TI; ++b) {
-            const int64_t i = ti.i0 + wi * WI + b * 16 + (lane & 15);
-            if (i >= ti.ihi) continue;
+            const int64_t i = i0 + wi * WI + b * 16 + (lane & 15);
+            if (i >= ihi) continue;
             const v4f r = acc[a][b];
             if (g.out_f32) {
                 float* o = reinterpret_cast<float*>(O) + i * g.ldo + j;
@@ -313,26 +346,35 @@ __global__ __launch_bounds__(256, 2) void k_gemm(GemmArgs g) {
     }
 }
 
-template <int BI, int BJ, int TI, int TJ, int SM>
+template <int BI, int BJ, int TI, int TJ, int NW, int SM>
 static hipError_t launch_cfg(const GemmArgs& a, hipStream_t st) {
-    const int64_t jt = (a.Nn + BJ - 1) / BJ;
-    int64_t it, z = 1;
-    if (a.group_mode == GROUP_ROWS) it = (a.M + BI - 1) / BI + a.E;
-    else it = (a.M + BI - 1) / BI;
-    if (a.group_mode == GROUP_K) z = a.E;
-    if (jt == 0 || it == 0 || z == 0) return hipSuccess;
-    if (jt > 0x7FFFFFFF || it > 65535 || z > 65535) return hipErrorInvalidValue;
-    k_gemm<BI, BJ, TI, TJ, SM><<<dim3((unsigned)jt, (unsigned)it, (unsigned)z), 256, 0, st>>>(a);
+    const int64_t nbj = (a.Nn + BJ - 1) / BJ;
+    const int64_t nbi = (a.M + BI - 1) / BI;
+    dim3 grid;
+    if (a.group_mode == GROUP_ROWS) {
+        const int64_t rt = nbi + a.E;                              // bound on the experts' row tiles
+        if (nbj == 0 || rt == 0) return hipSuccess;
+        if (nbj > 0x7FFFFFFF || rt > 65535) return hipErrorInvalidValue;
+        grid = dim3((unsigned)nbj, (unsigned)rt, 1);
+    } else {
+        const int64_t tiles = nbi * nbj;
+        const int64_t z = a.group_mode == GROUP_K ? a.E : 1;
+        if (tiles == 0 || z == 0) return hipSuccess;
+        if (tiles > 0x7FFFFFFF || z > 65535) return hipErrorInvalidValue;
+        grid = dim3((unsigned)tiles, (unsigned)z, 1);
+    }
+    k_gemm<BI, BJ, TI, TJ, NW, SM><<<grid, 64 * NW, 0, st>>>(a);
     return hipGetLastError();
 }
 
 template <int SM>
 static hipError_t launch_sm(const GemmArgs& a, hipStream_t st) {
-    // Small-M (decode) problems take 64-row tiles so the weight stream is
-    // spread over more blocks; the per-element arithmetic is identical.
+    // Small-M (decode) problems take 64x64 tiles so the weight stream is
+    // spread over many blocks; large problems take 256x256 tiles with eight
+    // waves (two per SIMD).  The per-element arithmetic is the same in both.
     if (a.group_mode == GROUP_NONE && a.M <= 64)
-        return launch_cfg<64, 128, 4, 2, SM>(a, st);
-    return launch_cfg<128, 128, 4, 4, SM>(a, st);
+        return launch_cfg<64, 64, 4, 1, 4, SM>(a, st);
+    return launch_cfg<256, 256, 4, 8, 8, SM>(a, st);        // 8 waves of 64 x 128
 }
 
 hipError_t launch_gemm(const GemmArgs& a, hipStream_t st) {
