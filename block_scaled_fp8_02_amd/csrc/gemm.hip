@@ -161,20 +161,25 @@ __global__ __launch_bounds__(64 * NW, 1) void k_gemm(GemmArgs g) {
     const int64_t jhi = j0 + BJ < g.Nn ? j0 + BJ : g.Nn;
 
     // ---------------------------------------------------- DMA addressing
-    // Chunk q = c*NT + tid of a stage lands at LDS byte 16*q: row q/8,
-    // physical chunk q%8, which holds logical chunk (q%8) ^ (row&7).
-    const uint8_t* src[NCH];
+    // Chunk q = c*NT + tid of a stage lands at LDS byte 16*q: tile row q/8,
+    // physical chunk q%8, which holds logical chunk (q%8) ^ (row&7).  Rows
+    // c < NCP are P rows, the rest Q rows.  Sources are a block-uniform base
+    // (SGPRs) plus a 32-bit per-lane offset; rows past the matrix edge are
+    // clamped to its last row (they are computed but never stored).
+    constexpr int NCP = BI * 8 / NT;
+    static_assert(NCP * NT == BI * 8, "P rows must fill whole DMA rounds");
+    const uint8_t* pbase = g.P + i0 * g.ldp + kbase * 128;
+    const uint8_t* qbase = Q + j0 * g.ldq + kbase * 128;
+    uint32_t soff[NCH];
 #pragma unroll
     for (int c = 0; c < NCH; ++c) {
         const int q = c * NT + tid, row = q >> 3, lch = (q & 7) ^ (row & 7);
-        if (row < BI) {
-            int64_t r = i0 + row;
-            r = r < ihi ? r : ihi - 1;                             // clamp: rows past the edge are never stored
-            src[c] = g.P + r * g.ldp + kbase * 128 + lch * 16;
+        if (c < NCP) {
+            const int64_t r = row < ihi - i0 ? row : ihi - i0 - 1;
+            soff[c] = (uint32_t)(r * g.ldp + lch * 16);
         } else {
-            int64_t r = j0 + row - BI;
-            r = r < jhi ? r : jhi - 1;
-            src[c] = Q + r * g.ldq + kbase * 128 + lch * 16;
+            const int64_t r = row - BI < jhi - j0 ? row - BI : jhi - j0 - 1;
+            soff[c] = (uint32_t)(r * g.ldq + lch * 16);
         }
     }
 
@@ -188,7 +193,7 @@ __global__ __launch_bounds__(64 * NW, 1) void k_gemm(GemmArgs g) {
         int64_t r = i0 + tid;
         r = r < ihi ? r : ihi - 1;
         sbase = static_cast<const char*>(g.sP) + (r * g.ldsp + (SM == SCALE_MX ? kbase * 4 : kbase)) * sq_elem;
-        sstep = SM == SCALE_MX ? 4 : 4;
+        sstep = 4;
     } else {
         int64_t r = j0 + (tid < BI + BJ ? tid - BI : 0);
         r = r < jhi ? r : jhi - 1;
@@ -204,20 +209,27 @@ __global__ __launch_bounds__(64 * NW, 1) void k_gemm(GemmArgs g) {
     // It is issued from inline assembly so that the compiler, which cannot
     // tell the stage being filled from the stage being read, does not stall
     // the fragment reads on it; completion is awaited explicitly before the
-    // barrier that ends each K step.
+    // barrier that ends each K step.  The DMAs of the next stage are spread
+    // over the first Q sub-tiles of the current one, so that they queue
+    // behind the matrix work instead of stalling every wave at once.
     const uint32_t lds_base = (uint32_t)(uintptr_t)smem;
-#define FP8B_DMA(kb_, buf_)                                                                         \
+#define FP8B_DMA_PART(kb_, buf_, c0_, c1_)                                                         \
     do {                                                                                            \
-        _Pragma("unroll") for (int c = 0; c < NCH; ++c) {                                           \
+        _Pragma("unroll") for (int c = (c0_); c < (c1_); ++c) {                                     \
             const uint32_t la = __builtin_amdgcn_readfirstlane(                                     \
                 lds_base + (uint32_t)((buf_) * STAGE + (c * NT + wave * 64) * 16));                 \
-            const uint8_t* ga = src[c] + (kb_) * 128;                                               \
+            const uint64_t gv = (uint64_t)(uintptr_t)((c < NCP ? pbase : qbase) + (kb_) * 128);    \
+            /* readfirstlane returns int: widen through uint32_t, never sign-extend */               \
+            const uint64_t gb =                                                                     \
+                ((uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(gv >> 32)) << 32) |  \
+                (uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)gv);                   \
             uint32_t m0save;                                                                        \
             asm volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %1\n\t"                                \
-                         "global_load_lds_dwordx4 %2, off\n\ts_mov_b32 m0, %0"                      \
-                         : "=&s"(m0save) : "s"(la), "v"(ga) : "memory");                           \
+                         "global_load_lds_dwordx4 %2, %3\n\ts_mov_b32 m0, %0"                       \
+                         : "=&s"(m0save) : "s"(la), "v"(soff[c]), "s"(gb) : "memory");             \
         }                                                                                           \
     } while (0)
+    constexpr int DMA_PER_STEP = (NCH + TJ - 1) / TJ > 2 ? (NCH + TJ - 1) / TJ : 2;
 
     v4f acc[TJ][TI];
 #pragma unroll
@@ -226,7 +238,7 @@ __global__ __launch_bounds__(64 * NW, 1) void k_gemm(GemmArgs g) {
         for (int b = 0; b < TI; ++b) acc[a][b] = v4f{0.f, 0.f, 0.f, 0.f};
 
     if (KB > 0) {
-        FP8B_DMA(0, 0);
+        FP8B_DMA_PART(0, 0, 0, NCH);
         sscale[0][tid] = load_scale(0);
     }
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
@@ -234,10 +246,11 @@ __global__ __launch_bounds__(64 * NW, 1) void k_gemm(GemmArgs g) {
 
     const int prow_l = wi * WI + (lane & 15);                        // tile row of this lane's first P fragment
     const int qrow_l = BI + wj * WJ;                                 // tile row of this wave's first Q row
+    const int sh = 8 * (lane >> 4);
     for (int64_t kb = 0; kb < KB; ++kb) {
         const int buf = (int)(kb & 1);
         const int64_t kn = kb + 1 < KB ? kb + 1 : kb;             // the last block reloads itself into
-        FP8B_DMA(kn, buf ^ 1);                                     // the idle stage: no branch in the loop
+                                                                   // the idle stage: no branch in the loop
         const uint32_t snext = load_scale(kn);
         const uint8_t* base = smem + buf * STAGE;
         const uint32_t* sc = sscale[buf];
@@ -245,7 +258,6 @@ __global__ __launch_bounds__(64 * NW, 1) void k_gemm(GemmArgs g) {
         // P fragments and P-side scales for the whole K block; Q fragments
         // stream through a two-deep register pipeline (the next Q sub-tile's
         // LDS reads are in flight while the current one is multiplied).
-        const int sh = 8 * (lane >> 4);
         v8i bf[TI];
         float sp[TI];
         int eb[TI];
@@ -264,46 +276,81 @@ __global__ __launch_bounds__(64 * NW, 1) void k_gemm(GemmArgs g) {
         v8i af = lds_frag(base, qrow_l + (lane & 15), lane);
         uint4 sqa = *reinterpret_cast<const uint4*>(&sc[qrow_l + 4 * (lane >> 4)]);
         uint32_t eaw = sc[qrow_l + (lane & 15)];
+        if constexpr (SM == SCALE_MX) {
 #pragma unroll
-        for (int a = 0; a < TJ; ++a) {
-            v8i af_n = af;
-            uint4 sqa_n = sqa;
-            uint32_t eaw_n = eaw;
-            if (a + 1 < TJ) {
-                const int qr = qrow_l + (a + 1) * 16;
-                af_n = lds_frag(base, qr + (lane & 15), lane);
-                if constexpr (SM == SCALE_Q_ROW) sqa_n = *reinterpret_cast<const uint4*>(&sc[qr + 4 * (lane >> 4)]);
-                if constexpr (SM == SCALE_MX) eaw_n = sc[qr + (lane & 15)];
-            }
+            for (int a = 0; a < TJ; ++a) {
+                if (a * DMA_PER_STEP < NCH)
+                    FP8B_DMA_PART(kn, buf ^ 1, a * DMA_PER_STEP,
+                                  (a + 1) * DMA_PER_STEP < NCH ? (a + 1) * DMA_PER_STEP : NCH);
+                v8i af_n = af;
+                uint32_t eaw_n = eaw;
+                if (a + 1 < TJ) {
+                    const int qr = qrow_l + (a + 1) * 16;
+                    af_n = lds_frag(base, qr + (lane & 15), lane);
+                    eaw_n = sc[qr + (lane & 15)];
+                }
 #pragma unroll
-            for (int b = 0; b < TI; ++b) {
-                if constexpr (SM == SCALE_MX) {
+                for (int b = 0; b < TI; ++b)
                     acc[a][b] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
                         af, bf[b], acc[a][b], 0, 0, 0, (int)((eaw >> sh) & 0xFFu), 0, eb[b]);
-                } else {
-                    const v4f pr = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
-                        af, bf[b], v4f{0.f, 0.f, 0.f, 0.f}, 0, 0, 0, 0, 0, 0);
-                    if constexpr (SM == SCALE_Q_BLOCK) {
+                af = af_n;
+                eaw = eaw_n;
+                __builtin_amdgcn_sched_barrier(0);
+            }
+        } else {
+            // Software pipeline: step a issues the MFMAs of Q sub-tile a and
+            // the promotion FMAs of sub-tile a-1, whose results are ready.
+            v4f prev[TI];
+            uint4 sqa_prev = sqa;
 #pragma unroll
-                        for (int r = 0; r < 4; ++r) acc[a][b][r] = __builtin_fmaf(pr[r], sp[b], acc[a][b][r]);
-                    } else {
-                        acc[a][b][0] = __builtin_fmaf(pr[0], sp[b] * __uint_as_float(sqa.x), acc[a][b][0]);
-                        acc[a][b][1] = __builtin_fmaf(pr[1], sp[b] * __uint_as_float(sqa.y), acc[a][b][1]);
-                        acc[a][b][2] = __builtin_fmaf(pr[2], sp[b] * __uint_as_float(sqa.z), acc[a][b][2]);
-                        acc[a][b][3] = __builtin_fmaf(pr[3], sp[b] * __uint_as_float(sqa.w), acc[a][b][3]);
+            for (int a = 0; a <= TJ; ++a) {
+                if (a * DMA_PER_STEP < NCH)
+                    FP8B_DMA_PART(kn, buf ^ 1, a * DMA_PER_STEP,
+                                  (a + 1) * DMA_PER_STEP < NCH ? (a + 1) * DMA_PER_STEP : NCH);
+                v8i af_n = af;
+                uint4 sqa_n = sqa;
+                if (a + 1 < TJ) {
+                    const int qr = qrow_l + (a + 1) * 16;
+                    af_n = lds_frag(base, qr + (lane & 15), lane);
+                    if constexpr (SM == SCALE_Q_ROW) sqa_n = *reinterpret_cast<const uint4*>(&sc[qr + 4 * (lane >> 4)]);
+                }
+                v4f cur[TI];
+                if (a < TJ) {
+#pragma unroll
+                    for (int b = 0; b < TI; ++b)
+                        cur[b] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+                            af, bf[b], v4f{0.f, 0.f, 0.f, 0.f}, 0, 0, 0, 0, 0, 0);
+                }
+                if (a > 0) {
+#pragma unroll
+                    for (int b = 0; b < TI; ++b) {
+                        if constexpr (SM == SCALE_Q_BLOCK) {
+#pragma unroll
+                            for (int r = 0; r < 4; ++r)
+                                acc[a - 1][b][r] = __builtin_fmaf(prev[b][r], sp[b], acc[a - 1][b][r]);
+                        } else {
+                            acc[a - 1][b][0] = __builtin_fmaf(prev[b][0], sp[b] * __uint_as_float(sqa_prev.x), acc[a - 1][b][0]);
+                            acc[a - 1][b][1] = __builtin_fmaf(prev[b][1], sp[b] * __uint_as_float(sqa_prev.y), acc[a - 1][b][1]);
+                            acc[a - 1][b][2] = __builtin_fmaf(prev[b][2], sp[b] * __uint_as_float(sqa_prev.z), acc[a - 1][b][2]);
+                            acc[a - 1][b][3] = __builtin_fmaf(prev[b][3], sp[b] * __uint_as_float(sqa_prev.w), acc[a - 1][b][3]);
+                        }
                     }
                 }
+                if (a < TJ) {
+#pragma unroll
+                    for (int b = 0; b < TI; ++b) prev[b] = cur[b];
+                }
+                sqa_prev = sqa;
+                af = af_n;
+                sqa = sqa_n;
+                __builtin_amdgcn_sched_barrier(0);
             }
-            af = af_n;
-            sqa = sqa_n;
-            eaw = eaw_n;
-            __builtin_amdgcn_sched_barrier(0);
         }
         sscale[buf ^ 1][tid] = snext;
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");           // next stage's DMA has landed
         __syncthreads();
     }
-#undef FP8B_DMA
+#undef FP8B_DMA_PART
 
     // ---------------------------------------------------- epilogue
     const int64_t jw = j0 + wj * WJ;
