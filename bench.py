@@ -51,6 +51,9 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="rough CPU budget of the oracle baseline sample")
+    ap.add_argument("--traffic", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="no GPU work: turn two rocprofv3 --pmc counter_collection.csv files "
+                         "(FETCH_SIZE, WRITE_SIZE) of this benchmark into profiles/traffic_gemm_train.json")
     return ap.parse_args()
 
 
@@ -77,8 +80,67 @@ def algorithmic_bytes():
     }
 
 
+KERNEL_ORDER = ["quant_weight", "quant_dual_X", "fprop", "quant_dual_dY", "dgrad", "wgrad"]
+CALIB_BYTES = 256 << 20       # the copy kernel reads and writes this many bytes
+
+
+def calibrate_copy(torch, dev):
+    """A plain copy kernel of known size (torch's elementwise neg over 256 MiB
+    of fp32), run once before the timed region; its FETCH_SIZE / WRITE_SIZE
+    readings calibrate the counters of the library's kernels."""
+    a = torch.ones(CALIB_BYTES // 4, dtype=torch.float32, device=dev)
+    out = torch.empty_like(a)
+    torch.neg(a, out=out)
+    torch.cuda.synchronize()
+    del a, out
+
+
+def traffic_summary(fetch_csv, write_csv):
+    """Per-launch HBM-side bytes of every library kernel from two --pmc runs.
+    Counter values are KiB per dispatch, summed over the dispatch's instances;
+    each is scaled by copy_bytes / counter reading of the calibration copy."""
+    import csv
+
+    def load(path, counter):
+        per = {}
+        for r in csv.DictReader(open(path)):
+            if r["Counter_Name"] != counter:
+                continue
+            d = int(r["Dispatch_Id"])
+            e = per.setdefault(d, [r["Kernel_Name"], 0.0])
+            e[1] += float(r["Counter_Value"]) * 1024.0
+        return [per[d] for d in sorted(per)]
+
+    out = {"src_sha": src_sha("gemm.hip", "device_common.hpp"), "src_sha_quant": src_sha("quant.hip", "device_common.hpp"),
+           "copy_bytes": CALIB_BYTES, "kernels": {}}
+    for counter, path, key in (("FETCH_SIZE", fetch_csv, "fetch"), ("WRITE_SIZE", write_csv, "write")):
+        rows = load(path, counter)
+        calib = [v for n, v in rows if "neg" in n.lower()]
+        if not calib:
+            raise SystemExit(f"{path}: no calibration copy dispatch found")
+        factor = CALIB_BYTES / calib[0]
+        out[f"{key}_factor"] = round(factor, 5)
+        lib = [(n, v) for n, v in rows if "k_quant" in n or "k_gemm" in n]
+        for k, (n, v) in enumerate(lib):
+            name = KERNEL_ORDER[k % len(KERNEL_ORDER)]
+            e = out["kernels"].setdefault(name, {"kernel": n.split("(")[0], "fetch": [], "write": []})
+            e[key].append(v * factor)
+    for name, e in out["kernels"].items():
+        e["fetch_bytes"] = round(float(np.median(e.pop("fetch"))))
+        e["write_bytes"] = round(float(np.median(e.pop("write"))))
+        e["bytes_per_launch"] = e["fetch_bytes"] + e["write_bytes"]
+        e["alg_bytes"] = algorithmic_bytes()[name]
+    path = os.path.join(ROOT, "profiles", "traffic_gemm_train.json")
+    with open(path, "w") as f:
+        json.dump(out, f, indent=1)
+    print(json.dumps(out, indent=1))
+
+
 def main():
     args = parse()
+    if args.traffic:
+        traffic_summary(*args.traffic)
+        return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
               f"(this build runs on a single MI355X).", file=sys.stderr)
@@ -117,7 +179,8 @@ def main():
         dw=torch.empty((D, C), dtype=torch.bfloat16, device=dev),
     )
     b = bufs
-    names = ["quant_weight", "quant_dual_X", "fprop", "quant_dual_dY", "dgrad", "wgrad"]
+    names = KERNEL_ORDER
+    calibrate_copy(torch, dev)
     events = {n: [] for n in names}
 
     def step(i, record):
@@ -162,7 +225,9 @@ def main():
     kernels = {}
     for n in names:
         t = float(np.mean(events[n]))
-        ent = {"us": round(t * 1e6, 2), "us_min": round(float(np.min(events[n])) * 1e6, 2)}
+        p10, p50, p90 = np.percentile(events[n], [10, 50, 90])
+        ent = {"us": round(t * 1e6, 2), "us_p10": round(p10 * 1e6, 2), "us_median": round(p50 * 1e6, 2),
+               "us_p90": round(p90 * 1e6, 2)}
         if n in ("fprop", "dgrad", "wgrad"):
             tf = flops_gemm / t / 1e12
             ent.update(tflops=round(tf, 1), frac_fp8_peak=round(tf / PEAK_FP8_TFLOPS, 4))
@@ -175,12 +240,18 @@ def main():
     dom = max(("fprop", "dgrad", "wgrad"), key=lambda n: kernels[n]["us"])
     t_dom = kernels[dom]["us"] * 1e-6
     achieved = flops_gemm / t_dom / 1e12
+    # HBM-side bytes per launch from the committed counter runs, used only
+    # while the kernel sources are the ones the counters were taken on
     traffic = None
     tfile = os.path.join(ROOT, "profiles", "traffic_gemm_train.json")
     if os.path.exists(tfile):
         tj = json.load(open(tfile))
-        if tj.get("src_sha") == src_sha("gemm.hip") and dom in tj.get("kernels", {}):
-            traffic = tj["kernels"][dom]["bytes_per_launch"]
+        fresh = {"gemm": tj.get("src_sha") == src_sha("gemm.hip", "device_common.hpp"),
+                 "quant": tj.get("src_sha_quant") == src_sha("quant.hip", "device_common.hpp")}
+        for n, e in tj.get("kernels", {}).items():
+            if n in kernels and fresh["quant" if n.startswith("quant") else "gemm"]:
+                kernels[n]["traffic_bytes"] = e["bytes_per_launch"]
+        traffic = kernels[dom].get("traffic_bytes")
     roofline = {"bound": "mfma", "kernel": dom, "achieved": round(achieved, 1),
                 "peak": PEAK_FP8_TFLOPS, "unit": "TFLOP/s", "frac": round(achieved / PEAK_FP8_TFLOPS, 4),
                 "traffic": traffic, "alg_bytes": abytes[dom]}
