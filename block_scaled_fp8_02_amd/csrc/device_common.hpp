@@ -41,19 +41,38 @@ __device__ __forceinline__ float group_scale(float amax) {
     return (float)((double)amax / 448.0);
 }
 
-// R = 1/S rounded to binary64; 0 when S == 0, so that x * R is the signed
-// zero of x (an all-zero group, or one whose scale underflowed).
-__device__ __forceinline__ double quotient_recip(float S) {
-    return S == 0.0f ? 0.0 : 1.0 / (double)S;
+// The quotient fl32(x / S), without the long IEEE division sequence.  With
+// r = RN32(1/S), q0 = RN32(x * r) is within one ulp of x/S; the residual
+// e = q0*S - x is then exact in one FMA, and one Newton step q0 - e*r
+// rounds to RN32(x/S) (Markstein's theorem on FMA-based division): three
+// full-rate fp32 operations per element.  The residual is formed as
+// q0*S - x and subtracted, so that a zero x keeps its sign (x = -0 gives
+// q0 = -0, e = +0, -0 - 0*r = -0).
+//
+// The theorem needs every intermediate to stay normal.  A group scale S
+// outside [2^-60, 2^60] is therefore first moved into range by an exact
+// power of two P (prescale): x/S = (x*P)/(S*P), S*P is exact (S*2^64 for a
+// tiny or subnormal S; S*2^-64 for a huge one), and so is x*P, except that
+// x*P may underflow when S is huge -- then |x/S| < 2^-126 and the code is
+// the signed zero of x either way.  S = 0 keeps P = 1 and r = 0: every x of
+// such a group is a zero or rounds to one, and q0 - e*r is the signed zero
+// of x.  Quotients below 2^-11, whose residuals may underflow, still come
+// out below 2^-10 with the sign of x, so their E4M3 code is unaffected.
+__device__ __forceinline__ float prescale(float S) {
+    return (S < 0x1p-60f && S != 0.0f) ? 0x1p64f : (S > 0x1p60f ? 0x1p-64f : 1.0f);
 }
 
-// fl32(x / S) from R = RN64(1/S).  x * R carries a relative error below
-// 2^-52, while a quotient of two binary32 numbers is either exactly
-// representable or at least 2^-49 (relative) away from every binary32
-// rounding boundary and never exactly on one; so rounding x * R to binary32
-// gives exactly the correctly rounded fp32 quotient.
-__device__ __forceinline__ float exact_quotient(float x, double R) {
-    return (float)((double)x * R);
+// r = RN32(1/S) (0 when S == 0); double rounding through binary64 is
+// innocuous here as for group_scale.
+__device__ __forceinline__ float recip32(float S) {
+    return S == 0.0f ? 0.0f : (float)(1.0 / (double)S);
+}
+
+// RN32(x / S) for S = S_group * P and x = x_in * P (P = prescale(S_group)).
+__device__ __forceinline__ float quotient32(float x, float S, float r) {
+    const float q0 = x * r;
+    const float e = __builtin_fmaf(q0, S, -x);
+    return __builtin_fmaf(-e, r, q0);
 }
 
 // E4M3 code of a finite fp32 value: nearest, ties to even, |y| >= 448
@@ -82,9 +101,13 @@ __device__ __forceinline__ uint32_t e4m3_pack4(float a, float b, float c, float 
     return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(sat448(c), sat448(d), lo, true);
 }
 
-// Encode four quotients x / S (R = 1/S as above) into one word.
-__device__ __forceinline__ uint32_t encode4(float a, float b, float c, float d, double R) {
-    return e4m3_pack4(exact_quotient(a, R), exact_quotient(b, R), exact_quotient(c, R), exact_quotient(d, R));
+// Four codes of quantizer quotients, without the clamp.  A quotient x/S of
+// a group member never exceeds amax / fl32(amax/448) <= 448 (1 + 2^-24), so
+// its fp32 value is at most one ulp above 448, which the conversion rounds
+// to 448 (0x7E) like any value below the next midpoint (464).
+__device__ __forceinline__ uint32_t e4m3_pack4_q(float a, float b, float c, float d) {
+    const int lo = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
+    return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(c, d, lo, true);
 }
 
 // Max over the 16 lanes of an aligned 16-lane group.
@@ -135,6 +158,30 @@ __device__ __forceinline__ void load8(const float* p, int valid, float v[8]) {
 
 __device__ __forceinline__ int clamp_valid(int64_t remaining) {
     return remaining >= 8 ? 8 : (remaining <= 0 ? 0 : (int)remaining);
+}
+
+// Transpose an 8x8 byte block with byte permutes (32 v_perm_b32): rows
+// (lo = bytes 0..3, hi = 4..7) in, columns out.  perm(a, b, sel) picks
+// bytes of the 8-byte value {a:b} (b = bytes 0..3, a = bytes 4..7).
+__device__ __forceinline__ void transpose8x8_perm(const uint32_t lo[8], const uint32_t hi[8],
+                                                  uint32_t tlo[8], uint32_t thi[8]) {
+    // stage 1: interleave rows 2i and 2i+1 -> [r0c0 r1c0 r0c1 r1c1] ...
+    uint32_t a[4][4];   // [row pair][word]: words 0,1 from lo (cols 0-1, 2-3), 2,3 from hi (cols 4-5, 6-7)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        a[i][0] = __builtin_amdgcn_perm(lo[2 * i + 1], lo[2 * i], 0x05010400u);
+        a[i][1] = __builtin_amdgcn_perm(lo[2 * i + 1], lo[2 * i], 0x07030602u);
+        a[i][2] = __builtin_amdgcn_perm(hi[2 * i + 1], hi[2 * i], 0x05010400u);
+        a[i][3] = __builtin_amdgcn_perm(hi[2 * i + 1], hi[2 * i], 0x07030602u);
+    }
+    // stage 2: join row pairs (0,1)+(2,3) for tlo and (4,5)+(6,7) for thi
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+        tlo[2 * w] = __builtin_amdgcn_perm(a[1][w], a[0][w], 0x05040100u);
+        tlo[2 * w + 1] = __builtin_amdgcn_perm(a[1][w], a[0][w], 0x07060302u);
+        thi[2 * w] = __builtin_amdgcn_perm(a[3][w], a[2][w], 0x05040100u);
+        thi[2 * w + 1] = __builtin_amdgcn_perm(a[3][w], a[2][w], 0x07060302u);
+    }
 }
 
 // Transpose an 8x8 byte block held as rows (lo = bytes 0..3, hi = 4..7):

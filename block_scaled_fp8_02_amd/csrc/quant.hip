@@ -1,14 +1,14 @@
 // quant.hip -- gfx950 quantizer kernels for the block-scaled FP8 path.
 //
-// All three kernels apply the quantizer Q of the Jet-RL notes (section
-// 2.1): S = max|x| / 448 per group, code = E4M3(fl32(x / S)), nearest-even,
-// saturating.  They differ only in the grouping (section 4.2 of the notes;
-// the summary page's weight and activation quantization paragraphs):
+// Both kernels apply the quantizer Q of the Jet-RL notes (section 2.1):
+// S = max|x| / 448 per group, code = E4M3(fl32(x / S)), nearest-even,
+// saturating.  They differ in the grouping (section 4.2 of the notes; the
+// summary page's weight and activation quantization paragraphs):
 //   k_quant_rows    1x128 along the contiguous axis (X for FProp, dY for DGrad)
-//   k_quant_weight  128x128 blocks of W, optionally also the transposed codes
-//   k_quant_cols    1x128 along the token axis, written transposed (the
-//                   WGrad operands), optionally also the row-wise copy from
-//                   the same read of the input
+//   k_quant_tiles   128x128 tiles: weight blocks (optionally also the
+//                   transposed codes), or 1x128 groups along the token axis
+//                   written transposed (the WGrad operands), optionally with
+//                   the row-wise copy from the same read of the input
 //
 // Data movement: every input element is read from HBM exactly once with
 // 16-byte vector loads; codes leave as 8- or 16-byte stores.  The
@@ -42,244 +42,347 @@ __global__ __launch_bounds__(256) void k_quant_rows(const T* __restrict__ x, int
     for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(v[i]));
     amax = max16(amax);
     const float S = group_scale(amax);
-    const double R = quotient_recip(S);
+    const float P = prescale(S);
+    const float Sp = S * P, r = recip32(Sp);
+    float y[8];
+    if (__all(P == 1.0f)) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) y[i] = quotient32(v[i], Sp, r);
+    } else {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) y[i] = quotient32(v[i] * P, Sp, r);
+    }
     uint2 out;
-    out.x = encode4(v[0], v[1], v[2], v[3], R);
-    out.y = encode4(v[4], v[5], v[6], v[7], R);
+    out.x = e4m3_pack4_q(y[0], y[1], y[2], y[3]);
+    out.y = e4m3_pack4_q(y[4], y[5], y[6], y[7]);
     *reinterpret_cast<uint2*>(q + (int64_t)row * ldq + col0) = out;
     if (lane16 == 0) s[(int64_t)row * lds + g] = S;
 }
 
 // ---------------------------------------------------------------------
-// 128x128 weight tile per block.  Thread t holds rows 8*(t/16)..+7 and
-// columns 8*(t%16)..+7 of the tile (64 values); one scale per tile.
+// Tile quantizer: 128x128 tiles, persistent blocks.
+//
+// One 256-thread block walks tiles k = blockIdx.x, +gridDim.x, ... in
+// row-tile-major order; the next tile's input is loaded into registers
+// while the current one is quantized, so every block keeps one tile of
+// loads in flight.  Thread t owns rows 8*(t/16)..+7 and columns
+// 8*(t%16)..+7 of a tile.
+//
+//   QT_WEIGHT     one scale per tile (128x128 weight blocks): codes q and,
+//                 optionally, the same codes transposed (qT)
+//   QT_COLS       1x128 groups along the row (token) axis: per-column
+//                 scales, codes written transposed (qT, sT)
+//   QT_COLS_ROWS  as QT_COLS, plus the row-wise 1x128 codes (q, s) from
+//                 the same registers
+//
+// Grouped (MoE) token-axis mode: rows [offsets[e], offsets[e+1]) form
+// expert e; its row tiles never cross the expert's end and its transposed
+// codes start at the padded position P_e = sum_{e'<e} round_up(n_e', 128).
+// Every block advances a cursor over the experts as its tile index grows.
 // ---------------------------------------------------------------------
-template <typename T>
-__global__ __launch_bounds__(256) void k_quant_weight(const T* __restrict__ w, int64_t D, int64_t C, int64_t ldw,
-                                                      uint8_t* __restrict__ q, int64_t ldq,
-                                                      float* __restrict__ s, int64_t lds,
-                                                      uint8_t* __restrict__ qT, int64_t ldqT) {
-    __shared__ float red[4];
-    __shared__ __attribute__((aligned(16))) uint8_t tileT[128 * 128];
-    const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
-    const int rg = t >> 4, cg = t & 15;
-    const int64_t bi = blockIdx.x, bj = blockIdx.y;
-    const int64_t r0 = bi * 128 + rg * 8;
-    const int64_t c0 = bj * 128 + cg * 8;
-    const int cvalid = clamp_valid(C - c0);
+enum { QT_WEIGHT = 0, QT_COLS = 1, QT_COLS_ROWS = 2 };
 
-    float v[8][8];
-#pragma unroll
-    for (int p = 0; p < 8; ++p) {
-        const int64_t r = r0 + p;
-        const bool in = r < D;
-        load8(w + (in ? r : 0) * ldw + c0, in ? cvalid : 0, v[p]);
-    }
-    float amax = 0.0f;
-#pragma unroll
-    for (int p = 0; p < 8; ++p)
-#pragma unroll
-        for (int j = 0; j < 8; ++j) amax = fmaxf(amax, fabsf(v[p][j]));
-    amax = max64(amax);
-    if (lane == 0) red[wave] = amax;
-    __syncthreads();
-    amax = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
-    const float S = group_scale(amax);
-    const double R = quotient_recip(S);
-    if (t == 0) s[bi * lds + bj] = S;
-
-    uint32_t lo[8], hi[8];
-#pragma unroll
-    for (int p = 0; p < 8; ++p) {
-        lo[p] = encode4(v[p][0], v[p][1], v[p][2], v[p][3], R);
-        hi[p] = encode4(v[p][4], v[p][5], v[p][6], v[p][7], R);
-        if (r0 + p < D) *reinterpret_cast<uint2*>(q + (r0 + p) * ldq + c0) = make_uint2(lo[p], hi[p]);
-    }
-    if (qT == nullptr) return;                       // uniform across the block
-
-    uint32_t tlo[8], thi[8];
-    transpose8x8(lo, hi, tlo, thi);
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-        const int crow = cg * 8 + j;                 // row of the transposed tile
-        *reinterpret_cast<uint2*>(tileT + crow * 128 + ((rg ^ cg) << 3)) = make_uint2(tlo[j], thi[j]);
-    }
-    __syncthreads();
-    const int crow = t >> 1, h = t & 1;
-    const int64_t c = bj * 128 + crow;
-    if (c < C) {
-        uint32_t wv[16];
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            const int phys = (8 * h + i) ^ (crow >> 3);
-            const uint2 u = *reinterpret_cast<const uint2*>(tileT + crow * 128 + (phys << 3));
-            wv[2 * i] = u.x;
-            wv[2 * i + 1] = u.y;
-        }
-        uint8_t* dst = qT + c * ldqT + bi * 128 + 64 * h;
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-            *reinterpret_cast<uint4*>(dst + 16 * i) = make_uint4(wv[4 * i], wv[4 * i + 1], wv[4 * i + 2], wv[4 * i + 3]);
-    }
-}
-
-// ---------------------------------------------------------------------
-// Token-axis 1x128 groups, written transposed; optional row-wise copy.
-// Tile: 128 rows (one token group) x 128 columns, thread layout as in
-// k_quant_weight.  In grouped mode the row tiles follow the experts'
-// segments and block row-index y enumerates them expert by expert.
-// ---------------------------------------------------------------------
-struct SegInfo {
-    int64_t a, b, pos;   // rows [a, b) of this tile; first output column pos
+struct QuantTileArgs {
+    const void* x; int64_t rows, cols, ldx;
+    const int32_t* offsets; int64_t E;
+    uint8_t* q; int64_t ldq; float* s; int64_t lds;
+    uint8_t* qT; int64_t ldqT; float* sT; int64_t ldsT;
+    int64_t col_tiles;
+    int64_t tiles;          // dense: exact tile count; grouped: an upper bound
 };
 
-__device__ __forceinline__ SegInfo find_segment_tile(const int32_t* offsets, int64_t E, int64_t tile) {
-    // Linear scan over experts: tile index -> (expert, group within expert).
-    int64_t acc = 0, P = 0;
-    for (int64_t e = 0; e < E; ++e) {
-        const int64_t a = offsets[e], b = offsets[e + 1];
-        const int64_t n = b - a;
-        const int64_t tiles = (n + 127) / 128;
-        if (tile < acc + tiles) {
-            const int64_t g = tile - acc;
-            const int64_t ra = a + 128 * g;
-            return SegInfo{ra, ra + 128 < b ? ra + 128 : b, P + 128 * g};
-        }
-        acc += tiles;
-        P += 128 * tiles;
+// 8 rows x 8 columns of raw input per thread.
+template <typename T> struct RawTile;
+template <> struct RawTile<uint16_t> { uint4 w[8]; };
+template <> struct RawTile<float> { uint4 w[16]; };
+
+__device__ __forceinline__ void load_raw_row(const uint16_t* p, int valid, RawTile<uint16_t>& rt, int i) {
+    if (valid == 8) {
+        rt.w[i] = *reinterpret_cast<const uint4*>(p);
+    } else {
+        uint32_t h[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) h[j] = j < valid ? (uint32_t)p[j] : 0u;
+        rt.w[i] = make_uint4(h[0] | (h[1] << 16), h[2] | (h[3] << 16), h[4] | (h[5] << 16), h[6] | (h[7] << 16));
     }
-    return SegInfo{0, 0, -1};
 }
 
-template <typename T, bool ROWS>
-__global__ __launch_bounds__(256) void k_quant_cols(const T* __restrict__ x, int64_t rows, int64_t cols, int64_t ldx,
-                                                    const int32_t* __restrict__ offsets, int64_t E,
-                                                    uint8_t* __restrict__ qT, int64_t ldqT,
-                                                    float* __restrict__ sT, int64_t ldsT,
-                                                    uint8_t* __restrict__ q, int64_t ldq,
-                                                    float* __restrict__ s, int64_t lds) {
-    __shared__ float colmax[4][128];
-    __shared__ double colR[128];
-    __shared__ double rowR[128];
-    __shared__ int64_t seg[3];
-    __shared__ __attribute__((aligned(16))) uint8_t tileT[128 * 128];
-    const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
-    const int rg = t >> 4, cg = t & 15;
-
-    int64_t a, b, pos;
-    if (offsets == nullptr) {
-        a = (int64_t)blockIdx.x * 128;
-        b = a + 128 < rows ? a + 128 : rows;
-        pos = a;
+__device__ __forceinline__ void load_raw_row(const float* p, int valid, RawTile<float>& rt, int i) {
+    if (valid == 8) {
+        rt.w[2 * i] = *reinterpret_cast<const uint4*>(p);
+        rt.w[2 * i + 1] = *reinterpret_cast<const uint4*>(p + 4);
     } else {
-        if (t == 0) {
-            const SegInfo si = find_segment_tile(offsets, E, blockIdx.x);
-            seg[0] = si.a; seg[1] = si.b; seg[2] = si.pos;
-        }
-        __syncthreads();
-        a = seg[0]; b = seg[1]; pos = seg[2];
-        if (pos < 0) return;                         // beyond the last tile: whole block
+        uint32_t h[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) h[j] = j < valid ? __float_as_uint(p[j]) : 0u;
+        rt.w[2 * i] = make_uint4(h[0], h[1], h[2], h[3]);
+        rt.w[2 * i + 1] = make_uint4(h[4], h[5], h[6], h[7]);
     }
-    const int64_t cb = (int64_t)blockIdx.y * 128;
-    const int64_t c0 = cb + cg * 8;
-    const int cvalid = clamp_valid(cols - c0);
+}
 
-    float v[8][8];
+__device__ __forceinline__ void unpack_row(const RawTile<uint16_t>& rt, int i, float v[8]) {
+    const uint4 w = rt.w[i];
+    v[0] = __uint_as_float(w.x << 16); v[1] = __uint_as_float(w.x & 0xFFFF0000u);
+    v[2] = __uint_as_float(w.y << 16); v[3] = __uint_as_float(w.y & 0xFFFF0000u);
+    v[4] = __uint_as_float(w.z << 16); v[5] = __uint_as_float(w.z & 0xFFFF0000u);
+    v[6] = __uint_as_float(w.w << 16); v[7] = __uint_as_float(w.w & 0xFFFF0000u);
+}
+
+__device__ __forceinline__ void unpack_row(const RawTile<float>& rt, int i, float v[8]) {
+    const uint4 a = rt.w[2 * i], b = rt.w[2 * i + 1];
+    v[0] = __uint_as_float(a.x); v[1] = __uint_as_float(a.y); v[2] = __uint_as_float(a.z); v[3] = __uint_as_float(a.w);
+    v[4] = __uint_as_float(b.x); v[5] = __uint_as_float(b.y); v[6] = __uint_as_float(b.z); v[7] = __uint_as_float(b.w);
+}
+
+// Where a tile lies: input rows [a, b), first column cb, first position of
+// its transposed codes pos, row-tile index rt (scale row of QT_WEIGHT) and
+// column-tile index ct.
+struct TileAt {
+    int64_t a, b, cb, pos, rt, ct;
+    bool valid;
+};
+
+struct TileCursor {       // grouped mode: expert e, its first row tile, its padded start
+    int64_t e, first, P;
+};
+
+__device__ __forceinline__ TileAt locate_tile(const QuantTileArgs& A, int64_t k, TileCursor& cur) {
+    TileAt at;
+    at.rt = k / A.col_tiles;
+    at.ct = k - at.rt * A.col_tiles;
+    at.cb = at.ct * 128;
+    if (A.offsets == nullptr) {
+        at.valid = k < A.tiles;
+        at.a = at.rt * 128;
+        at.b = at.a + 128 < A.rows ? at.a + 128 : A.rows;
+        at.pos = at.a;
+        return at;
+    }
+    // the cursor only moves forward: a block's tile index never decreases
+    while (cur.e < A.E) {
+        const int64_t lo = A.offsets[cur.e], hi = A.offsets[cur.e + 1];
+        const int64_t nt = (hi - lo + 127) / 128;
+        if (at.rt < cur.first + nt) {
+            const int64_t g = at.rt - cur.first;
+            at.a = lo + 128 * g;
+            at.b = at.a + 128 < hi ? at.a + 128 : hi;
+            at.pos = cur.P + 128 * g;
+            at.valid = true;
+            return at;
+        }
+        cur.first += nt;
+        cur.P += 128 * nt;
+        ++cur.e;
+    }
+    at.a = at.b = at.pos = 0;
+    at.valid = false;
+    return at;
+}
+
+template <typename T>
+__device__ __forceinline__ void load_tile(const QuantTileArgs& A, const TileAt& at, int rg, int cg, RawTile<T>& raw) {
+    const T* x = static_cast<const T*>(A.x);
+    const int64_t c0 = at.cb + cg * 8;
+    const int cvalid = clamp_valid(A.cols - c0);
 #pragma unroll
     for (int p = 0; p < 8; ++p) {
-        const int64_t r = a + rg * 8 + p;
-        const bool in = r < b;
-        load8(x + (in ? r : 0) * ldx + c0, in ? cvalid : 0, v[p]);
+        const int64_t r = at.a + rg * 8 + p;
+        const bool in = r < at.b;
+        load_raw_row(x + (in ? r : 0) * A.ldx + c0, in ? cvalid : 0, raw, p);
     }
+}
 
-    // column maxima: 8 rows in-thread, 4 row-slices in-wave, 4 waves via LDS
-    float cm[8];
+// Codes of one thread's 8x8 values with one scale per row (PER_ROW) or
+// per column: S = S_group*P, r = RN32(1/S), P = prescale(S_group).  The
+// multiplication by P is skipped when every P of the tile is 1 (plain).
+template <bool PER_ROW, bool SCALED>
+__device__ __forceinline__ void encode_8x8_v(const float v[8][8], const float S[8], const float r[8], const float P[8],
+                                             uint32_t lo[8], uint32_t hi[8]) {
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-        float m = 0.0f;
+    for (int p = 0; p < 8; ++p) {
+        float y[8];
 #pragma unroll
-        for (int p = 0; p < 8; ++p) m = fmaxf(m, fabsf(v[p][j]));
-        m = fmaxf(m, __shfl_xor(m, 16));
-        m = fmaxf(m, __shfl_xor(m, 32));
-        cm[j] = m;
+        for (int j = 0; j < 8; ++j) {
+            const int g = PER_ROW ? p : j;
+            y[j] = quotient32(SCALED ? v[p][j] * P[g] : v[p][j], S[g], r[g]);
+        }
+        lo[p] = e4m3_pack4_q(y[0], y[1], y[2], y[3]);
+        hi[p] = e4m3_pack4_q(y[4], y[5], y[6], y[7]);
     }
-    if (lane < 16) {
+}
+
+template <bool PER_ROW>
+__device__ __forceinline__ void encode_8x8(bool plain, const float v[8][8], const float S[8], const float r[8],
+                                           const float P[8], uint32_t lo[8], uint32_t hi[8]) {
+    if (plain)
+        encode_8x8_v<PER_ROW, false>(v, S, r, P, lo, hi);
+    else
+        encode_8x8_v<PER_ROW, true>(v, S, r, P, lo, hi);
+}
+
+// Eight consecutive LDS floats.
+__device__ __forceinline__ void lds_read8(const float* p, float o[8]) {
+    const float4 a = *reinterpret_cast<const float4*>(p);
+    const float4 b = *reinterpret_cast<const float4*>(p + 4);
+    o[0] = a.x; o[1] = a.y; o[2] = a.z; o[3] = a.w; o[4] = b.x; o[5] = b.y; o[6] = b.z; o[7] = b.w;
+}
+
+// Barrier for LDS traffic only.  __syncthreads() also waits for every
+// outstanding global load, which would drain the next tile's prefetch at
+// the first barrier of each tile; LDS writes only need lgkmcnt(0).
+__device__ __forceinline__ void lds_barrier() {
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+template <typename T, int MODE>
+__global__ __launch_bounds__(256, 2) void k_quant_tiles(QuantTileArgs A) {
+    __shared__ __attribute__((aligned(16))) float red_col[16][128];   // [row slice][column]
+    __shared__ __attribute__((aligned(16))) float red_row[16][128];   // [column slice][row]
+    __shared__ __attribute__((aligned(16))) float sc_col[3][128];     // S*P, RN32(1/(S*P)), P per column
+    __shared__ __attribute__((aligned(16))) float sc_row[3][128];     // the same per row
+    __shared__ __attribute__((aligned(16))) uint8_t tileT[128 * 128];
+    __shared__ float red4[4];
+    __shared__ int scaled_flag;       // some group of the tile needs P != 1
+
+    const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+    const int rg = t >> 4, cg = t & 15;
+    const bool want_qT = MODE != QT_WEIGHT || A.qT != nullptr;
+    if (t == 0) scaled_flag = 0;
+
+    TileCursor cur{0, 0, 0};
+    int64_t k = blockIdx.x;
+    TileAt at = locate_tile(A, k, cur);
+    RawTile<T> raw;
+    if (at.valid) load_tile<T>(A, at, rg, cg, raw);
+    lds_barrier();
+
+    while (at.valid) {
+        float v[8][8];
 #pragma unroll
-        for (int j = 0; j < 8; ++j) colmax[wave][cg * 8 + j] = cm[j];
-    }
-    if (ROWS) {
-        float rm[8];
-#pragma unroll
-        for (int p = 0; p < 8; ++p) {
+        for (int p = 0; p < 8; ++p) unpack_row(raw, p, v[p]);
+        // prefetch the next tile while this one is quantized
+        const int64_t kn = k + gridDim.x;
+        const TileAt nx = locate_tile(A, kn, cur);
+        if (nx.valid) load_tile<T>(A, nx, rg, cg, raw);
+
+        uint32_t lo[8], hi[8];
+        if (MODE == QT_WEIGHT) {
             float m = 0.0f;
 #pragma unroll
-            for (int j = 0; j < 8; ++j) m = fmaxf(m, fabsf(v[p][j]));
-            rm[p] = max16(m);
-        }
-        if (cg < 8) {
-            float m = rm[0];
+            for (int p = 0; p < 8; ++p)
 #pragma unroll
-            for (int p = 1; p < 8; ++p) m = cg == p ? rm[p] : m;
+                for (int j = 0; j < 8; ++j) m = fmaxf(m, fabsf(v[p][j]));
+            m = max64(m);
+            if (lane == 0) red4[wave] = m;
+            lds_barrier();                                           // (1)
+            m = fmaxf(fmaxf(red4[0], red4[1]), fmaxf(red4[2], red4[3]));
             const float S = group_scale(m);
-            rowR[rg * 8 + cg] = quotient_recip(S);
-            const int64_t r = a + rg * 8 + cg;
-            if (r < b) s[r * lds + blockIdx.y] = S;
+            if (t == 0) A.s[at.rt * A.lds + at.ct] = S;
+            const float P = prescale(S);
+            float Sv[8], rv[8], Pv[8];
+#pragma unroll
+            for (int i = 0; i < 8; ++i) { Sv[i] = S * P; rv[i] = recip32(S * P); Pv[i] = P; }
+            encode_8x8<true>(P == 1.0f, v, Sv, rv, Pv, lo, hi);       // P is uniform over the block
+#pragma unroll
+            for (int p = 0; p < 8; ++p) {
+                const int64_t row = at.a + rg * 8 + p;
+                if (row < at.b) *reinterpret_cast<uint2*>(A.q + row * A.ldq + at.cb + cg * 8) = make_uint2(lo[p], hi[p]);
+            }
+        } else {
+            // partial maxima: columns over this thread's 8 rows, rows over its 8 columns
+            float cm[8], rm[8];
+#pragma unroll
+            for (int j = 0; j < 8; ++j) cm[j] = 0.0f;
+#pragma unroll
+            for (int p = 0; p < 8; ++p) {
+                float m = 0.0f;
+#pragma unroll
+                for (int j = 0; j < 8; ++j) {
+                    const float a = fabsf(v[p][j]);
+                    cm[j] = fmaxf(cm[j], a);
+                    m = fmaxf(m, a);
+                }
+                rm[p] = m;
+            }
+            *reinterpret_cast<float4*>(&red_col[rg][cg * 8]) = make_float4(cm[0], cm[1], cm[2], cm[3]);
+            *reinterpret_cast<float4*>(&red_col[rg][cg * 8 + 4]) = make_float4(cm[4], cm[5], cm[6], cm[7]);
+            if (MODE == QT_COLS_ROWS) {
+                *reinterpret_cast<float4*>(&red_row[cg][rg * 8]) = make_float4(rm[0], rm[1], rm[2], rm[3]);
+                *reinterpret_cast<float4*>(&red_row[cg][rg * 8 + 4]) = make_float4(rm[4], rm[5], rm[6], rm[7]);
+            }
+            lds_barrier();                                           // (1)
+            if (t < 128) {
+                float m = red_col[0][t];
+#pragma unroll
+                for (int i = 1; i < 16; ++i) m = fmaxf(m, red_col[i][t]);
+                const float S = group_scale(m), P = prescale(S);
+                sc_col[0][t] = S * P;
+                sc_col[1][t] = recip32(S * P);
+                sc_col[2][t] = P;
+                if (P != 1.0f) scaled_flag = 1;
+                if (at.cb + t < A.cols) A.sT[(at.cb + t) * A.ldsT + at.pos / 128] = S;
+            } else if (MODE == QT_COLS_ROWS) {
+                const int rr = t - 128;
+                float m = red_row[0][rr];
+#pragma unroll
+                for (int i = 1; i < 16; ++i) m = fmaxf(m, red_row[i][rr]);
+                const float S = group_scale(m), P = prescale(S);
+                sc_row[0][rr] = S * P;
+                sc_row[1][rr] = recip32(S * P);
+                sc_row[2][rr] = P;
+                if (P != 1.0f) scaled_flag = 1;
+                if (at.a + rr < at.b) A.s[(at.a + rr) * A.lds + at.ct] = S;
+            }
+            lds_barrier();                                           // (2)
+            const bool plain = scaled_flag == 0;
+            float Sv[8], rv[8], Pv[8];
+            if (MODE == QT_COLS_ROWS) {
+                lds_read8(&sc_row[0][rg * 8], Sv);
+                lds_read8(&sc_row[1][rg * 8], rv);
+                lds_read8(&sc_row[2][rg * 8], Pv);
+                encode_8x8<true>(plain, v, Sv, rv, Pv, lo, hi);
+#pragma unroll
+                for (int p = 0; p < 8; ++p) {
+                    const int64_t row = at.a + rg * 8 + p;
+                    if (row < at.b) *reinterpret_cast<uint2*>(A.q + row * A.ldq + at.cb + cg * 8) = make_uint2(lo[p], hi[p]);
+                }
+            }
+            lds_read8(&sc_col[0][cg * 8], Sv);
+            lds_read8(&sc_col[1][cg * 8], rv);
+            lds_read8(&sc_col[2][cg * 8], Pv);
+            encode_8x8<false>(plain, v, Sv, rv, Pv, lo, hi);
         }
-    }
-    __syncthreads();
-    if (t < 128) {
-        const float m = fmaxf(fmaxf(colmax[0][t], colmax[1][t]), fmaxf(colmax[2][t], colmax[3][t]));
-        const float S = group_scale(m);
-        colR[t] = quotient_recip(S);
-        if (cb + t < cols) sT[(cb + t) * ldsT + pos / 128] = S;
-    }
-    __syncthreads();
 
-    if (ROWS) {
+        if (want_qT) {
+            uint32_t tlo[8], thi[8];
+            transpose8x8_perm(lo, hi, tlo, thi);
 #pragma unroll
-        for (int p = 0; p < 8; ++p) {
-            const double R = rowR[rg * 8 + p];
-            const int64_t r = a + rg * 8 + p;
-            const uint32_t lo = encode4(v[p][0], v[p][1], v[p][2], v[p][3], R);
-            const uint32_t hi = encode4(v[p][4], v[p][5], v[p][6], v[p][7], R);
-            if (r < b) *reinterpret_cast<uint2*>(q + r * ldq + c0) = make_uint2(lo, hi);
+            for (int j = 0; j < 8; ++j)
+                *reinterpret_cast<uint2*>(tileT + (cg * 8 + j) * 128 + ((rg ^ cg) << 3)) = make_uint2(tlo[j], thi[j]);
         }
-    }
-
-    uint32_t lo[8], hi[8];
-    {
-        double Rc[8];
+        lds_barrier();                                               // (3)
+        if (want_qT) {
+            const int crow = t >> 1, h = t & 1;
+            const int64_t c = at.cb + crow;
+            if (c < A.cols) {
+                uint32_t wv[16];
 #pragma unroll
-        for (int j = 0; j < 8; ++j) Rc[j] = colR[cg * 8 + j];
+                for (int i = 0; i < 8; ++i) {
+                    const int phys = (8 * h + i) ^ (crow >> 3);
+                    const uint2 u = *reinterpret_cast<const uint2*>(tileT + crow * 128 + (phys << 3));
+                    wv[2 * i] = u.x;
+                    wv[2 * i + 1] = u.y;
+                }
+                uint8_t* dst = A.qT + c * A.ldqT + at.pos + 64 * h;
 #pragma unroll
-        for (int p = 0; p < 8; ++p) {
-            lo[p] = e4m3_pack4(exact_quotient(v[p][0], Rc[0]), exact_quotient(v[p][1], Rc[1]),
-                               exact_quotient(v[p][2], Rc[2]), exact_quotient(v[p][3], Rc[3]));
-            hi[p] = e4m3_pack4(exact_quotient(v[p][4], Rc[4]), exact_quotient(v[p][5], Rc[5]),
-                               exact_quotient(v[p][6], Rc[6]), exact_quotient(v[p][7], Rc[7]));
+                for (int i = 0; i < 4; ++i)
+                    *reinterpret_cast<uint4*>(dst + 16 * i) =
+                        make_uint4(wv[4 * i], wv[4 * i + 1], wv[4 * i + 2], wv[4 * i + 3]);
+            }
         }
-    }
-    uint32_t tlo[8], thi[8];
-    transpose8x8(lo, hi, tlo, thi);
-#pragma unroll
-    for (int j = 0; j < 8; ++j)
-        *reinterpret_cast<uint2*>(tileT + (cg * 8 + j) * 128 + ((rg ^ cg) << 3)) = make_uint2(tlo[j], thi[j]);
-    __syncthreads();
-    const int crow = t >> 1, h = t & 1;
-    const int64_t c = cb + crow;
-    if (c < cols) {
-        uint32_t wv[16];
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            const int phys = (8 * h + i) ^ (crow >> 3);
-            const uint2 u = *reinterpret_cast<const uint2*>(tileT + crow * 128 + (phys << 3));
-            wv[2 * i] = u.x;
-            wv[2 * i + 1] = u.y;
-        }
-        uint8_t* dst = qT + c * ldqT + pos + 64 * h;
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-            *reinterpret_cast<uint4*>(dst + 16 * i) = make_uint4(wv[4 * i], wv[4 * i + 1], wv[4 * i + 2], wv[4 * i + 3]);
+        if (MODE != QT_WEIGHT && t == 0) scaled_flag = 0;   // every wave has read it (before barrier 3)
+        k = kn;
+        at = nx;
     }
 }
 
@@ -290,8 +393,15 @@ __global__ __launch_bounds__(256) void k_encode(const float* __restrict__ x, con
                                                 int64_t n, uint8_t* __restrict__ out) {
     const int64_t stride = (int64_t)gridDim.x * blockDim.x;
     for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += stride) {
-        const double R = s ? quotient_recip(s[i]) : 1.0;
-        out[i] = (uint8_t)e4m3_encode(exact_quotient(x[i], R));
+        float y = x[i];
+        if (s != nullptr) {
+            const float S = s[i], P = prescale(S), Sp = S * P, r = recip32(Sp);
+            const float xp = y * P, q0 = xp * r;
+            // |x/S| beyond 2^10 saturates whatever its exact value (q0 may be
+            // +-inf); below it quotient32's conditions hold
+            y = fabsf(q0) < 1024.0f ? quotient32(xp, Sp, r) : q0;
+        }
+        out[i] = (uint8_t)e4m3_encode(y);
     }
 }
 
@@ -314,18 +424,44 @@ hipError_t launch_quant_rows(const void* x, bool in_bf16, int64_t rows, int64_t 
     return hipGetLastError();
 }
 
+// Blocks of the persistent tile quantizer: two per compute unit (its
+// register and LDS budget allows two), never more than there are tiles.
+static int64_t tile_grid(int64_t tiles) {
+    static int cu_count[64];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0) dev = 0;
+    int cus = dev < 64 ? cu_count[dev] : 0;
+    if (cus <= 0) {
+        if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0) cus = 256;
+        if (dev < 64) cu_count[dev] = cus;
+    }
+    const int64_t g = 2 * (int64_t)cus;
+    return tiles < g ? tiles : g;
+}
+
+template <int MODE>
+static hipError_t launch_tiles(bool in_bf16, const QuantTileArgs& A, hipStream_t st) {
+    const int64_t blocks = tile_grid(A.tiles);
+    if (blocks <= 0) return hipSuccess;
+    if (in_bf16)
+        k_quant_tiles<uint16_t, MODE><<<dim3((unsigned)blocks), 256, 0, st>>>(A);
+    else
+        k_quant_tiles<float, MODE><<<dim3((unsigned)blocks), 256, 0, st>>>(A);
+    return hipGetLastError();
+}
+
 hipError_t launch_quant_weight(const void* w, bool in_bf16, int64_t D, int64_t C, int64_t ldw,
                                uint8_t* q, int64_t ldq, float* s, int64_t lds,
                                uint8_t* qT, int64_t ldqT, hipStream_t st) {
     if (D == 0 || C == 0) return hipSuccess;
-    const int64_t bd = (D + 127) / 128, bc = (C + 127) / 128;
-    if (bd > 0x7FFFFFFF || bc > 65535) return hipErrorInvalidValue;
-    const dim3 grid((unsigned)bd, (unsigned)bc);
-    if (in_bf16)
-        k_quant_weight<uint16_t><<<grid, 256, 0, st>>>(static_cast<const uint16_t*>(w), D, C, ldw, q, ldq, s, lds, qT, ldqT);
-    else
-        k_quant_weight<float><<<grid, 256, 0, st>>>(static_cast<const float*>(w), D, C, ldw, q, ldq, s, lds, qT, ldqT);
-    return hipGetLastError();
+    QuantTileArgs A{};
+    A.x = w; A.rows = D; A.cols = C; A.ldx = ldw;
+    A.offsets = nullptr; A.E = 0;
+    A.q = q; A.ldq = ldq; A.s = s; A.lds = lds;
+    A.qT = qT; A.ldqT = ldqT; A.sT = nullptr; A.ldsT = 0;
+    A.col_tiles = (C + 127) / 128;
+    A.tiles = (D + 127) / 128 * A.col_tiles;
+    return launch_tiles<QT_WEIGHT>(in_bf16, A, st);
 }
 
 hipError_t launch_quant_cols(const void* x, bool in_bf16, int64_t rows, int64_t cols, int64_t ldx,
@@ -333,25 +469,15 @@ hipError_t launch_quant_cols(const void* x, bool in_bf16, int64_t rows, int64_t 
                              uint8_t* qT, int64_t ldqT, float* sT, int64_t ldsT,
                              uint8_t* q, int64_t ldq, float* s, int64_t lds, hipStream_t st) {
     if (rows == 0 || cols == 0) return hipSuccess;
-    const int64_t row_tiles = (rows + 127) / 128 + (offsets ? E : 0);
-    const int64_t col_tiles = (cols + 127) / 128;
-    if (row_tiles > 0x7FFFFFFF || col_tiles > 65535) return hipErrorInvalidValue;
-    const dim3 grid((unsigned)row_tiles, (unsigned)col_tiles);
-    const bool rowsout = q != nullptr;
-    if (in_bf16) {
-        auto xp = static_cast<const uint16_t*>(x);
-        if (rowsout)
-            k_quant_cols<uint16_t, true><<<grid, 256, 0, st>>>(xp, rows, cols, ldx, offsets, E, qT, ldqT, sT, ldsT, q, ldq, s, lds);
-        else
-            k_quant_cols<uint16_t, false><<<grid, 256, 0, st>>>(xp, rows, cols, ldx, offsets, E, qT, ldqT, sT, ldsT, q, ldq, s, lds);
-    } else {
-        auto xp = static_cast<const float*>(x);
-        if (rowsout)
-            k_quant_cols<float, true><<<grid, 256, 0, st>>>(xp, rows, cols, ldx, offsets, E, qT, ldqT, sT, ldsT, q, ldq, s, lds);
-        else
-            k_quant_cols<float, false><<<grid, 256, 0, st>>>(xp, rows, cols, ldx, offsets, E, qT, ldqT, sT, ldsT, q, ldq, s, lds);
-    }
-    return hipGetLastError();
+    QuantTileArgs A{};
+    A.x = x; A.rows = rows; A.cols = cols; A.ldx = ldx;
+    A.offsets = offsets; A.E = offsets ? E : 0;
+    A.q = q; A.ldq = ldq; A.s = s; A.lds = lds;
+    A.qT = qT; A.ldqT = ldqT; A.sT = sT; A.ldsT = ldsT;
+    A.col_tiles = (cols + 127) / 128;
+    // grouped: at most one partial tile per expert beyond rows/128
+    A.tiles = ((rows + 127) / 128 + A.E) * A.col_tiles;
+    return q != nullptr ? launch_tiles<QT_COLS_ROWS>(in_bf16, A, st) : launch_tiles<QT_COLS>(in_bf16, A, st);
 }
 
 hipError_t launch_encode(const float* x, const float* s, int64_t n, uint8_t* out, hipStream_t st) {

@@ -150,6 +150,30 @@ def test_classes_zeros_maxes_boundary():
         check_cols(arr)
 
 
+def test_group_max_quotient_above_448():
+    """Groups whose scale rounded down, so that amax / S is one fp32 ulp
+    above 448: the largest element must still encode to +-448 (0x7E/0xFE),
+    on every quantizer (the conversion there runs without a clamp)."""
+    banner("largest quotient above 448")
+    rng = np.random.default_rng(448)
+    cand = (np.exp(rng.uniform(-30, 30, 1 << 16))).astype(np.float32)
+    S = cand / np.float32(448.0)
+    above = cand[(cand / S) > np.float32(448.0)]
+    assert above.size > 1000, "expected many scales that round down"
+    rows = 256
+    x = (rng.uniform(-1, 1, (rows, 384)).astype(np.float32) * 0.999)
+    amax = above[:rows][:, None]
+    x = (x * amax).astype(np.float32)
+    for g in range(3):                       # one maximal element per 128-group, random sign
+        col = g * 128 + rng.integers(0, 128, rows)
+        x[np.arange(rows), col] = amax[:, 0] * np.where(rng.integers(0, 2, rows) == 1, 1, -1)
+    wq, _ = oracle.quant_1x128(x)
+    assert np.isin(wq, [0x7E, 0xFE]).sum(axis=1).min() >= 3
+    check_rows(x)
+    check_weight(x)
+    check_cols(np.ascontiguousarray(x.T))
+
+
 def test_decode_workload_full():
     w = wl.decode(0)
     banner("decode: X [64x4096] row-wise, W [24576x4096] 128x128 + transpose")
