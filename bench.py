@@ -49,6 +49,7 @@ def parse():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-other", action="store_true", help="skip the decode / MXFP8 / MoE kernel timings")
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="rough CPU budget of the oracle baseline sample")
     ap.add_argument("--traffic", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
@@ -276,6 +277,12 @@ def main():
         tf = flops_gemm / t / 1e12
         bf[name] = {"us": round(t * 1e6, 1), "tflops": round(tf, 1), "frac_bf16_peak": round(tf / PEAK_BF16_TFLOPS, 4)}
 
+    other = None
+    if not args.no_other:
+        del copies, bufs, b
+        torch.cuda.empty_cache()
+        other = other_workloads(torch, fb, wl, dev, args.seed)
+
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(w, args.cpu_seconds)
@@ -290,8 +297,134 @@ def main():
                                "1x128 act/grad + 128x128 weight FP8 path, FProp+DGrad+WGrad",
                    "N": N, "C": C, "D": D, "seed": args.seed, "inputs_resident_in_hbm": True},
         "kernels": kernels, "roofline": roofline, "bf16_baseline": bf, "cpu_baseline": cpu,
+        "other_workloads": other,
     }
     print(json.dumps(out), flush=True)
+
+
+def time_cold(torch, fn, flush, reps=10, warmup=2):
+    """Median seconds of fn() on the current stream, each launch preceded
+    (outside the events) by a 1 GiB read so that L2 and the Infinity Cache
+    hold none of its operands."""
+    for _ in range(warmup):
+        fn()
+    ts = []
+    for _ in range(reps):
+        flush.sum()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        fn()
+        e1.record()
+        torch.cuda.synchronize()
+        ts.append(e0.elapsed_time(e1) * 1e-3)
+    return float(np.median(ts))
+
+
+def report(t, alg_bytes, flops=None):
+    """Time, rates and the fraction of the kernel's own roofline,
+    t_min / t with t_min = max(flops / FP8 peak, bytes / HBM peak)."""
+    t_min = max(alg_bytes / (PEAK_HBM_GBS * 1e9), (flops or 0.0) / (PEAK_FP8_TFLOPS * 1e12))
+    e = {"us": round(t * 1e6, 2), "alg_bytes": int(alg_bytes), "gbs": round(alg_bytes / t / 1e9, 1),
+         "bound": "hbm" if alg_bytes / (PEAK_HBM_GBS * 1e9) >= (flops or 0.0) / (PEAK_FP8_TFLOPS * 1e12) else "mfma",
+         "frac_roofline": round(t_min / t, 4)}
+    if flops:
+        e["tflops"] = round(flops / t / 1e12, 1)
+        e["frac_fp8_peak"] = round(flops / t / 1e12 / PEAK_FP8_TFLOPS, 4)
+    return e
+
+
+def other_workloads(torch, fb, wl, dev, seed):
+    """The decode (1x128 and MXFP8) and MoE layers: every kernel timed cold,
+    reported against its own roofline (these shapes are HBM-bound)."""
+    out = {}
+    cd = lambda a, b: (a + b - 1) // b
+    flush = torch.empty(1 << 28, dtype=torch.float32, device=dev).fill_(1.0)
+    to = lambda bits: torch.from_numpy(bits).view(torch.bfloat16).to(dev)
+
+    # decode FProp: X [64 x 4096] against the fused gate+up W [24576 x 4096]
+    w = wl.mx(seed)
+    N, C, D = w["N"], w["C"], w["D"]
+    X, W, dY = to(w["X"]), to(w["W"]), to(w["dY"])
+    xq, xs = fb.fp8_quantize_act_1x128(X)
+    wq, ws, _ = fb.fp8_quantize_weight_128x128(W, transpose=False)
+    y = torch.empty((N, D), dtype=torch.bfloat16, device=dev)
+    dec = {}
+    dec["quant_act_1x128"] = report(time_cold(torch, lambda: fb.fp8_quantize_act_1x128(X, xq, xs), flush),
+                                    N * C * 3 + N * cd(C, 128) * 4)
+    dec["quant_weight"] = report(time_cold(torch, lambda: fb.fp8_quantize_weight_128x128(
+        W, transpose=False, q=wq, s=ws), flush), D * C * 3 + cd(D, 128) * cd(C, 128) * 4)
+    dec["fprop"] = report(time_cold(torch, lambda: fb.fp8_gemm_fprop(xq, xs, wq, ws, N, D, C, y=y), flush),
+                          N * C + D * C + N * cd(C, 128) * 4 + cd(D, 128) * cd(C, 128) * 4 + N * D * 2,
+                          2.0 * N * D * C)
+    out["decode_1x128"] = dec
+
+    # the same tensors through the MXFP8 path (plus dY [64 x 24576])
+    mx = {}
+    q_x = fb.fp8_mx_quantize_1x32(X)
+    q_w = fb.fp8_mx_quantize_1x32(W)
+    q_g = fb.fp8_mx_quantize_1x32(dY)
+    both = lambda r, c: r * c * 2 + 2 * (r * c + r * c // 32)
+    mx["quant_X"] = report(time_cold(torch, lambda: fb.fp8_mx_quantize_1x32(X), flush), both(N, C))
+    mx["quant_W"] = report(time_cold(torch, lambda: fb.fp8_mx_quantize_1x32(W), flush), both(D, C))
+    mx["quant_dY"] = report(time_cold(torch, lambda: fb.fp8_mx_quantize_1x32(dY), flush), both(N, D))
+    dx = torch.empty((N, C), dtype=torch.bfloat16, device=dev)
+    dw = torch.empty((D, C), dtype=torch.bfloat16, device=dev)
+    mx["fprop"] = report(time_cold(torch, lambda: fb.fp8_mx_gemm_fprop(q_x[0], q_x[1], q_w[0], q_w[1], N, D, C, y=y),
+                                   flush), N * C * 33 // 32 + D * C * 33 // 32 + N * D * 2, 2.0 * N * D * C)
+    mx["dgrad"] = report(time_cold(torch, lambda: fb.fp8_mx_gemm_dgrad(q_g[0], q_g[1], q_w[2], q_w[3], N, D, C, dx=dx),
+                                   flush), N * D * 33 // 32 + D * C * 33 // 32 + N * C * 2, 2.0 * N * D * C)
+    Kp = 128   # the token axis (64) padded to one 128-wide block
+    mx["wgrad"] = report(time_cold(torch, lambda: fb.fp8_mx_gemm_wgrad(q_g[2], q_g[3], q_x[2], q_x[3], N, D, C, dw=dw),
+                                   flush), (D + C) * Kp * 33 // 32 + D * C * 2, 2.0 * N * D * C)
+    out["decode_mxfp8"] = mx
+    del X, W, dY, q_x, q_w, q_g, wq, xq, dx, dw, y
+
+    # MoE layer: 4096 tokens, top-8 of 128 experts, hidden 2048, intermediate 768
+    m = wl.moe(seed)
+    offs = m["offsets"]
+    E, I2, H = m["W_gu"].shape
+    I = m["inter"]
+    R = int(offs[-1])
+    od = torch.from_numpy(offs.astype(np.int32)).to(dev)
+    Wgu, Wd = to(m["W_gu"].reshape(E * I2, H)), to(m["W_d"].reshape(E * H, I))
+    Xp, A, dH, dYd = to(m["X_perm"]), to(m["A"]), to(m["dH"]), to(m["dY_d"])
+    moe = {}
+    gu = fb.fp8_quantize_weight_128x128(Wgu)
+    dn = fb.fp8_quantize_weight_128x128(Wd)
+    moe["quant_W_gu"] = report(time_cold(torch, lambda: fb.fp8_quantize_weight_128x128(Wgu, q=gu[0], s=gu[1], qT=gu[2]),
+                                         flush), E * I2 * H * 4)
+    qx = fb.fp8_quantize_transposed_grouped(Xp, od, rowwise=True)
+    qa = fb.fp8_quantize_transposed_grouped(A, od, rowwise=True)
+    qh = fb.fp8_quantize_transposed_grouped(dH, od, rowwise=True)
+    qy = fb.fp8_quantize_transposed_grouped(dYd, od, rowwise=True)
+    moe["quant_dual_X"] = report(time_cold(torch, lambda: fb.fp8_quantize_transposed_grouped(
+        Xp, od, rowwise=True, qT=qx[0], sT=qx[1], q=qx[2], s=qx[3]), flush), R * H * 4)
+    fl_gu, fl_d = 2.0 * R * I2 * H, 2.0 * R * H * I
+    y_gu = torch.empty((R, I2), dtype=torch.bfloat16, device=dev)
+    y_d = torch.empty((R, H), dtype=torch.bfloat16, device=dev)
+    dx_gu = torch.empty((R, H), dtype=torch.bfloat16, device=dev)
+    dx_d = torch.empty((R, I), dtype=torch.bfloat16, device=dev)
+    dw_gu = torch.empty((E, I2, H), dtype=torch.bfloat16, device=dev)
+    dw_d = torch.empty((E, H, I), dtype=torch.bfloat16, device=dev)
+    moe["gu_fprop"] = report(time_cold(torch, lambda: fb.fp8_gemm_fprop_grouped(
+        qx[2], qx[3], gu[0], I2 * gu[0].stride(0), gu[1], (I2 // 128) * gu[1].stride(0), od, R, I2, H, y=y_gu),
+        flush), R * H + E * I2 * H + R * I2 * 2, fl_gu)
+    moe["gu_dgrad"] = report(time_cold(torch, lambda: fb.fp8_gemm_dgrad_grouped(
+        qh[2], qh[3], gu[2], I2, gu[1], (I2 // 128) * gu[1].stride(0), od, R, I2, H, dx=dx_gu),
+        flush), R * I2 + E * I2 * H + R * H * 2, fl_gu)
+    moe["gu_wgrad"] = report(time_cold(torch, lambda: fb.fp8_gemm_wgrad_grouped(
+        qh[0], qh[1], qx[0], qx[1], od, R, I2, H, dw=dw_gu), flush), R * (I2 + H) + E * I2 * H * 2, fl_gu)
+    moe["d_fprop"] = report(time_cold(torch, lambda: fb.fp8_gemm_fprop_grouped(
+        qa[2], qa[3], dn[0], H * dn[0].stride(0), dn[1], (H // 128) * dn[1].stride(0), od, R, H, I, y=y_d),
+        flush), R * I + E * H * I + R * H * 2, fl_d)
+    moe["d_dgrad"] = report(time_cold(torch, lambda: fb.fp8_gemm_dgrad_grouped(
+        qy[2], qy[3], dn[2], H, dn[1], (H // 128) * dn[1].stride(0), od, R, H, I, dx=dx_d),
+        flush), R * H + E * H * I + R * I * 2, fl_d)
+    moe["d_wgrad"] = report(time_cold(torch, lambda: fb.fp8_gemm_wgrad_grouped(
+        qy[0], qy[1], qa[0], qa[1], od, R, H, I, dw=dw_d), flush), R * (H + I) + E * H * I * 2, fl_d)
+    out["moe_layer"] = moe
+    torch.cuda.synchronize()
+    return out
 
 
 def cpu_baseline(w, budget_s: float):

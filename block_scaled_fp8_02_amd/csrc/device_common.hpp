@@ -160,6 +160,55 @@ __device__ __forceinline__ int clamp_valid(int64_t remaining) {
     return remaining >= 8 ? 8 : (remaining <= 0 ? 0 : (int)remaining);
 }
 
+// Grouped (MoE) row segments: expert e owns rows [off[e], off[e+1]); its
+// rows are cut into tiles of `bi` rows, and the experts' tiles are numbered
+// in expert order.  SegPos is a position in that enumeration: expert e, the
+// number of tiles before it, and the number of 128-padded rows before it
+// (sum over earlier experts of round_up(n, 128)).
+struct SegPos {
+    int64_t e, first, P;
+};
+
+// Inclusive prefix sum over the 64 lanes of a wavefront.
+__device__ __forceinline__ int64_t wave_incl_scan(int64_t v) {
+    const int lane = threadIdx.x & 63;
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+        const int64_t t = __shfl_up(v, d);
+        if (lane >= d) v += t;
+    }
+    return v;
+}
+
+// Wave-cooperative search, from position `from` onwards (from.e <= the
+// expert sought), for the expert holding tile number `tile`: 64 experts per
+// step, each lane reading one expert's bounds.  Every lane of the wave
+// returns the same result; e == E means the tile does not exist.
+__device__ __forceinline__ SegPos wave_find_tile(const int32_t* off, int64_t E, int64_t tile, int64_t bi, SegPos from) {
+    const int lane = threadIdx.x & 63;
+    while (from.e < E) {
+        const int64_t e = from.e + lane;
+        const bool valid = e < E;
+        const int64_t n = valid ? (int64_t)off[e + 1] - off[e] : 0;
+        const int64_t nt = (n + bi - 1) / bi, np = (n + 127) / 128 * 128;
+        const int64_t it = wave_incl_scan(nt), ip = wave_incl_scan(np);
+        const uint64_t hit = __ballot(valid && tile < from.first + it);
+        if (hit) {
+            const int l = __builtin_ctzll(hit);
+            SegPos r;
+            r.e = from.e + l;
+            r.first = from.first + __shfl(it - nt, l);
+            r.P = from.P + __shfl(ip - np, l);
+            return r;
+        }
+        from.e += 64;
+        from.first += __shfl(it, 63);
+        from.P += __shfl(ip, 63);
+    }
+    from.e = E;
+    return from;
+}
+
 // Transpose an 8x8 byte block with byte permutes (32 v_perm_b32): rows
 // (lo = bytes 0..3, hi = 4..7) in, columns out.  perm(a, b, sel) picks
 // bytes of the 8-byte value {a:b} (b = bytes 0..3, a = bytes 4..7).

@@ -74,26 +74,12 @@ __device__ __forceinline__ int64_t xcd_remap(int64_t b, int64_t total) {
     return (b % 8) * (total / 8) + b / 8;
 }
 
-// Row tile `tile` of the grouped (MoE) row enumeration -> rows [i0, ihi) of expert e.
-__device__ __forceinline__ void find_row_tile(const int32_t* off, int64_t E, int64_t tile, int64_t BI,
-                                              int64_t& i0, int64_t& ihi, int64_t& e_out) {
-    int64_t acc = 0;
-    for (int64_t e = 0; e < E; ++e) {
-        const int64_t a = off[e], b = off[e + 1];
-        const int64_t tiles = (b - a + BI - 1) / BI;
-        if (tile < acc + tiles) {
-            i0 = a + (tile - acc) * BI;
-            ihi = i0 + BI < b ? i0 + BI : b;
-            e_out = e;
-            return;
-        }
-        acc += tiles;
-    }
-    i0 = 0; ihi = 0; e_out = -1;
-}
+// s_waitcnt immediate that waits until at most n vector-memory operations
+// are outstanding and leaves the LDS/scalar and export counters alone.
+constexpr int vmcnt_imm(int n) { return (n & 0xF) | ((n >> 4) << 14) | (0x7 << 4) | (0xF << 8); }
 
-// BI x BJ block tile, NW waves, wave tile (16*TI) x (16*TJ).
-template <int BI, int BJ, int TI, int TJ, int NW, int SM>
+// BI x BJ block tile, NW waves, wave tile (16*TI) x (16*TJ), NS LDS stages.
+template <int BI, int BJ, int TI, int TJ, int NW, int SM, int NS>
 __global__ __launch_bounds__(64 * NW, 1) void k_gemm(GemmArgs g) {
     constexpr int NT = 64 * NW;
     constexpr int WI = 16 * TI, WJ = 16 * TJ;
@@ -103,13 +89,20 @@ __global__ __launch_bounds__(64 * NW, 1) void k_gemm(GemmArgs g) {
     constexpr int STAGE = (BI + BJ) * 128;
     constexpr int NCH = (BI + BJ) * 8 / NT;                 // 16-byte DMA chunks per thread per stage
     static_assert(NCH * NT == (BI + BJ) * 8, "DMA chunks must divide evenly");
-    static_assert(BI + BJ <= NT, "one scale loader per tile row");
+    constexpr int NSL = (BI + BJ + NT - 1) / NT;           // scale words per thread per stage
+    static_assert(NS >= 2, "at least double buffering");
+    // vector-memory operations a thread issues per stage: NCH chunks + NSL scale words;
+    // at the end of a K step the NS-2 newest stages may still be in flight
+    constexpr int INFLIGHT = (NS - 2) * (NCH + NSL);
+    static_assert(INFLIGHT <= 63, "vmcnt holds at most 63");
+    // the bf16 output tile fits in the stage buffers for the staged epilogue
+    constexpr bool STAGED_OUT = BI * BJ * 2 <= NS * STAGE;
 
-    __shared__ __attribute__((aligned(16))) uint8_t smem[2 * STAGE];
+    __shared__ __attribute__((aligned(16))) uint8_t smem[NS * STAGE];
     // Per K block, one 32-bit scale word per tile row (P rows, then Q rows):
     // the fp32 group/block scale, or for MX the four E8M0 bytes of the row's
-    // four 32-wide sub-blocks.
-    __shared__ __attribute__((aligned(16))) uint32_t sscale[2][NT];
+    // four 32-wide sub-blocks.  Filled by DMA like the operand stages.
+    __shared__ __attribute__((aligned(16))) uint32_t sscale[NS][NSL * NT];
     __shared__ int64_t tinfo[4];
 
     const int tid = threadIdx.x, lane = tid & 63;
@@ -125,10 +118,14 @@ __global__ __launch_bounds__(64 * NW, 1) void k_gemm(GemmArgs g) {
     const int64_t nbj = (g.Nn + BJ - 1) / BJ;
     int64_t i0, ihi, j0, kbase = 0, KB = (g.K + 127) / 128;
     if (g.group_mode == GROUP_ROWS) {
-        if (tid == 0) {
-            int64_t a, b, e;
-            find_row_tile(g.offsets, g.E, blockIdx.y, BI, a, b, e);
-            tinfo[0] = a; tinfo[1] = b; tinfo[2] = e;
+        if (tid < 64) {                                            // wave 0 locates the row tile
+            const SegPos sp = wave_find_tile(g.offsets, g.E, blockIdx.y, BI, SegPos{0, 0, 0});
+            if (tid == 0) {
+                const bool ok = sp.e < g.E;
+                const int64_t a = ok ? g.offsets[sp.e] + (blockIdx.y - sp.first) * BI : 0;
+                const int64_t b = ok ? g.offsets[sp.e + 1] : 0;
+                tinfo[0] = a; tinfo[1] = a + BI < b ? a + BI : b; tinfo[2] = ok ? sp.e : -1;
+            }
         }
         __syncthreads();
         i0 = tinfo[0]; ihi = tinfo[1];
@@ -146,11 +143,19 @@ __global__ __launch_bounds__(64 * NW, 1) void k_gemm(GemmArgs g) {
         j0 = tj * BJ;
         if (g.group_mode == GROUP_K) {
             const int64_t e = blockIdx.y;
-            if (tid == 0) {
+            if (tid < 64) {                                        // wave 0: padded start of expert e
                 int64_t P = 0;
-                for (int64_t x = 0; x < e; ++x) P += (g.offsets[x + 1] - g.offsets[x] + 127) / 128 * 128;
-                tinfo[0] = P / 128;
-                tinfo[1] = (g.offsets[e + 1] - g.offsets[e] + 127) / 128;
+                for (int64_t x0 = 0; x0 < e; x0 += 64) {
+                    const int64_t x = x0 + lane;
+                    int64_t np = x < e ? ((int64_t)g.offsets[x + 1] - g.offsets[x] + 127) / 128 : 0;
+#pragma unroll
+                    for (int d = 32; d >= 1; d >>= 1) np += __shfl_xor(np, d);
+                    P += np;
+                }
+                if (tid == 0) {
+                    tinfo[0] = P;                                  // in 128-row blocks
+                    tinfo[1] = (g.offsets[e + 1] - g.offsets[e] + 127) / 128;
+                }
             }
             __syncthreads();
             kbase = tinfo[0];
@@ -184,35 +189,38 @@ __global__ __launch_bounds__(64 * NW, 1) void k_gemm(GemmArgs g) {
     }
 
     // ---------------------------------------------------- scale loader
-    // Thread t < BI+BJ fetches the scale word of tile row t for each K block
-    // (the others fetch a valid word they never use, which keeps the K loop
-    // free of branches).
-    const char* sbase;
-    int64_t sstep;                                                  // bytes per K block
-    if (tid < BI) {
-        int64_t r = i0 + tid;
-        r = r < ihi ? r : ihi - 1;
-        sbase = static_cast<const char*>(g.sP) + (r * g.ldsp + (SM == SCALE_MX ? kbase * 4 : kbase)) * sq_elem;
-        sstep = 4;
-    } else {
-        int64_t r = j0 + (tid < BI + BJ ? tid - BI : 0);
-        r = r < jhi ? r : jhi - 1;
-        const int64_t rr = SM == SCALE_Q_BLOCK ? r / 128 : r;
-        sbase = sQ + (rr * g.sq_rs + (SM == SCALE_MX ? kbase * 4 : kbase * g.sq_ks)) * sq_elem;
-        sstep = SM == SCALE_MX ? 4 : 4 * g.sq_ks;
+    // Tile row t = s*NT + tid (s < NSL) has its scale word fetched by this
+    // thread for each K block; t >= BI+BJ fetches a valid word that is never
+    // used, so that every thread issues the same DMA sequence.
+    const char* sbase[NSL];
+    int64_t sstep[NSL];                                             // bytes per K block
+#pragma unroll
+    for (int sl = 0; sl < NSL; ++sl) {
+        const int t = sl * NT + tid;
+        if (t < BI) {
+            int64_t r = i0 + t;
+            r = r < ihi ? r : ihi - 1;
+            sbase[sl] = static_cast<const char*>(g.sP) + (r * g.ldsp + (SM == SCALE_MX ? kbase * 4 : kbase)) * sq_elem;
+            sstep[sl] = 4;
+        } else {
+            int64_t r = j0 + (t < BI + BJ ? t - BI : 0);
+            r = r < jhi ? r : jhi - 1;
+            const int64_t rr = SM == SCALE_Q_BLOCK ? r / 128 : r;
+            sbase[sl] = sQ + (rr * g.sq_rs + (SM == SCALE_MX ? kbase * 4 : kbase * g.sq_ks)) * sq_elem;
+            sstep[sl] = SM == SCALE_MX ? 4 : 4 * g.sq_ks;
+        }
     }
-    auto load_scale = [&](int64_t kb) -> uint32_t {
-        return *reinterpret_cast<const uint32_t*>(sbase + kb * sstep);
-    };
 
-    // global_load_lds_dwordx4 writes lane l's 16 bytes to LDS at m0 + 16*l.
-    // It is issued from inline assembly so that the compiler, which cannot
-    // tell the stage being filled from the stage being read, does not stall
-    // the fragment reads on it; completion is awaited explicitly before the
-    // barrier that ends each K step.  The DMAs of the next stage are spread
-    // over the first Q sub-tiles of the current one, so that they queue
-    // behind the matrix work instead of stalling every wave at once.
+    // global_load_lds_dwordx4 writes lane l's 16 bytes to LDS at m0 + 16*l
+    // (global_load_lds_dword: 4 bytes at m0 + 4*l).  Both are issued from
+    // inline assembly, so the compiler tracks no vector-memory loads in the
+    // K loop and inserts no waits of its own: completion is awaited
+    // explicitly (vmcnt) before the barrier that ends each K step, leaving
+    // the NS-2 newer stages in flight.  The DMAs of a stage are spread over
+    // the first Q sub-tiles of a step, so that they queue behind the matrix
+    // work instead of stalling every wave at once.
     const uint32_t lds_base = (uint32_t)(uintptr_t)smem;
+    const uint32_t lds_scale = (uint32_t)(uintptr_t)&sscale[0][0];
 #define FP8B_DMA_PART(kb_, buf_, c0_, c1_)                                                         \
     do {                                                                                            \
         _Pragma("unroll") for (int c = (c0_); c < (c1_); ++c) {                                     \
@@ -229,6 +237,18 @@ __global__ __launch_bounds__(64 * NW, 1) void k_gemm(GemmArgs g) {
                          : "=&s"(m0save) : "s"(la), "v"(soff[c]), "s"(gb) : "memory");             \
         }                                                                                           \
     } while (0)
+#define FP8B_DMA_SCALE(kb_, buf_)                                                                   \
+    do {                                                                                            \
+        _Pragma("unroll") for (int sl = 0; sl < NSL; ++sl) {                                        \
+            const uint32_t la = __builtin_amdgcn_readfirstlane(                                     \
+                lds_scale + (uint32_t)(((buf_) * NSL * NT + sl * NT + wave * 64) * 4));             \
+            const uint64_t ga = (uint64_t)(uintptr_t)(sbase[sl] + (kb_) * sstep[sl]);               \
+            uint32_t m0save;                                                                        \
+            asm volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %1\n\t"                                \
+                         "global_load_lds_dword %2, off\n\ts_mov_b32 m0, %0"                        \
+                         : "=&s"(m0save) : "s"(la), "v"(ga) : "memory");                           \
+        }                                                                                           \
+    } while (0)
     constexpr int DMA_PER_STEP = (NCH + TJ - 1) / TJ > 2 ? (NCH + TJ - 1) / TJ : 2;
 
     v4f acc[TJ][TI];
@@ -238,22 +258,30 @@ __global__ __launch_bounds__(64 * NW, 1) void k_gemm(GemmArgs g) {
         for (int b = 0; b < TI; ++b) acc[a][b] = v4f{0.f, 0.f, 0.f, 0.f};
 
     if (KB > 0) {
-        FP8B_DMA_PART(0, 0, 0, NCH);
-        sscale[0][tid] = load_scale(0);
+        // stages 0 .. NS-2 hold K blocks 0 .. NS-2 (the last block repeated
+        // where there are fewer): every thread issues the same sequence
+#pragma unroll
+        for (int st = 0; st < NS - 1; ++st) {
+            const int64_t kk = st < KB ? st : KB - 1;
+            FP8B_DMA_PART(kk, st, 0, NCH);
+            FP8B_DMA_SCALE(kk, st);
+        }
+        __builtin_amdgcn_s_waitcnt(vmcnt_imm(INFLIGHT));
     }
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
 
     const int prow_l = wi * WI + (lane & 15);                        // tile row of this lane's first P fragment
     const int qrow_l = BI + wj * WJ;                                 // tile row of this wave's first Q row
     const int sh = 8 * (lane >> 4);
+    int buf = 0;                                                     // stage of K block kb
+    int nbuf = NS - 1;                                               // stage that receives block kb + NS - 1
     for (int64_t kb = 0; kb < KB; ++kb) {
-        const int buf = (int)(kb & 1);
-        const int64_t kn = kb + 1 < KB ? kb + 1 : kb;             // the last block reloads itself into
-                                                                   // the idle stage: no branch in the loop
-        const uint32_t snext = load_scale(kn);
+        const int64_t kn = kb + NS - 1 < KB ? kb + NS - 1 : KB - 1;  // past the end the last block is
+                                                                     // reloaded into an idle stage:
+                                                                     // no branch in the loop
         const uint8_t* base = smem + buf * STAGE;
         const uint32_t* sc = sscale[buf];
+        FP8B_DMA_SCALE(kn, nbuf);
 
         // P fragments and P-side scales for the whole K block; Q fragments
         // stream through a two-deep register pipeline (the next Q sub-tile's
@@ -280,7 +308,7 @@ __global__ __launch_bounds__(64 * NW, 1) void k_gemm(GemmArgs g) {
 #pragma unroll
             for (int a = 0; a < TJ; ++a) {
                 if (a * DMA_PER_STEP < NCH)
-                    FP8B_DMA_PART(kn, buf ^ 1, a * DMA_PER_STEP,
+                    FP8B_DMA_PART(kn, nbuf, a * DMA_PER_STEP,
                                   (a + 1) * DMA_PER_STEP < NCH ? (a + 1) * DMA_PER_STEP : NCH);
                 v8i af_n = af;
                 uint32_t eaw_n = eaw;
@@ -297,6 +325,8 @@ __global__ __launch_bounds__(64 * NW, 1) void k_gemm(GemmArgs g) {
                 eaw = eaw_n;
                 __builtin_amdgcn_sched_barrier(0);
             }
+            // a wave tile narrower than the DMA spread issues the rest here
+            if (TJ * DMA_PER_STEP < NCH) FP8B_DMA_PART(kn, nbuf, TJ * DMA_PER_STEP, NCH);
         } else {
             // Software pipeline: step a issues the MFMAs of Q sub-tile a and
             // the promotion FMAs of sub-tile a-1, whose results are ready.
@@ -305,7 +335,7 @@ __global__ __launch_bounds__(64 * NW, 1) void k_gemm(GemmArgs g) {
 #pragma unroll
             for (int a = 0; a <= TJ; ++a) {
                 if (a * DMA_PER_STEP < NCH)
-                    FP8B_DMA_PART(kn, buf ^ 1, a * DMA_PER_STEP,
+                    FP8B_DMA_PART(kn, nbuf, a * DMA_PER_STEP,
                                   (a + 1) * DMA_PER_STEP < NCH ? (a + 1) * DMA_PER_STEP : NCH);
                 v8i af_n = af;
                 uint4 sqa_n = sqa;
@@ -346,14 +376,68 @@ __global__ __launch_bounds__(64 * NW, 1) void k_gemm(GemmArgs g) {
                 __builtin_amdgcn_sched_barrier(0);
             }
         }
-        sscale[buf ^ 1][tid] = snext;
-        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");           // next stage's DMA has landed
+        __builtin_amdgcn_s_waitcnt(vmcnt_imm(INFLIGHT));            // block kb + 1 has landed
         __syncthreads();
+        buf = buf + 1 == NS ? 0 : buf + 1;
+        nbuf = nbuf + 1 == NS ? 0 : nbuf + 1;
     }
 #undef FP8B_DMA_PART
+#undef FP8B_DMA_SCALE
+    // the tail's repeated DMAs target idle stages; let them land before the
+    // stage memory is reused or the block exits
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+    __syncthreads();
 
     // ---------------------------------------------------- epilogue
     const int64_t jw = j0 + wj * WJ;
+    if (STAGED_OUT && !g.out_f32) {
+        // bf16 tile through LDS: lanes hold 4 consecutive columns of one row,
+        // rows stride BJ*2 bytes; 8-byte column chunks are XOR-swizzled by
+        // 2*(row % 16) so that 16 rows' writes hit distinct banks and 16-byte
+        // pairs stay whole.  Rows then leave as contiguous 16-byte stores.
+        uint8_t* stile = smem;
+        constexpr int CPR = BJ / 4;                                  // 8-byte chunks per tile row
+#pragma unroll
+        for (int a = 0; a < TJ; ++a) {
+            const int jl = wj * WJ + a * 16 + 4 * (lane >> 4);
+#pragma unroll
+            for (int b = 0; b < TI; ++b) {
+                const int il = wi * WI + b * 16 + (lane & 15);
+                const v4f r = acc[a][b];
+                uint2 v;
+                v.x = f32_to_bf16(r[0]) | (f32_to_bf16(r[1]) << 16);
+                v.y = f32_to_bf16(r[2]) | (f32_to_bf16(r[3]) << 16);
+                const int ch = (jl >> 2) ^ ((2 * (il & 15)) & (CPR - 1) & ~1);
+                *reinterpret_cast<uint2*>(stile + (il * CPR + ch) * 8) = v;
+            }
+        }
+        __syncthreads();
+        constexpr int PPR = CPR / 2;                                 // 16-byte pairs per tile row
+        const bool full_cols = jhi - j0 == BJ && (g.ldo % 8) == 0;
+#pragma unroll
+        for (int it = 0; it < (BI * PPR + NT - 1) / NT; ++it) {
+            const int q = it * NT + tid;
+            if (q < BI * PPR) {
+                const int il = q / PPR, pp = q % PPR;
+                const int64_t i = i0 + il;
+                if (i < ihi) {
+                    const int ch = (2 * pp) ^ ((2 * (il & 15)) & (CPR - 1) & ~1);
+                    const uint4 v = *reinterpret_cast<const uint4*>(stile + (il * CPR + ch) * 8);
+                    const int64_t j = j0 + 8 * pp;
+                    uint16_t* o = reinterpret_cast<uint16_t*>(O) + i * g.ldo + j;
+                    if (full_cols) {
+                        *reinterpret_cast<uint4*>(o) = v;
+                    } else {
+                        const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+                        for (int e = 0; e < 8; ++e)
+                            if (j + e < g.Nn) o[e] = (uint16_t)(w[e >> 1] >> (16 * (e & 1)));
+                    }
+                }
+            }
+        }
+        return;
+    }
 #pragma unroll
     for (int a = 0; a < TJ; ++a) {
         const int64_t j = jw + a * 16 + 4 * (lane >> 4);
@@ -393,7 +477,7 @@ __global__ __launch_bounds__(64 * NW, 1) void k_gemm(GemmArgs g) {
     }
 }
 
-template <int BI, int BJ, int TI, int TJ, int NW, int SM>
+template <int BI, int BJ, int TI, int TJ, int NW, int SM, int NS>
 static hipError_t launch_cfg(const GemmArgs& a, hipStream_t st) {
     const int64_t nbj = (a.Nn + BJ - 1) / BJ;
     const int64_t nbi = (a.M + BI - 1) / BI;
@@ -410,18 +494,21 @@ static hipError_t launch_cfg(const GemmArgs& a, hipStream_t st) {
         if (tiles > 0x7FFFFFFF || z > 65535) return hipErrorInvalidValue;
         grid = dim3((unsigned)tiles, (unsigned)z, 1);
     }
-    k_gemm<BI, BJ, TI, TJ, NW, SM><<<grid, 64 * NW, 0, st>>>(a);
+    k_gemm<BI, BJ, TI, TJ, NW, SM, NS><<<grid, 64 * NW, 0, st>>>(a);
     return hipGetLastError();
 }
 
 template <int SM>
 static hipError_t launch_sm(const GemmArgs& a, hipStream_t st) {
-    // Small-M (decode) problems take 64x64 tiles so the weight stream is
-    // spread over many blocks; large problems take 256x256 tiles with eight
-    // waves (two per SIMD).  The per-element arithmetic is the same in both.
-    if (a.group_mode == GROUP_NONE && a.M <= 64)
-        return launch_cfg<64, 64, 4, 1, 4, SM>(a, st);
-    return launch_cfg<256, 256, 4, 8, 8, SM>(a, st);        // 8 waves of 64 x 128
+    // Few rows (decode, M <= 64): the weight stream dominates, so the tile is
+    // narrow along Q (32 or 16 rows) to spread it over at least one block per
+    // compute unit, and 4 or 8 stages keep enough of it in flight.  The
+    // per-element arithmetic is the same in every configuration.
+    if (a.M <= 64 && a.group_mode == GROUP_NONE) {
+        if ((a.Nn + 31) / 32 >= 512) return launch_cfg<64, 32, 4, 1, 2, SM, 4>(a, st);
+        return launch_cfg<64, 16, 2, 1, 2, SM, 8>(a, st);
+    }
+    return launch_cfg<256, 256, 4, 8, 8, SM, 2>(a, st);       // 8 waves of 64 x 128
 }
 
 hipError_t launch_gemm(const GemmArgs& a, hipStream_t st) {

@@ -134,6 +134,36 @@ __device__ __forceinline__ void unpack_row(const RawTile<float>& rt, int i, floa
     v[4] = __uint_as_float(b.x); v[5] = __uint_as_float(b.y); v[6] = __uint_as_float(b.z); v[7] = __uint_as_float(b.w);
 }
 
+// Element (p, j) of a thread's raw 8x8 values as fp32.
+__device__ __forceinline__ float raw_elem(const RawTile<uint16_t>& rt, int p, int j) {
+    const uint4 w = rt.w[p];
+    const uint32_t u = j < 2 ? w.x : j < 4 ? w.y : j < 6 ? w.z : w.w;
+    return (j & 1) ? __uint_as_float(u & 0xFFFF0000u) : __uint_as_float(u << 16);
+}
+
+__device__ __forceinline__ float raw_elem(const RawTile<float>& rt, int p, int j) {
+    const uint4 w = rt.w[2 * p + (j >> 2)];
+    const int i = j & 3;
+    return __uint_as_float(i == 0 ? w.x : i == 1 ? w.y : i == 2 ? w.z : w.w);
+}
+
+// A thread's values, either unpacked once into 64 fp32 registers (KEEPF)
+// or unpacked from the raw registers at every use.
+template <typename T, bool KEEPF> struct TileVals;
+template <typename T> struct TileVals<T, true> {
+    float v[8][8];
+    __device__ __forceinline__ void set(const RawTile<T>& rt) {
+#pragma unroll
+        for (int p = 0; p < 8; ++p) unpack_row(rt, p, v[p]);
+    }
+    __device__ __forceinline__ float operator()(int p, int j) const { return v[p][j]; }
+};
+template <typename T> struct TileVals<T, false> {
+    RawTile<T> r;
+    __device__ __forceinline__ void set(const RawTile<T>& rt) { r = rt; }
+    __device__ __forceinline__ float operator()(int p, int j) const { return raw_elem(r, p, j); }
+};
+
 // Where a tile lies: input rows [a, b), first column cb, first position of
 // its transposed codes pos, row-tile index rt (scale row of QT_WEIGHT) and
 // column-tile index ct.
@@ -142,11 +172,7 @@ struct TileAt {
     bool valid;
 };
 
-struct TileCursor {       // grouped mode: expert e, its first row tile, its padded start
-    int64_t e, first, P;
-};
-
-__device__ __forceinline__ TileAt locate_tile(const QuantTileArgs& A, int64_t k, TileCursor& cur) {
+__device__ __forceinline__ TileAt locate_tile(const QuantTileArgs& A, int64_t k, SegPos& cur) {
     TileAt at;
     at.rt = k / A.col_tiles;
     at.ct = k - at.rt * A.col_tiles;
@@ -159,23 +185,17 @@ __device__ __forceinline__ TileAt locate_tile(const QuantTileArgs& A, int64_t k,
         return at;
     }
     // the cursor only moves forward: a block's tile index never decreases
-    while (cur.e < A.E) {
-        const int64_t lo = A.offsets[cur.e], hi = A.offsets[cur.e + 1];
-        const int64_t nt = (hi - lo + 127) / 128;
-        if (at.rt < cur.first + nt) {
-            const int64_t g = at.rt - cur.first;
-            at.a = lo + 128 * g;
-            at.b = at.a + 128 < hi ? at.a + 128 : hi;
-            at.pos = cur.P + 128 * g;
-            at.valid = true;
-            return at;
-        }
-        cur.first += nt;
-        cur.P += 128 * nt;
-        ++cur.e;
+    cur = wave_find_tile(A.offsets, A.E, at.rt, 128, cur);
+    at.valid = cur.e < A.E;
+    if (!at.valid) {
+        at.a = at.b = at.pos = 0;
+        return at;
     }
-    at.a = at.b = at.pos = 0;
-    at.valid = false;
+    const int64_t hi = A.offsets[cur.e + 1];
+    const int64_t g = at.rt - cur.first;
+    at.a = A.offsets[cur.e] + 128 * g;
+    at.b = at.a + 128 < hi ? at.a + 128 : hi;
+    at.pos = cur.P + 128 * g;
     return at;
 }
 
@@ -195,8 +215,8 @@ __device__ __forceinline__ void load_tile(const QuantTileArgs& A, const TileAt& 
 // Codes of one thread's 8x8 values with one scale per row (PER_ROW) or
 // per column: S = S_group*P, r = RN32(1/S), P = prescale(S_group).  The
 // multiplication by P is skipped when every P of the tile is 1 (plain).
-template <bool PER_ROW, bool SCALED>
-__device__ __forceinline__ void encode_8x8_v(const float v[8][8], const float S[8], const float r[8], const float P[8],
+template <bool PER_ROW, bool SCALED, class V>
+__device__ __forceinline__ void encode_8x8_v(const V& v, const float S[8], const float r[8], const float P[8],
                                              uint32_t lo[8], uint32_t hi[8]) {
 #pragma unroll
     for (int p = 0; p < 8; ++p) {
@@ -204,15 +224,15 @@ __device__ __forceinline__ void encode_8x8_v(const float v[8][8], const float S[
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
             const int g = PER_ROW ? p : j;
-            y[j] = quotient32(SCALED ? v[p][j] * P[g] : v[p][j], S[g], r[g]);
+            y[j] = quotient32(SCALED ? v(p, j) * P[g] : v(p, j), S[g], r[g]);
         }
         lo[p] = e4m3_pack4_q(y[0], y[1], y[2], y[3]);
         hi[p] = e4m3_pack4_q(y[4], y[5], y[6], y[7]);
     }
 }
 
-template <bool PER_ROW>
-__device__ __forceinline__ void encode_8x8(bool plain, const float v[8][8], const float S[8], const float r[8],
+template <bool PER_ROW, class V>
+__device__ __forceinline__ void encode_8x8(bool plain, const V& v, const float S[8], const float r[8],
                                            const float P[8], uint32_t lo[8], uint32_t hi[8]) {
     if (plain)
         encode_8x8_v<PER_ROW, false>(v, S, r, P, lo, hi);
@@ -234,8 +254,11 @@ __device__ __forceinline__ void lds_barrier() {
     asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 
-template <typename T, int MODE>
-__global__ __launch_bounds__(256, 2) void k_quant_tiles(QuantTileArgs A) {
+// PREFETCH: load the next tile into a second register set while this one
+// is quantized.  KEEPF: hold the values as fp32 (else unpack at each use).
+// MINB: blocks per compute unit the register budget is sized for.
+template <typename T, int MODE, bool PREFETCH, bool KEEPF, int MINB>
+__global__ __launch_bounds__(256, MINB) void k_quant_tiles(QuantTileArgs A) {
     __shared__ __attribute__((aligned(16))) float red_col[16][128];   // [row slice][column]
     __shared__ __attribute__((aligned(16))) float red_row[16][128];   // [column slice][row]
     __shared__ __attribute__((aligned(16))) float sc_col[3][128];     // S*P, RN32(1/(S*P)), P per column
@@ -249,7 +272,7 @@ __global__ __launch_bounds__(256, 2) void k_quant_tiles(QuantTileArgs A) {
     const bool want_qT = MODE != QT_WEIGHT || A.qT != nullptr;
     if (t == 0) scaled_flag = 0;
 
-    TileCursor cur{0, 0, 0};
+    SegPos cur{0, 0, 0};
     int64_t k = blockIdx.x;
     TileAt at = locate_tile(A, k, cur);
     RawTile<T> raw;
@@ -257,13 +280,11 @@ __global__ __launch_bounds__(256, 2) void k_quant_tiles(QuantTileArgs A) {
     lds_barrier();
 
     while (at.valid) {
-        float v[8][8];
-#pragma unroll
-        for (int p = 0; p < 8; ++p) unpack_row(raw, p, v[p]);
-        // prefetch the next tile while this one is quantized
+        TileVals<T, KEEPF> v;
+        v.set(raw);
         const int64_t kn = k + gridDim.x;
         const TileAt nx = locate_tile(A, kn, cur);
-        if (nx.valid) load_tile<T>(A, nx, rg, cg, raw);
+        if (PREFETCH && nx.valid) load_tile<T>(A, nx, rg, cg, raw);   // next tile, while this one is quantized
 
         uint32_t lo[8], hi[8];
         if (MODE == QT_WEIGHT) {
@@ -271,7 +292,7 @@ __global__ __launch_bounds__(256, 2) void k_quant_tiles(QuantTileArgs A) {
 #pragma unroll
             for (int p = 0; p < 8; ++p)
 #pragma unroll
-                for (int j = 0; j < 8; ++j) m = fmaxf(m, fabsf(v[p][j]));
+                for (int j = 0; j < 8; ++j) m = fmaxf(m, fabsf(v(p, j)));
             m = max64(m);
             if (lane == 0) red4[wave] = m;
             lds_barrier();                                           // (1)
@@ -298,7 +319,7 @@ __global__ __launch_bounds__(256, 2) void k_quant_tiles(QuantTileArgs A) {
                 float m = 0.0f;
 #pragma unroll
                 for (int j = 0; j < 8; ++j) {
-                    const float a = fabsf(v[p][j]);
+                    const float a = fabsf(v(p, j));
                     cm[j] = fmaxf(cm[j], a);
                     m = fmaxf(m, a);
                 }
@@ -381,6 +402,7 @@ __global__ __launch_bounds__(256, 2) void k_quant_tiles(QuantTileArgs A) {
             }
         }
         if (MODE != QT_WEIGHT && t == 0) scaled_flag = 0;   // every wave has read it (before barrier 3)
+        if (!PREFETCH && nx.valid) load_tile<T>(A, nx, rg, cg, raw);
         k = kn;
         at = nx;
     }
@@ -444,9 +466,9 @@ static hipError_t launch_tiles(bool in_bf16, const QuantTileArgs& A, hipStream_t
     const int64_t blocks = tile_grid(A.tiles);
     if (blocks <= 0) return hipSuccess;
     if (in_bf16)
-        k_quant_tiles<uint16_t, MODE><<<dim3((unsigned)blocks), 256, 0, st>>>(A);
+        k_quant_tiles<uint16_t, MODE, true, true, 2><<<dim3((unsigned)blocks), 256, 0, st>>>(A);
     else
-        k_quant_tiles<float, MODE><<<dim3((unsigned)blocks), 256, 0, st>>>(A);
+        k_quant_tiles<float, MODE, true, true, 2><<<dim3((unsigned)blocks), 256, 0, st>>>(A);
     return hipGetLastError();
 }
 
