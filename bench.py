@@ -277,6 +277,48 @@ def main():
         tf = flops_gemm / t / 1e12
         bf[name] = {"us": round(t * 1e6, 1), "tflops": round(tf, 1), "frac_bf16_peak": round(tf / PEAK_BF16_TFLOPS, 4)}
 
+    # measured ceilings on this GPU, same process: a streaming copy (1 GiB
+    # read + 1 GiB written) and the per-tensor-scaled fp8 GEMM of hipBLASLt
+    # on the same codes (no per-block scales: an upper reference for the
+    # block-scaled kernels, which also pay the per-block promotion)
+    ceil = {}
+    src = torch.empty(1 << 28, dtype=torch.float32, device=dev).fill_(1.0)
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(10):
+        dst.copy_(src)
+    e1.record()
+    torch.cuda.synchronize()
+    copy_gbs = 2 * src.numel() * 4 / (e0.elapsed_time(e1) * 1e-3 / 10) / 1e9
+    ceil["hbm_copy_gbs"] = round(copy_gbs, 1)
+    del src, dst
+    for n in ("quant_weight", "quant_dual_X", "quant_dual_dY"):
+        kernels[n]["frac_measured_copy"] = round(kernels[n]["gbs"] / copy_gbs, 4)
+    one = torch.ones((), device=dev)
+    f8 = lambda t: t.view(torch.float8_e4m3fn)
+    tw = {}
+    for name, (a_, b_) in (("fprop", (b["xq"], b["wq"])), ("dgrad", (b["gq"], b["wqT"])),
+                           ("wgrad", (b["gqT"], b["xqT"]))):
+        try:
+            fn = lambda: torch._scaled_mm(f8(a_), f8(b_).t(), scale_a=one, scale_b=one, out_dtype=torch.bfloat16)
+            for _ in range(3):
+                fn()
+            torch.cuda.synchronize()
+            e0.record()
+            for _ in range(10):
+                fn()
+            e1.record()
+            torch.cuda.synchronize()
+            t = e0.elapsed_time(e1) * 1e-3 / 10
+            tw[name] = {"us": round(t * 1e6, 1), "tflops": round(flops_gemm / t / 1e12, 1)}
+        except Exception as ex:                                     # no fp8 GEMM in this torch build
+            tw[name] = {"error": str(ex)[:120]}
+    ceil["fp8_tensorwise_hipblaslt"] = tw
+
     other = None
     if not args.no_other:
         del copies, bufs, b
@@ -297,6 +339,7 @@ def main():
                                "1x128 act/grad + 128x128 weight FP8 path, FProp+DGrad+WGrad",
                    "N": N, "C": C, "D": D, "seed": args.seed, "inputs_resident_in_hbm": True},
         "kernels": kernels, "roofline": roofline, "bf16_baseline": bf, "cpu_baseline": cpu,
+        "measured_ceilings": ceil,
         "other_workloads": other,
     }
     print(json.dumps(out), flush=True)

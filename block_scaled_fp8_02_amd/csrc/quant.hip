@@ -134,34 +134,14 @@ __device__ __forceinline__ void unpack_row(const RawTile<float>& rt, int i, floa
     v[4] = __uint_as_float(b.x); v[5] = __uint_as_float(b.y); v[6] = __uint_as_float(b.z); v[7] = __uint_as_float(b.w);
 }
 
-// Element (p, j) of a thread's raw 8x8 values as fp32.
-__device__ __forceinline__ float raw_elem(const RawTile<uint16_t>& rt, int p, int j) {
-    const uint4 w = rt.w[p];
-    const uint32_t u = j < 2 ? w.x : j < 4 ? w.y : j < 6 ? w.z : w.w;
-    return (j & 1) ? __uint_as_float(u & 0xFFFF0000u) : __uint_as_float(u << 16);
-}
-
-__device__ __forceinline__ float raw_elem(const RawTile<float>& rt, int p, int j) {
-    const uint4 w = rt.w[2 * p + (j >> 2)];
-    const int i = j & 3;
-    return __uint_as_float(i == 0 ? w.x : i == 1 ? w.y : i == 2 ? w.z : w.w);
-}
-
-// A thread's values, either unpacked once into 64 fp32 registers (KEEPF)
-// or unpacked from the raw registers at every use.
-template <typename T, bool KEEPF> struct TileVals;
-template <typename T> struct TileVals<T, true> {
+// A thread's 8x8 values, unpacked once into fp32 registers.
+template <typename T> struct TileVals {
     float v[8][8];
     __device__ __forceinline__ void set(const RawTile<T>& rt) {
 #pragma unroll
         for (int p = 0; p < 8; ++p) unpack_row(rt, p, v[p]);
     }
     __device__ __forceinline__ float operator()(int p, int j) const { return v[p][j]; }
-};
-template <typename T> struct TileVals<T, false> {
-    RawTile<T> r;
-    __device__ __forceinline__ void set(const RawTile<T>& rt) { r = rt; }
-    __device__ __forceinline__ float operator()(int p, int j) const { return raw_elem(r, p, j); }
 };
 
 // Where a tile lies: input rows [a, b), first column cb, first position of
@@ -172,22 +152,40 @@ struct TileAt {
     bool valid;
 };
 
+// Tiles are numbered in bands of QT_BAND row tiles walked column by
+// column, so that the tiles in flight at one time (one per resident block,
+// consecutive numbers) cover QT_BAND row tiles x a few column tiles: the
+// input, the row-wise codes and the transposed codes are all touched in runs
+// of several KB rather than one of them in 128-byte pieces.
+constexpr int64_t QT_BAND = 32;
+
 __device__ __forceinline__ TileAt locate_tile(const QuantTileArgs& A, int64_t k, SegPos& cur) {
     TileAt at;
-    at.rt = k / A.col_tiles;
-    at.ct = k - at.rt * A.col_tiles;
+    at.valid = k < A.tiles;
+    const int64_t nr = A.tiles / A.col_tiles;                     // row tiles (grouped: an upper bound)
+    const int64_t band = k / (QT_BAND * A.col_tiles);
+    const int64_t r0 = band * QT_BAND;
+    const int64_t rows_b = nr - r0 < QT_BAND ? nr - r0 : QT_BAND;
+    const int64_t rin = k - band * QT_BAND * A.col_tiles;
+    at.rt = r0 + (rows_b > 0 ? rin % rows_b : 0);
+    at.ct = rows_b > 0 ? rin / rows_b : 0;
     at.cb = at.ct * 128;
     if (A.offsets == nullptr) {
-        at.valid = k < A.tiles;
         at.a = at.rt * 128;
         at.b = at.a + 128 < A.rows ? at.a + 128 : A.rows;
         at.pos = at.a;
         return at;
     }
-    // the cursor only moves forward: a block's tile index never decreases
+    if (!at.valid) {
+        at.a = at.b = at.pos = 0;
+        return at;
+    }
+    // a block's row-tile index normally only grows; search afresh if not
+    if (at.rt < cur.first) cur = SegPos{0, 0, 0};
     cur = wave_find_tile(A.offsets, A.E, at.rt, 128, cur);
     at.valid = cur.e < A.E;
-    if (!at.valid) {
+    if (!at.valid) {                                               // past the experts' last tile
+        cur = SegPos{0, 0, 0};
         at.a = at.b = at.pos = 0;
         return at;
     }
@@ -254,11 +252,8 @@ __device__ __forceinline__ void lds_barrier() {
     asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 
-// PREFETCH: load the next tile into a second register set while this one
-// is quantized.  KEEPF: hold the values as fp32 (else unpack at each use).
-// MINB: blocks per compute unit the register budget is sized for.
-template <typename T, int MODE, bool PREFETCH, bool KEEPF, int MINB>
-__global__ __launch_bounds__(256, MINB) void k_quant_tiles(QuantTileArgs A) {
+template <typename T, int MODE>
+__global__ __launch_bounds__(256, 2) void k_quant_tiles(QuantTileArgs A) {
     __shared__ __attribute__((aligned(16))) float red_col[16][128];   // [row slice][column]
     __shared__ __attribute__((aligned(16))) float red_row[16][128];   // [column slice][row]
     __shared__ __attribute__((aligned(16))) float sc_col[3][128];     // S*P, RN32(1/(S*P)), P per column
@@ -279,12 +274,16 @@ __global__ __launch_bounds__(256, MINB) void k_quant_tiles(QuantTileArgs A) {
     if (at.valid) load_tile<T>(A, at, rg, cg, raw);
     lds_barrier();
 
-    while (at.valid) {
-        TileVals<T, KEEPF> v;
+    for (; k < A.tiles; k += gridDim.x) {
+        const TileAt nx = locate_tile(A, k + gridDim.x, cur);
+        if (!at.valid) {                                           // (grouped) a tile past an expert's end
+            if (nx.valid) load_tile<T>(A, nx, rg, cg, raw);
+            at = nx;
+            continue;
+        }
+        TileVals<T> v;
         v.set(raw);
-        const int64_t kn = k + gridDim.x;
-        const TileAt nx = locate_tile(A, kn, cur);
-        if (PREFETCH && nx.valid) load_tile<T>(A, nx, rg, cg, raw);   // next tile, while this one is quantized
+        if (nx.valid) load_tile<T>(A, nx, rg, cg, raw);            // next tile, while this one is quantized
 
         uint32_t lo[8], hi[8];
         if (MODE == QT_WEIGHT) {
@@ -402,8 +401,6 @@ __global__ __launch_bounds__(256, MINB) void k_quant_tiles(QuantTileArgs A) {
             }
         }
         if (MODE != QT_WEIGHT && t == 0) scaled_flag = 0;   // every wave has read it (before barrier 3)
-        if (!PREFETCH && nx.valid) load_tile<T>(A, nx, rg, cg, raw);
-        k = kn;
         at = nx;
     }
 }
@@ -466,9 +463,9 @@ static hipError_t launch_tiles(bool in_bf16, const QuantTileArgs& A, hipStream_t
     const int64_t blocks = tile_grid(A.tiles);
     if (blocks <= 0) return hipSuccess;
     if (in_bf16)
-        k_quant_tiles<uint16_t, MODE, true, true, 2><<<dim3((unsigned)blocks), 256, 0, st>>>(A);
+        k_quant_tiles<uint16_t, MODE><<<dim3((unsigned)blocks), 256, 0, st>>>(A);
     else
-        k_quant_tiles<float, MODE, true, true, 2><<<dim3((unsigned)blocks), 256, 0, st>>>(A);
+        k_quant_tiles<float, MODE><<<dim3((unsigned)blocks), 256, 0, st>>>(A);
     return hipGetLastError();
 }
 
