@@ -74,6 +74,17 @@ __device__ __forceinline__ int64_t xcd_remap(int64_t b, int64_t total) {
     return (b % 8) * (total / 8) + b / 8;
 }
 
+// A value the whole block agrees on (read from LDS after a barrier), moved
+// to scalar registers so that addresses built from it stay scalar.
+__device__ __forceinline__ int64_t uniform64(int64_t v) {
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(uint64_t)v);
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)((uint64_t)v >> 32));
+    return (int64_t)(((uint64_t)hi << 32) | lo);
+}
+
+// Experts one GROUP_K block walks through at most.
+constexpr int MAX_EPB = 64;
+
 // s_waitcnt immediate that waits until at most n vector-memory operations
 // are outstanding and leaves the LDS/scalar and export counters alone.
 constexpr int vmcnt_imm(int n) { return (n & 0xF) | ((n >> 4) << 14) | (0x7 << 4) | (0xF << 8); }
@@ -104,6 +115,7 @@ __global__ __launch_bounds__(64 * NW, 1) void k_gemm(GemmArgs g) {
     // four 32-wide sub-blocks.  Filled by DMA like the operand stages.
     __shared__ __attribute__((aligned(16))) uint32_t sscale[NS][NSL * NT];
     __shared__ int64_t tinfo[4];
+    __shared__ int32_t ekb[MAX_EPB];                                // GROUP_K: K blocks of each expert
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -117,6 +129,7 @@ __global__ __launch_bounds__(64 * NW, 1) void k_gemm(GemmArgs g) {
     const size_t o_elem = g.out_f32 ? 4 : 2;
     const int64_t nbj = (g.Nn + BJ - 1) / BJ;
     int64_t i0, ihi, j0, kbase = 0, KB = (g.K + 127) / 128;
+    int64_t e_first = 0, e_end = 1;                                 // GROUP_K: the block's experts
     if (g.group_mode == GROUP_ROWS) {
         if (tid < 64) {                                            // wave 0 locates the row tile
             const SegPos sp = wave_find_tile(g.offsets, g.E, blockIdx.y, BI, SegPos{0, 0, 0});
@@ -128,8 +141,8 @@ __global__ __launch_bounds__(64 * NW, 1) void k_gemm(GemmArgs g) {
             }
         }
         __syncthreads();
-        i0 = tinfo[0]; ihi = tinfo[1];
-        const int64_t e = tinfo[2];
+        i0 = uniform64(tinfo[0]); ihi = uniform64(tinfo[1]);
+        const int64_t e = uniform64(tinfo[2]);
         if (e < 0) return;                                         // whole block
         j0 = (int64_t)blockIdx.x * BJ;
         Q += e * g.q_estride;
@@ -142,25 +155,33 @@ __global__ __launch_bounds__(64 * NW, 1) void k_gemm(GemmArgs g) {
         ihi = i0 + BI < g.M ? i0 + BI : g.M;
         j0 = tj * BJ;
         if (g.group_mode == GROUP_K) {
-            const int64_t e = blockIdx.y;
-            if (tid < 64) {                                        // wave 0: padded start of expert e
+            // experts [e_first, e_end) in turn, for the same output tile: their
+            // K ranges are consecutive in the padded token axis, so the K loop
+            // runs through all of them and stores one output tile per expert
+            e_first = (int64_t)blockIdx.y * g.epb;
+            e_end = e_first + g.epb < g.E ? e_first + g.epb : g.E;
+            if (tid < 64) {                                        // wave 0: padded start, K blocks
                 int64_t P = 0;
-                for (int64_t x0 = 0; x0 < e; x0 += 64) {
+                for (int64_t x0 = 0; x0 < e_first; x0 += 64) {
                     const int64_t x = x0 + lane;
-                    int64_t np = x < e ? ((int64_t)g.offsets[x + 1] - g.offsets[x] + 127) / 128 : 0;
+                    int64_t np = x < e_first ? ((int64_t)g.offsets[x + 1] - g.offsets[x] + 127) / 128 : 0;
 #pragma unroll
                     for (int d = 32; d >= 1; d >>= 1) np += __shfl_xor(np, d);
                     P += np;
                 }
+                const int64_t x = e_first + lane;
+                int64_t kx = x < e_end ? ((int64_t)g.offsets[x + 1] - g.offsets[x] + 127) / 128 : 0;
+                if (lane < MAX_EPB) ekb[lane] = (int32_t)kx;
+#pragma unroll
+                for (int d = 32; d >= 1; d >>= 1) kx += __shfl_xor(kx, d);
                 if (tid == 0) {
                     tinfo[0] = P;                                  // in 128-row blocks
-                    tinfo[1] = (g.offsets[e + 1] - g.offsets[e] + 127) / 128;
+                    tinfo[1] = kx;
                 }
             }
             __syncthreads();
-            kbase = tinfo[0];
-            KB = tinfo[1];
-            O += e * g.o_estride * o_elem;
+            kbase = uniform64(tinfo[0]);
+            KB = uniform64(tinfo[1]);
         }
     }
     const int64_t jhi = j0 + BJ < g.Nn ? j0 + BJ : g.Nn;
@@ -191,25 +212,32 @@ __global__ __launch_bounds__(64 * NW, 1) void k_gemm(GemmArgs g) {
     // ---------------------------------------------------- scale loader
     // Tile row t = s*NT + tid (s < NSL) has its scale word fetched by this
     // thread for each K block; t >= BI+BJ fetches a valid word that is never
-    // used, so that every thread issues the same DMA sequence.
-    const char* sbase[NSL];
+    // used, so that every thread issues the same DMA sequence.  BI is a
+    // multiple of 64, so a wave's rows are all P rows or all Q rows: the
+    // address is a wave-uniform base (SGPRs) plus a small per-lane offset.
+    const char* sbase[NSL];                                         // wave-uniform, at K block 0
     int64_t sstep[NSL];                                             // bytes per K block
+    uint32_t soffs[NSL];                                            // per lane
 #pragma unroll
     for (int sl = 0; sl < NSL; ++sl) {
         const int t = sl * NT + tid;
-        if (t < BI) {
+        if (sl * NT + wave * 64 < BI) {                             // the wave holds P rows
             int64_t r = i0 + t;
             r = r < ihi ? r : ihi - 1;
-            sbase[sl] = static_cast<const char*>(g.sP) + (r * g.ldsp + (SM == SCALE_MX ? kbase * 4 : kbase)) * sq_elem;
+            sbase[sl] = static_cast<const char*>(g.sP) + (i0 * g.ldsp + (SM == SCALE_MX ? kbase * 4 : kbase)) * sq_elem;
+            soffs[sl] = (uint32_t)((r - i0) * g.ldsp * sq_elem);
             sstep[sl] = 4;
         } else {
             int64_t r = j0 + (t < BI + BJ ? t - BI : 0);
             r = r < jhi ? r : jhi - 1;
             const int64_t rr = SM == SCALE_Q_BLOCK ? r / 128 : r;
-            sbase[sl] = sQ + (rr * g.sq_rs + (SM == SCALE_MX ? kbase * 4 : kbase * g.sq_ks)) * sq_elem;
+            const int64_t rr0 = SM == SCALE_Q_BLOCK ? j0 / 128 : j0;
+            sbase[sl] = sQ + (rr0 * g.sq_rs + (SM == SCALE_MX ? kbase * 4 : kbase * g.sq_ks)) * sq_elem;
+            soffs[sl] = (uint32_t)((rr - rr0) * g.sq_rs * sq_elem);
             sstep[sl] = SM == SCALE_MX ? 4 : 4 * g.sq_ks;
         }
     }
+    static_assert(BI % 64 == 0, "P and Q scale rows must not share a wave");
 
     // global_load_lds_dwordx4 writes lane l's 16 bytes to LDS at m0 + 16*l
     // (global_load_lds_dword: 4 bytes at m0 + 4*l).  Both are issued from
@@ -242,11 +270,14 @@ __global__ __launch_bounds__(64 * NW, 1) void k_gemm(GemmArgs g) {
         _Pragma("unroll") for (int sl = 0; sl < NSL; ++sl) {                                        \
             const uint32_t la = __builtin_amdgcn_readfirstlane(                                     \
                 lds_scale + (uint32_t)(((buf_) * NSL * NT + sl * NT + wave * 64) * 4));             \
-            const uint64_t ga = (uint64_t)(uintptr_t)(sbase[sl] + (kb_) * sstep[sl]);               \
+            const uint64_t gv = (uint64_t)(uintptr_t)(sbase[sl] + (kb_) * sstep[sl]);               \
+            const uint64_t gb =                                                                     \
+                ((uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(gv >> 32)) << 32) |  \
+                (uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)gv);                   \
             uint32_t m0save;                                                                        \
             asm volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %1\n\t"                                \
-                         "global_load_lds_dword %2, off\n\ts_mov_b32 m0, %0"                        \
-                         : "=&s"(m0save) : "s"(la), "v"(ga) : "memory");                           \
+                         "global_load_lds_dword %2, %3\n\ts_mov_b32 m0, %0"                         \
+                         : "=&s"(m0save) : "s"(la), "v"(soffs[sl]), "s"(gb) : "memory");           \
         }                                                                                           \
     } while (0)
     constexpr int DMA_PER_STEP = (NCH + TJ - 1) / TJ > 2 ? (NCH + TJ - 1) / TJ : 2;
@@ -272,10 +303,114 @@ __global__ __launch_bounds__(64 * NW, 1) void k_gemm(GemmArgs g) {
 
     const int prow_l = wi * WI + (lane & 15);                        // tile row of this lane's first P fragment
     const int qrow_l = BI + wj * WJ;                                 // tile row of this wave's first Q row
+    // Direct epilogue: lane stores its 4 consecutive outputs of one row.
+    const int64_t jw = j0 + wj * WJ;
+    auto store_direct = [&](char* Ob) {
+        // an opaque copy of the lane index keeps the compiler from hoisting
+        // these addresses out of the expert loop (they would stay live
+        // across the K loop and push its registers into scratch)
+        int ln = lane;
+        asm volatile("" : "+v"(ln));
+#pragma unroll
+    for (int a = 0; a < TJ; ++a) {
+        const int64_t j = jw + a * 16 + 4 * (ln >> 4);
+#pragma unroll
+        for (int b = 0; b < TI; ++b) {
+            const int64_t i = i0 + wi * WI + b * 16 + (ln & 15);
+            if (i >= ihi) continue;
+            const v4f r = acc[a][b];
+            if (g.out_f32) {
+                float* o = reinterpret_cast<float*>(Ob) + i * g.ldo + j;
+                if (j + 3 < g.Nn) {
+                    float4 v = make_float4(r[0], r[1], r[2], r[3]);
+                    if (g.beta) {
+                        const float4 old = *reinterpret_cast<const float4*>(o);
+                        v.x += old.x; v.y += old.y; v.z += old.z; v.w += old.w;
+                    }
+                    *reinterpret_cast<float4*>(o) = v;
+                } else {
+#pragma unroll
+                    for (int q = 0; q < 4; ++q)
+                        if (j + q < g.Nn) o[q] = g.beta ? o[q] + r[q] : r[q];
+                }
+            } else {
+                uint16_t* o = reinterpret_cast<uint16_t*>(Ob) + i * g.ldo + j;
+                if (j + 3 < g.Nn) {
+                    uint2 v;
+                    v.x = f32_to_bf16(r[0]) | (f32_to_bf16(r[1]) << 16);
+                    v.y = f32_to_bf16(r[2]) | (f32_to_bf16(r[3]) << 16);
+                    *reinterpret_cast<uint2*>(o) = v;
+                } else {
+#pragma unroll
+                    for (int q = 0; q < 4; ++q)
+                        if (j + q < g.Nn) o[q] = (uint16_t)f32_to_bf16(r[q]);
+                }
+            }
+        }
+    }
+    };
+
+    // Staged epilogue of output rows [r0, r0 + rh) (whole waves' rows) in
+    // bf16: the waves holding them write their accumulators to LDS at stile
+    // (rows stride BJ*2 bytes; 8-byte column chunks XOR-swizzled by
+    // 2*(row % 16), so that 16 rows' writes hit distinct banks and 16-byte
+    // pairs stay whole), then every thread sends whole rows out as
+    // contiguous 16-byte stores.  Ends with a barrier: stile is free again.
+    constexpr int CPR = BJ / 4;                                      // 8-byte chunks per tile row
+    constexpr int PPR = CPR / 2;                                     // 16-byte pairs per tile row
+    auto store_staged = [&](char* Ob, uint8_t* stile, int r0, int rh) {
+        int ln = lane;
+        asm volatile("" : "+v"(ln));
+        if (wi * WI >= r0 && wi * WI < r0 + rh) {
+#pragma unroll
+            for (int a = 0; a < TJ; ++a) {
+                const int jl = wj * WJ + a * 16 + 4 * (ln >> 4);
+#pragma unroll
+                for (int b = 0; b < TI; ++b) {
+                    const int il = wi * WI + b * 16 + (ln & 15) - r0;
+                    const v4f r = acc[a][b];
+                    uint2 v;
+                    v.x = f32_to_bf16(r[0]) | (f32_to_bf16(r[1]) << 16);
+                    v.y = f32_to_bf16(r[2]) | (f32_to_bf16(r[3]) << 16);
+                    const int ch = (jl >> 2) ^ ((2 * (il & 15)) & (CPR - 1) & ~1);
+                    *reinterpret_cast<uint2*>(stile + (il * CPR + ch) * 8) = v;
+                }
+            }
+        }
+        __syncthreads();
+        const bool full_cols = jhi - j0 == BJ && (g.ldo % 8) == 0;
+        for (int q = tid; q < rh * PPR; q += NT) {
+            const int il = q / PPR, pp = q % PPR;
+            const int64_t i = i0 + r0 + il;
+            if (i < ihi) {
+                const int ch = (2 * pp) ^ ((2 * (il & 15)) & (CPR - 1) & ~1);
+                const uint4 v = *reinterpret_cast<const uint4*>(stile + (il * CPR + ch) * 8);
+                const int64_t j = j0 + 8 * pp;
+                uint16_t* o = reinterpret_cast<uint16_t*>(Ob) + i * g.ldo + j;
+                if (full_cols) {
+                    *reinterpret_cast<uint4*>(o) = v;
+                } else {
+                    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+                    for (int e = 0; e < 8; ++e)
+                        if (j + e < g.Nn) o[e] = (uint16_t)(w[e >> 1] >> (16 * (e & 1)));
+                }
+            }
+        }
+        __syncthreads();
+    };
+    // rows of one staged piece that fit in a single stage (whole waves)
+    constexpr int RH = (STAGE / (BJ * 2)) / WI * WI;
+    constexpr bool STAGED_PIECES = RH >= WI && BI % (RH > 0 ? RH : 1) == 0;
+
     const int sh = 8 * (lane >> 4);
     int buf = 0;                                                     // stage of K block kb
     int nbuf = NS - 1;                                               // stage that receives block kb + NS - 1
-    for (int64_t kb = 0; kb < KB; ++kb) {
+    int64_t ecur = e_first;                                          // expert whose K blocks run (GROUP_K)
+    int64_t kend = g.group_mode == GROUP_K ? uniform64(ekb[0]) : KB;
+    int64_t kb = 0;
+    for (;;) {
+    for (; kb < kend; ++kb) {
         const int64_t kn = kb + NS - 1 < KB ? kb + NS - 1 : KB - 1;  // past the end the last block is
                                                                      // reloaded into an idle stage:
                                                                      // no branch in the loop
@@ -381,6 +516,23 @@ __global__ __launch_bounds__(64 * NW, 1) void k_gemm(GemmArgs g) {
         buf = buf + 1 == NS ? 0 : buf + 1;
         nbuf = nbuf + 1 == NS ? 0 : nbuf + 1;
     }
+    if (g.group_mode != GROUP_K || ecur + 1 >= e_end) break;
+    // expert boundary: the next expert's first K block has landed in stage
+    // buf and nothing is in flight, so stage nbuf is free: this expert's tile
+    // leaves through it in pieces of RH rows (or by direct stores), then the
+    // next expert starts
+    if (STAGED_PIECES && !g.out_f32) {
+        for (int r0 = 0; r0 < BI; r0 += RH) store_staged(O + ecur * g.o_estride * o_elem, smem + nbuf * STAGE, r0, RH);
+    } else {
+        store_direct(O + ecur * g.o_estride * o_elem);
+    }
+#pragma unroll
+    for (int a = 0; a < TJ; ++a)
+#pragma unroll
+        for (int b = 0; b < TI; ++b) acc[a][b] = v4f{0.f, 0.f, 0.f, 0.f};
+    ++ecur;
+    kend += uniform64(ekb[ecur - e_first]);
+    }
 #undef FP8B_DMA_PART
 #undef FP8B_DMA_SCALE
     // the tail's repeated DMAs target idle stages; let them land before the
@@ -389,96 +541,18 @@ __global__ __launch_bounds__(64 * NW, 1) void k_gemm(GemmArgs g) {
     __syncthreads();
 
     // ---------------------------------------------------- epilogue
-    const int64_t jw = j0 + wj * WJ;
+    if (g.group_mode == GROUP_K) O += ecur * g.o_estride * o_elem;
     if (STAGED_OUT && !g.out_f32) {
-        // bf16 tile through LDS: lanes hold 4 consecutive columns of one row,
-        // rows stride BJ*2 bytes; 8-byte column chunks are XOR-swizzled by
-        // 2*(row % 16) so that 16 rows' writes hit distinct banks and 16-byte
-        // pairs stay whole.  Rows then leave as contiguous 16-byte stores.
-        uint8_t* stile = smem;
-        constexpr int CPR = BJ / 4;                                  // 8-byte chunks per tile row
-#pragma unroll
-        for (int a = 0; a < TJ; ++a) {
-            const int jl = wj * WJ + a * 16 + 4 * (lane >> 4);
-#pragma unroll
-            for (int b = 0; b < TI; ++b) {
-                const int il = wi * WI + b * 16 + (lane & 15);
-                const v4f r = acc[a][b];
-                uint2 v;
-                v.x = f32_to_bf16(r[0]) | (f32_to_bf16(r[1]) << 16);
-                v.y = f32_to_bf16(r[2]) | (f32_to_bf16(r[3]) << 16);
-                const int ch = (jl >> 2) ^ ((2 * (il & 15)) & (CPR - 1) & ~1);
-                *reinterpret_cast<uint2*>(stile + (il * CPR + ch) * 8) = v;
-            }
-        }
-        __syncthreads();
-        constexpr int PPR = CPR / 2;                                 // 16-byte pairs per tile row
-        const bool full_cols = jhi - j0 == BJ && (g.ldo % 8) == 0;
-#pragma unroll
-        for (int it = 0; it < (BI * PPR + NT - 1) / NT; ++it) {
-            const int q = it * NT + tid;
-            if (q < BI * PPR) {
-                const int il = q / PPR, pp = q % PPR;
-                const int64_t i = i0 + il;
-                if (i < ihi) {
-                    const int ch = (2 * pp) ^ ((2 * (il & 15)) & (CPR - 1) & ~1);
-                    const uint4 v = *reinterpret_cast<const uint4*>(stile + (il * CPR + ch) * 8);
-                    const int64_t j = j0 + 8 * pp;
-                    uint16_t* o = reinterpret_cast<uint16_t*>(O) + i * g.ldo + j;
-                    if (full_cols) {
-                        *reinterpret_cast<uint4*>(o) = v;
-                    } else {
-                        const uint32_t w[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-                        for (int e = 0; e < 8; ++e)
-                            if (j + e < g.Nn) o[e] = (uint16_t)(w[e >> 1] >> (16 * (e & 1)));
-                    }
-                }
-            }
-        }
+        store_staged(O, smem, 0, BI);                              // every stage is free now
         return;
     }
-#pragma unroll
-    for (int a = 0; a < TJ; ++a) {
-        const int64_t j = jw + a * 16 + 4 * (lane >> 4);
-#pragma unroll
-        for (int b = 0; b < TI; ++b) {
-            const int64_t i = i0 + wi * WI + b * 16 + (lane & 15);
-            if (i >= ihi) continue;
-            const v4f r = acc[a][b];
-            if (g.out_f32) {
-                float* o = reinterpret_cast<float*>(O) + i * g.ldo + j;
-                if (j + 3 < g.Nn) {
-                    float4 v = make_float4(r[0], r[1], r[2], r[3]);
-                    if (g.beta) {
-                        const float4 old = *reinterpret_cast<const float4*>(o);
-                        v.x += old.x; v.y += old.y; v.z += old.z; v.w += old.w;
-                    }
-                    *reinterpret_cast<float4*>(o) = v;
-                } else {
-#pragma unroll
-                    for (int q = 0; q < 4; ++q)
-                        if (j + q < g.Nn) o[q] = g.beta ? o[q] + r[q] : r[q];
-                }
-            } else {
-                uint16_t* o = reinterpret_cast<uint16_t*>(O) + i * g.ldo + j;
-                if (j + 3 < g.Nn) {
-                    uint2 v;
-                    v.x = f32_to_bf16(r[0]) | (f32_to_bf16(r[1]) << 16);
-                    v.y = f32_to_bf16(r[2]) | (f32_to_bf16(r[3]) << 16);
-                    *reinterpret_cast<uint2*>(o) = v;
-                } else {
-#pragma unroll
-                    for (int q = 0; q < 4; ++q)
-                        if (j + q < g.Nn) o[q] = (uint16_t)f32_to_bf16(r[q]);
-                }
-            }
-        }
-    }
+    store_direct(O);
 }
 
 template <int BI, int BJ, int TI, int TJ, int NW, int SM, int NS>
-static hipError_t launch_cfg(const GemmArgs& a, hipStream_t st) {
+static hipError_t launch_cfg(const GemmArgs& args, hipStream_t st) {
+    GemmArgs a = args;
+    a.epb = 1;
     const int64_t nbj = (a.Nn + BJ - 1) / BJ;
     const int64_t nbi = (a.M + BI - 1) / BI;
     dim3 grid;
@@ -489,7 +563,16 @@ static hipError_t launch_cfg(const GemmArgs& a, hipStream_t st) {
         grid = dim3((unsigned)nbj, (unsigned)rt, 1);
     } else {
         const int64_t tiles = nbi * nbj;
-        const int64_t z = a.group_mode == GROUP_K ? a.E : 1;
+        int64_t z = 1;
+        if (a.group_mode == GROUP_K) {
+            // several experts per block, sized so that about three blocks per
+            // compute unit remain (each expert holds only a few K blocks)
+            int64_t epb = tiles * a.E / (3 * (int64_t)device_cu_count());
+            epb = epb < 1 ? 1 : (epb > MAX_EPB ? MAX_EPB : epb);
+            if (NS != 2) epb = 1;     // the boundary store needs an idle stage and no DMA in flight
+            a.epb = epb;
+            z = (a.E + epb - 1) / epb;
+        }
         if (tiles == 0 || z == 0) return hipSuccess;
         if (tiles > 0x7FFFFFFF || z > 65535) return hipErrorInvalidValue;
         grid = dim3((unsigned)tiles, (unsigned)z, 1);

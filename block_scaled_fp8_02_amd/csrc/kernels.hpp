@@ -24,6 +24,9 @@ hipError_t launch_quant_cols(const void* x, bool in_bf16, int64_t rows, int64_t 
                              uint8_t* qT, int64_t ldqT, float* sT, int64_t ldsT,
                              uint8_t* q, int64_t ldq, float* s, int64_t lds, hipStream_t st);
 
+// Compute units of the current device (cached per device).
+int device_cu_count();
+
 // Elementwise codec access.
 hipError_t launch_encode(const float* x, const float* s, int64_t n, uint8_t* out, hipStream_t st);
 
@@ -53,6 +56,7 @@ struct GemmArgs {
     int group_mode;
     const int32_t* offsets; int64_t E;
     int64_t q_estride, sq_estride, o_estride;
+    int64_t epb;          // GROUP_K: experts per block (set by the launcher)
 };
 
 hipError_t launch_gemm(const GemmArgs& a, hipStream_t st);

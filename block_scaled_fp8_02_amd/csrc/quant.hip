@@ -445,7 +445,7 @@ hipError_t launch_quant_rows(const void* x, bool in_bf16, int64_t rows, int64_t 
 
 // Blocks of the persistent tile quantizer: two per compute unit (its
 // register and LDS budget allows two), never more than there are tiles.
-static int64_t tile_grid(int64_t tiles) {
+int device_cu_count() {
     static int cu_count[64];
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess || dev < 0) dev = 0;
@@ -454,7 +454,11 @@ static int64_t tile_grid(int64_t tiles) {
         if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0) cus = 256;
         if (dev < 64) cu_count[dev] = cus;
     }
-    const int64_t g = 2 * (int64_t)cus;
+    return cus;
+}
+
+static int64_t tile_grid(int64_t tiles) {
+    const int64_t g = 2 * (int64_t)device_cu_count();
     return tiles < g ? tiles : g;
 }
 
