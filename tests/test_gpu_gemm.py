@@ -87,7 +87,7 @@ def abs_products(X, W, dY):
 
 
 def check_f32(got, want, mag, what):
-    """fp32 output: the benchmark spec row-norm metric, and every element within
+    """fp32 output: the row-norm error metric, and every element within
     the fp32 accumulation bound of the oracle."""
     err = oracle.rel_row_error(got, want)
     ratio = float(np.max(np.abs(got - want) / np.maximum(mag, 1e-300)))
