@@ -42,12 +42,23 @@ namespace fp8blk {
 
 // MFMA operand fragment of one row: lane group g = lane/16 takes the 16-byte
 // chunks g and g+4 of the row's 128 K bytes, which is the K order of the
-// 16x16x128 instruction (so the 32-wide MX scale blocks line up too).
-__device__ __forceinline__ v8i lds_frag(const uint8_t* base, int row, int lane) {
-    const int g = lane >> 4;
-    const int sw = row & 7;
-    const uint4 x0 = *reinterpret_cast<const uint4*>(base + row * 128 + ((g ^ sw) << 4));
-    const uint4 x1 = *reinterpret_cast<const uint4*>(base + row * 128 + (((g + 4) ^ sw) << 4));
+// 16x16x128 instruction (so the 32-wide MX scale blocks line up too).  Chunk
+// c of tile row r sits at byte r*128 + ((c ^ (r & 7)) << 4) of a stage.
+// frag_off gives a lane's two byte offsets for its fragment row; rows 16
+// apart share them up to r*128, so sub-tiles differ by constant offsets.
+struct FragOff {
+    uint32_t o0, o1;
+};
+
+__device__ __forceinline__ FragOff frag_off(int row, int lane) {
+    const int g = lane >> 4, sw = row & 7;
+    return FragOff{(uint32_t)(row * 128 + ((g ^ sw) << 4)), (uint32_t)(row * 128 + (((g + 4) ^ sw) << 4))};
+}
+
+// Fragment at `delta` bytes (a multiple of 16 rows) past the offsets' row.
+__device__ __forceinline__ v8i lds_frag(const uint8_t* stage, FragOff f, int delta) {
+    const uint4 x0 = *reinterpret_cast<const uint4*>(stage + f.o0 + delta);
+    const uint4 x1 = *reinterpret_cast<const uint4*>(stage + f.o1 + delta);
     v8i r;
     r[0] = (int)x0.x; r[1] = (int)x0.y; r[2] = (int)x0.z; r[3] = (int)x0.w;
     r[4] = (int)x1.x; r[5] = (int)x1.y; r[6] = (int)x1.z; r[7] = (int)x1.w;
@@ -403,6 +414,8 @@ __global__ __launch_bounds__(64 * NW, 1) void k_gemm(GemmArgs g) {
     constexpr int RH = (STAGE / (BJ * 2)) / WI * WI;
     constexpr bool STAGED_PIECES = RH >= WI && BI % (RH > 0 ? RH : 1) == 0;
 
+    const FragOff pfo = frag_off(prow_l, lane);                      // this lane's P fragment row
+    const FragOff qfo = frag_off(qrow_l + (lane & 15), lane);        // and Q fragment row
     const int sh = 8 * (lane >> 4);
     int buf = 0;                                                     // stage of K block kb
     int nbuf = NS - 1;                                               // stage that receives block kb + NS - 1
@@ -426,7 +439,7 @@ __global__ __launch_bounds__(64 * NW, 1) void k_gemm(GemmArgs g) {
         int eb[TI];
 #pragma unroll
         for (int t = 0; t < TI; ++t) {
-            bf[t] = lds_frag(base, prow_l + t * 16, lane);
+            bf[t] = lds_frag(base, pfo, t * 16 * 128);
             const uint32_t w = sc[prow_l + t * 16];
             sp[t] = __uint_as_float(w);
             eb[t] = (int)((w >> sh) & 0xFFu);
@@ -436,7 +449,7 @@ __global__ __launch_bounds__(64 * NW, 1) void k_gemm(GemmArgs g) {
 #pragma unroll
             for (int t = 0; t < TI; ++t) sp[t] *= sq;                 // combined scale per P sub-tile
         }
-        v8i af = lds_frag(base, qrow_l + (lane & 15), lane);
+        v8i af = lds_frag(base, qfo, 0);
         uint4 sqa = *reinterpret_cast<const uint4*>(&sc[qrow_l + 4 * (lane >> 4)]);
         uint32_t eaw = sc[qrow_l + (lane & 15)];
         if constexpr (SM == SCALE_MX) {
@@ -449,7 +462,7 @@ __global__ __launch_bounds__(64 * NW, 1) void k_gemm(GemmArgs g) {
                 uint32_t eaw_n = eaw;
                 if (a + 1 < TJ) {
                     const int qr = qrow_l + (a + 1) * 16;
-                    af_n = lds_frag(base, qr + (lane & 15), lane);
+                    af_n = lds_frag(base, qfo, (a + 1) * 16 * 128);
                     eaw_n = sc[qr + (lane & 15)];
                 }
 #pragma unroll
@@ -476,7 +489,7 @@ __global__ __launch_bounds__(64 * NW, 1) void k_gemm(GemmArgs g) {
                 uint4 sqa_n = sqa;
                 if (a + 1 < TJ) {
                     const int qr = qrow_l + (a + 1) * 16;
-                    af_n = lds_frag(base, qr + (lane & 15), lane);
+                    af_n = lds_frag(base, qfo, (a + 1) * 16 * 128);
                     if constexpr (SM == SCALE_Q_ROW) sqa_n = *reinterpret_cast<const uint4*>(&sc[qr + 4 * (lane >> 4)]);
                 }
                 v4f cur[TI];
