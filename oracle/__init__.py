@@ -46,6 +46,9 @@ def _load():
     lib.ora_quant_1x128.argtypes = [_p, _i64, _i64, _i64, _p, _i64, _p, _i64]
     lib.ora_quant_128x128.argtypes = [_p, _i64, _i64, _i64, _p, _i64, _p, _i64, _p, _i64]
     lib.ora_quant_colwise.argtypes = [_p, _i64, _i64, _i64, _p, _i64, _p, _i64, _p, _i64]
+    lib.ora_quant_1x128_p2.argtypes = lib.ora_quant_1x128.argtypes
+    lib.ora_quant_128x128_p2.argtypes = lib.ora_quant_128x128.argtypes
+    lib.ora_quant_colwise_p2.argtypes = lib.ora_quant_colwise.argtypes
     lib.ora_mx_exponent.restype = ctypes.c_int
     lib.ora_mx_exponent.argtypes = [ctypes.c_float]
     lib.ora_mx_quant_rows.argtypes = [_p, _i64, _i64, _i64, _p, _i64, _p, _i64]
@@ -99,19 +102,20 @@ def e4m3_encode_f64(v: float) -> int:
 
 
 # ---------------------------------------------------------- quantizers
-def quant_1x128(x: np.ndarray):
+def quant_1x128(x: np.ndarray, pow2: bool = False):
     """1x128 groups along the last axis.  Returns (q [rows, rup(cols,128)] u8,
-    s [rows, ceil(cols/128)] f32)."""
+    s [rows, ceil(cols/128)] f32); pow2 selects power-of-two scales."""
     lib = _load()
     x = as_f32(x)
     rows, cols = x.shape
     q = np.full((rows, _rup(cols, 128)), 0xAA, dtype=np.uint8)
     s = np.empty((rows, _cdiv(cols, 128)), dtype=np.float32)
-    lib.ora_quant_1x128(_ptr(x), rows, cols, cols, _ptr(q), q.shape[1], _ptr(s), s.shape[1])
+    fn = lib.ora_quant_1x128_p2 if pow2 else lib.ora_quant_1x128
+    fn(_ptr(x), rows, cols, cols, _ptr(q), q.shape[1], _ptr(s), s.shape[1])
     return q, s
 
 
-def quant_128x128(w: np.ndarray, with_transpose: bool = True):
+def quant_128x128(w: np.ndarray, with_transpose: bool = True, pow2: bool = False):
     """128x128 blocks of W [D, C].  Returns (q [D, rup(C)], s [ceil(D/128),
     ceil(C/128)], qT [C, rup(D)] or None)."""
     lib = _load()
@@ -120,8 +124,9 @@ def quant_128x128(w: np.ndarray, with_transpose: bool = True):
     q = np.full((D, _rup(C, 128)), 0xAA, dtype=np.uint8)
     s = np.empty((_cdiv(D, 128), _cdiv(C, 128)), dtype=np.float32)
     qT = np.full((C, _rup(D, 128)), 0xAA, dtype=np.uint8) if with_transpose else None
-    lib.ora_quant_128x128(_ptr(w), D, C, C, _ptr(q), q.shape[1], _ptr(s), s.shape[1],
-                          _ptr(qT) if qT is not None else None, qT.shape[1] if qT is not None else 0)
+    fn = lib.ora_quant_128x128_p2 if pow2 else lib.ora_quant_128x128
+    fn(_ptr(w), D, C, C, _ptr(q), q.shape[1], _ptr(s), s.shape[1],
+       _ptr(qT) if qT is not None else None, qT.shape[1] if qT is not None else 0)
     return q, s, qT
 
 
@@ -132,9 +137,10 @@ def padded_offsets(offsets: np.ndarray) -> np.ndarray:
     return np.concatenate([[0], np.cumsum((n + 127) // 128 * 128)]).astype(np.int64)
 
 
-def quant_colwise(x: np.ndarray, offsets: np.ndarray | None = None):
+def quant_colwise(x: np.ndarray, offsets: np.ndarray | None = None, pow2: bool = False):
     """1x128 groups along the token (row) axis, written transposed.  Returns
-    (qT [cols, P] u8, sT [cols, P/128] f32) with P the padded token count."""
+    (qT [cols, P] u8, sT [cols, P/128] f32) with P the padded token count;
+    pow2 selects power-of-two scales."""
     lib = _load()
     x = as_f32(x)
     rows, cols = x.shape
@@ -149,9 +155,18 @@ def quant_colwise(x: np.ndarray, offsets: np.ndarray | None = None):
     qT = np.full((cols, max(P, 0)), 0xAA, dtype=np.uint8)
     sT = np.full((cols, max(P // 128, 0)), np.nan, dtype=np.float32)
     if P > 0:
-        lib.ora_quant_colwise(_ptr(x), rows, cols, cols, offs_p, E,
-                              _ptr(qT), qT.shape[1], _ptr(sT), sT.shape[1])
+        fn = lib.ora_quant_colwise_p2 if pow2 else lib.ora_quant_colwise
+        fn(_ptr(x), rows, cols, cols, offs_p, E, _ptr(qT), qT.shape[1], _ptr(sT), sT.shape[1])
     return qT, sT
+
+
+def e8m0_of_pow2(s: np.ndarray) -> np.ndarray:
+    """E8M0 bytes (k + 127) of power-of-two scales 2^k, k in [-127, 127]."""
+    s = np.asarray(s, dtype=np.float32)
+    m, e = np.frexp(s.astype(np.float64))
+    if not np.all(m == 0.5):
+        raise ValueError("not a power of two")
+    return (e - 1 + 127).astype(np.uint8)
 
 
 def mx_exponent(amax: float) -> int:

@@ -124,9 +124,40 @@ ORACLE_API void ora_e4m3_encode_array(const float* v, int64_t n, uint8_t* out)
 /* the signed zero of each input.                                        */
 /* ------------------------------------------------------------------ */
 
+/* The power-of-two exponent of a block with maximum magnitude amax: the
+ * smallest integer k with amax <= 448 * 2^k (so the block maximum never
+ * clips), clamped to [-127, 127]; an all-zero block takes k = -127.  Used
+ * for the E8M0 scales of MXFP8 and for the power-of-two FP32 scales. */
+static int mx_exponent(float amax)
+{
+    if (amax == 0.0f) return -127;
+    int lo = -127, hi = 127;                     /* predicate monotone in k */
+    if ((double)amax > ldexp(448.0, hi)) return 127;
+    while (lo < hi) {
+        int mid = lo + (hi - lo) / 2;
+        if ((double)amax <= ldexp(448.0, mid)) hi = mid; else lo = mid + 1;
+    }
+    return lo;
+}
+
 static float group_scale(float amax)
 {
     return amax / 448.0f;
+}
+
+/* Power-of-two FP32 block scale (the SkyRL section "FP8 quantization with
+ * FP32 and power-of-two block scales": scales constrained to powers of two,
+ * an exponent-only representation).  The pages do not say how the exponent
+ * is chosen; reading used here, as for the MXFP8 scales: rounded up so the
+ * block maximum does not clip, S = 2^k with k = mx_exponent(amax). */
+static float group_scale_p2(float amax)
+{
+    return ldexpf(1.0f, mx_exponent(amax));
+}
+
+static float scale_rule(float amax, int pow2)
+{
+    return pow2 ? group_scale_p2(amax) : group_scale(amax);
 }
 
 static uint8_t quant_elem(float x, float S)
@@ -139,8 +170,8 @@ static uint8_t quant_elem(float x, float S)
 /* 1x128 per-group quantization along the contiguous axis (activations X
  * for FProp, gradients dY for DGrad).  q: rows x ldq bytes, the columns
  * [cols, round_up(cols,128)) are written 0x00.  s: rows x ceil(cols/128). */
-ORACLE_API void ora_quant_1x128(const float* x, int64_t rows, int64_t cols, int64_t ldx,
-                                uint8_t* q, int64_t ldq, float* s, int64_t lds)
+static void quant_1x128(const float* x, int64_t rows, int64_t cols, int64_t ldx,
+                        uint8_t* q, int64_t ldq, float* s, int64_t lds, int pow2)
 {
     e4m3_build();
     int64_t groups = (cols + 127) / 128;
@@ -154,7 +185,7 @@ ORACLE_API void ora_quant_1x128(const float* x, int64_t rows, int64_t cols, int6
                 float a = fabsf(x[r * ldx + k]);
                 if (a > amax) amax = a;
             }
-            float S = group_scale(amax);
+            float S = scale_rule(amax, pow2);
             s[r * lds + g] = S;
             for (int64_t k = k0; k < k1; ++k) q[r * ldq + k] = quant_elem(x[r * ldx + k], S);
             for (int64_t k = k1; k < k0 + 128; ++k) q[r * ldq + k] = 0x00;
@@ -166,9 +197,9 @@ ORACLE_API void ora_quant_1x128(const float* x, int64_t rows, int64_t cols, int6
  * input channels).  s: ceil(D/128) x ceil(C/128).  qT (optional) holds the
  * same codes transposed, C x ldqT; its columns [D, round_up(D,128)) are
  * written 0x00, as are q's columns [C, round_up(C,128)). */
-ORACLE_API void ora_quant_128x128(const float* w, int64_t D, int64_t C, int64_t ldw,
-                                  uint8_t* q, int64_t ldq, float* s, int64_t lds,
-                                  uint8_t* qT, int64_t ldqT)
+static void quant_128x128(const float* w, int64_t D, int64_t C, int64_t ldw,
+                          uint8_t* q, int64_t ldq, float* s, int64_t lds,
+                          uint8_t* qT, int64_t ldqT, int pow2)
 {
     e4m3_build();
     int64_t bd = (D + 127) / 128, bc = (C + 127) / 128;
@@ -183,7 +214,7 @@ ORACLE_API void ora_quant_128x128(const float* w, int64_t D, int64_t C, int64_t 
                 float a = fabsf(w[d * ldw + c]);
                 if (a > amax) amax = a;
             }
-        float S = group_scale(amax);
+        float S = scale_rule(amax, pow2);
         s[i * lds + j] = S;
         for (int64_t d = d0; d < d1; ++d)
             for (int64_t c = c0; c < c1; ++c) {
@@ -209,9 +240,9 @@ ORACLE_API void ora_quant_128x128(const float* w, int64_t D, int64_t C, int64_t 
  * and its scales occupy sT columns [P_e/128, P_e/128 + ceil(n_e/128)).
  * Without offsets there is one segment covering all rows.  Positions past
  * a segment's last row inside its last group are written 0x00. */
-ORACLE_API void ora_quant_colwise(const float* x, int64_t rows, int64_t cols, int64_t ldx,
-                                  const int32_t* offsets, int64_t E,
-                                  uint8_t* qT, int64_t ldqT, float* sT, int64_t ldsT)
+static void quant_colwise(const float* x, int64_t rows, int64_t cols, int64_t ldx,
+                          const int32_t* offsets, int64_t E,
+                          uint8_t* qT, int64_t ldqT, float* sT, int64_t ldsT, int pow2)
 {
     e4m3_build();
     int64_t nseg = offsets ? E : 1;
@@ -231,7 +262,7 @@ ORACLE_API void ora_quant_colwise(const float* x, int64_t rows, int64_t cols, in
                     float v = fabsf(x[r * ldx + c]);
                     if (v > amax) amax = v;
                 }
-                float S = group_scale(amax);
+                float S = scale_rule(amax, pow2);
                 sT[c * ldsT + pos / 128 + g] = S;
                 for (int64_t r = r0; r < r1; ++r)
                     qT[c * ldqT + pos + (r - a)] = quant_elem(x[r * ldx + c], S);
@@ -243,6 +274,36 @@ ORACLE_API void ora_quant_colwise(const float* x, int64_t rows, int64_t cols, in
     }
 }
 
+/* Exported forms: FP32 scales (the pages' default recipe) and the
+ * power-of-two FP32 scales (_p2), same groupings and layouts. */
+ORACLE_API void ora_quant_1x128(const float* x, int64_t rows, int64_t cols, int64_t ldx,
+                                uint8_t* q, int64_t ldq, float* s, int64_t lds)
+{ quant_1x128(x, rows, cols, ldx, q, ldq, s, lds, 0); }
+
+ORACLE_API void ora_quant_1x128_p2(const float* x, int64_t rows, int64_t cols, int64_t ldx,
+                                   uint8_t* q, int64_t ldq, float* s, int64_t lds)
+{ quant_1x128(x, rows, cols, ldx, q, ldq, s, lds, 1); }
+
+ORACLE_API void ora_quant_128x128(const float* w, int64_t D, int64_t C, int64_t ldw,
+                                  uint8_t* q, int64_t ldq, float* s, int64_t lds,
+                                  uint8_t* qT, int64_t ldqT)
+{ quant_128x128(w, D, C, ldw, q, ldq, s, lds, qT, ldqT, 0); }
+
+ORACLE_API void ora_quant_128x128_p2(const float* w, int64_t D, int64_t C, int64_t ldw,
+                                     uint8_t* q, int64_t ldq, float* s, int64_t lds,
+                                     uint8_t* qT, int64_t ldqT)
+{ quant_128x128(w, D, C, ldw, q, ldq, s, lds, qT, ldqT, 1); }
+
+ORACLE_API void ora_quant_colwise(const float* x, int64_t rows, int64_t cols, int64_t ldx,
+                                  const int32_t* offsets, int64_t E,
+                                  uint8_t* qT, int64_t ldqT, float* sT, int64_t ldsT)
+{ quant_colwise(x, rows, cols, ldx, offsets, E, qT, ldqT, sT, ldsT, 0); }
+
+ORACLE_API void ora_quant_colwise_p2(const float* x, int64_t rows, int64_t cols, int64_t ldx,
+                                     const int32_t* offsets, int64_t E,
+                                     uint8_t* qT, int64_t ldqT, float* sT, int64_t ldsT)
+{ quant_colwise(x, rows, cols, ldx, offsets, E, qT, ldqT, sT, ldsT, 1); }
+
 /* ------------------------------------------------------------------ */
 /* MXFP8: 1x32 blocks with a shared power-of-two scale 2^k stored as the  */
 /* E8M0 byte k + 127.  k is the smallest integer with amax <= 448 * 2^k,  */
@@ -250,18 +311,6 @@ ORACLE_API void ora_quant_colwise(const float* x, int64_t rows, int64_t cols, in
 /* block takes k = -127.  Codes are E4M3(x * 2^-k): the product is exact */
 /* in double and the E4M3 rounding is the only rounding.                 */
 /* ------------------------------------------------------------------ */
-
-static int mx_exponent(float amax)
-{
-    if (amax == 0.0f) return -127;
-    int lo = -127, hi = 127;                     /* predicate monotone in k */
-    if ((double)amax > ldexp(448.0, hi)) return 127;
-    while (lo < hi) {
-        int mid = lo + (hi - lo) / 2;
-        if ((double)amax <= ldexp(448.0, mid)) hi = mid; else lo = mid + 1;
-    }
-    return lo;
-}
 
 ORACLE_API int ora_mx_exponent(float amax) { return mx_exponent(amax); }
 
