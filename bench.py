@@ -319,6 +319,10 @@ def main():
             tw[name] = {"error": str(ex)[:120]}
     ceil["fp8_tensorwise_hipblaslt"] = tw
 
+    pow2 = None
+    if not args.no_other:
+        pow2 = pow2_layer(torch, fb, copies, flops_gemm)
+
     other = None
     if not args.no_other:
         del copies, bufs, b
@@ -340,6 +344,7 @@ def main():
                    "N": N, "C": C, "D": D, "seed": args.seed, "inputs_resident_in_hbm": True},
         "kernels": kernels, "roofline": roofline, "bf16_baseline": bf, "cpu_baseline": cpu,
         "measured_ceilings": ceil,
+        "pow2_scales_layer": pow2,
         "other_workloads": other,
     }
     print(json.dumps(out), flush=True)
@@ -374,6 +379,50 @@ def report(t, alg_bytes, flops=None):
         e["tflops"] = round(flops / t / 1e12, 1)
         e["frac_fp8_peak"] = round(flops / t / 1e12 / PEAK_FP8_TFLOPS, 4)
     return e
+
+
+def pow2_layer(torch, fb, copies, flops_gemm):
+    """The same training layer with power-of-two block scales: the quantizers
+    also emit E8M0 bytes, and the three GEMMs run on the scaled MFMA (MXFP8
+    kernels), with no per-block promotion.  Warm operands like the main
+    step; each kernel timed alone over 10 launches."""
+    Xd, Wd, Gd = copies[0]
+    N, C = Xd.shape
+    D = Wd.shape[0]
+    xqT, xsT, xeT, xq, xs, xe = fb.fp8_quantize_transposed_pow2(Xd, rowwise=True)
+    gqT, gsT, geT, gq, gs, ge = fb.fp8_quantize_transposed_pow2(Gd, rowwise=True)
+    wq, ws, wqT, we, weT = fb.fp8_quantize_weight_128x128_pow2(Wd)
+    y = torch.empty((N, D), dtype=torch.bfloat16, device=Xd.device)
+    dx = torch.empty((N, C), dtype=torch.bfloat16, device=Xd.device)
+    dw = torch.empty((D, C), dtype=torch.bfloat16, device=Xd.device)
+    runs = {
+        "quant_weight": lambda: fb.fp8_quantize_weight_128x128_pow2(Wd),
+        "quant_dual_X": lambda: fb.fp8_quantize_transposed_pow2(Xd, rowwise=True),
+        "quant_dual_dY": lambda: fb.fp8_quantize_transposed_pow2(Gd, rowwise=True),
+        "fprop": lambda: fb.fp8_mx_gemm_fprop(xq, xe, wq, we, N, D, C, y=y),
+        "dgrad": lambda: fb.fp8_mx_gemm_dgrad(gq, ge, wqT, weT, N, D, C, dx=dx),
+        "wgrad": lambda: fb.fp8_mx_gemm_wgrad(gqT, geT, xqT, xeT, N, D, C, dw=dw),
+    }
+    out = {}
+    for name, fn in runs.items():
+        for _ in range(2):
+            fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(10):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        t = e0.elapsed_time(e1) * 1e-3 / 10
+        ent = {"us": round(t * 1e6, 2)}
+        if name in ("fprop", "dgrad", "wgrad"):
+            ent["tflops"] = round(flops_gemm / t / 1e12, 1)
+            ent["frac_fp8_peak"] = round(flops_gemm / t / 1e12 / PEAK_FP8_TFLOPS, 4)
+        out[name] = ent
+    gemm_us = sum(out[n]["us"] for n in ("fprop", "dgrad", "wgrad"))
+    out["gemm_tflops"] = round(3 * flops_gemm / (gemm_us * 1e-6) / 1e12, 1)
+    return out
 
 
 def other_workloads(torch, fb, wl, dev, seed):

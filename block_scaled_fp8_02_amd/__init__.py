@@ -44,6 +44,11 @@ _SIGS = {
     "fp8_quantize_transposed": [_p, _i32, _i64, _i64, _i64, _p, _i64, _p, _i64, _p, _i64, _p, _i64, _p],
     "fp8_quantize_transposed_grouped": [_p, _i32, _i64, _i64, _i64, _p, _i64, _p, _i64, _p, _i64,
                                         _p, _i64, _p, _i64, _p],
+    "fp8_quantize_act_1x128_pow2": [_p, _i32, _i64, _i64, _i64, _p, _i64, _p, _i64, _p, _i64, _p],
+    "fp8_quantize_weight_128x128_pow2": [_p, _i32, _i64, _i64, _i64, _p, _i64, _p, _i64, _p, _i64,
+                                         _p, _i64, _p, _i64, _p],
+    "fp8_quantize_transposed_pow2": [_p, _i32, _i64, _i64, _i64, _p, _i64, _p, _i64, _p, _i64,
+                                     _p, _i64, _p, _i64, _p, _i64, _p],
     "fp8_gemm_fprop": [_p, _i64, _p, _i64, _p, _i64, _p, _i64, _p, _i32, _i64, _i64, _i64, _i64, _p],
     "fp8_gemm_dgrad": [_p, _i64, _p, _i64, _p, _i64, _p, _i64, _p, _i32, _i64, _i64, _i64, _i64, _p],
     "fp8_gemm_wgrad": [_p, _i64, _p, _i64, _p, _i64, _p, _i64, _p, _i32, _i64, _i32, _i64, _i64, _i64, _p],
@@ -208,6 +213,60 @@ def fp8_quantize_transposed_grouped(x, offsets, rowwise: bool = False, qT=None, 
           _ptr(q), _ld(q) if q is not None else 0, _ptr(s), _ld(s) if s is not None else 0,
           _stream(x.device))
     return qT, sT, q, s
+
+
+# ------------------------------------------- power-of-two block scales
+def _e8(rows: int, K: int, dev):
+    return _new((rows, _rup(K) // 32), torch.uint8, dev)
+
+
+def fp8_quantize_act_1x128_pow2(x, e8: bool = True):
+    """R1 with power-of-two scales -> (q, s, e8 [rows, rup(cols)/32] or None)."""
+    _check_2d(x, "x")
+    rows, cols = x.shape
+    q = _new((rows, _rup(cols)), torch.uint8, x.device)
+    s = _new((rows, _cdiv(cols, 128)), torch.float32, x.device)
+    e = _e8(rows, cols, x.device) if e8 else None
+    _call("fp8_quantize_act_1x128_pow2", _ptr(x), _dtype_code(x), rows, cols, _ld(x),
+          _ptr(q), _ld(q), _ptr(s), _ld(s), _ptr(e), _ld(e) if e is not None else 0, _stream(x.device))
+    return q, s, e
+
+
+def fp8_quantize_weight_128x128_pow2(w, transpose: bool = True, e8: bool = True):
+    """R2 with power-of-two scales -> (q, s, qT or None, e8 [D, rup(C)/32]
+    or None, e8T [C, rup(D)/32] or None; e8T only with the transpose)."""
+    _check_2d(w, "w")
+    D, C = w.shape
+    q = _new((D, _rup(C)), torch.uint8, w.device)
+    s = _new((_cdiv(D, 128), _cdiv(C, 128)), torch.float32, w.device)
+    qT = _new((C, _rup(D)), torch.uint8, w.device) if transpose else None
+    e = _e8(D, C, w.device) if e8 else None
+    eT = _e8(C, D, w.device) if (e8 and transpose) else None
+    _call("fp8_quantize_weight_128x128_pow2", _ptr(w), _dtype_code(w), D, C, _ld(w),
+          _ptr(q), _ld(q), _ptr(s), _ld(s), _ptr(qT), _ld(qT) if qT is not None else 0,
+          _ptr(e), _ld(e) if e is not None else 0, _ptr(eT), _ld(eT) if eT is not None else 0,
+          _stream(w.device))
+    return q, s, qT, e, eT
+
+
+def fp8_quantize_transposed_pow2(x, rowwise: bool = False, e8: bool = True):
+    """R3 with power-of-two scales -> (qT, sT, e8T, q, s, e8); the row-wise
+    outputs are None unless rowwise, the E8M0 outputs None unless e8."""
+    _check_2d(x, "x")
+    rows, cols = x.shape
+    qT = _new((cols, _rup(rows)), torch.uint8, x.device)
+    sT = _new((cols, _cdiv(rows, 128)), torch.float32, x.device)
+    eT = _e8(cols, rows, x.device) if e8 else None
+    q = s = e = None
+    if rowwise:
+        q = _new((rows, _rup(cols)), torch.uint8, x.device)
+        s = _new((rows, _cdiv(cols, 128)), torch.float32, x.device)
+        e = _e8(rows, cols, x.device) if e8 else None
+    _call("fp8_quantize_transposed_pow2", _ptr(x), _dtype_code(x), rows, cols, _ld(x),
+          _ptr(qT), _ld(qT), _ptr(sT), _ld(sT), _ptr(eT), _ld(eT) if eT is not None else 0,
+          _ptr(q), _ld(q) if q is not None else 0, _ptr(s), _ld(s) if s is not None else 0,
+          _ptr(e), _ld(e) if e is not None else 0, _stream(x.device))
+    return qT, sT, eT, q, s, e
 
 
 # ---------------------------------------------------------------- GEMMs

@@ -154,30 +154,70 @@ const char* fp8b_status_string(int status) {
 
 int fp8b_last_hip_error(void) { return g_last_hip_error; }
 
-int fp8_quantize_act_1x128(const void* x, int xt, int64_t rows, int64_t cols, int64_t ldx,
-                           uint8_t* q, int64_t ldq, float* s, int64_t lds, void* stream) {
+// E8M0 bytes of power-of-two groups (nullable): rows x round_up(K,128)/32,
+// written as 4-byte words, so the pointer and the row stride are multiples of 4.
+static int check_e8(const uint8_t* e, int64_t rows, int64_t K, int64_t ld) {
+    if (e == nullptr) return FP8B_OK;
+    FP8B_TRY(check_scales(e, rows, rup128(K) / 32, ld, 4));
+    if (rows > 0 && K > 0 && ld % 4 != 0) return FP8B_EALIGN;
+    return FP8B_OK;
+}
+
+static int quantize_act_impl(const void* x, int xt, int64_t rows, int64_t cols, int64_t ldx,
+                             uint8_t* q, int64_t ldq, float* s, int64_t lds,
+                             bool pow2, uint8_t* e8, int64_t lde, void* stream) {
     FP8B_TRY(check_input(x, xt, rows, cols, ldx));
     FP8B_TRY(check_codes(q, rows, cols, ldq));
     FP8B_TRY(check_scales(s, rows, cdiv(cols, 128), lds, 4));
-    return hip_status(launch_quant_rows(x, xt == FP8B_BF16, rows, cols, ldx, q, ldq, s, lds,
+    FP8B_TRY(check_e8(e8, rows, cols, lde));
+    return hip_status(launch_quant_rows(x, xt == FP8B_BF16, rows, cols, ldx, q, ldq, s, lds, pow2, e8, lde,
                                         static_cast<hipStream_t>(stream)));
+}
+
+int fp8_quantize_act_1x128(const void* x, int xt, int64_t rows, int64_t cols, int64_t ldx,
+                           uint8_t* q, int64_t ldq, float* s, int64_t lds, void* stream) {
+    return quantize_act_impl(x, xt, rows, cols, ldx, q, ldq, s, lds, false, nullptr, 0, stream);
+}
+
+int fp8_quantize_act_1x128_pow2(const void* x, int xt, int64_t rows, int64_t cols, int64_t ldx,
+                                uint8_t* q, int64_t ldq, float* s, int64_t lds,
+                                uint8_t* e8, int64_t lde, void* stream) {
+    return quantize_act_impl(x, xt, rows, cols, ldx, q, ldq, s, lds, true, e8, lde, stream);
+}
+
+static int quantize_weight_impl(const void* w, int wt, int64_t D, int64_t C, int64_t ldw,
+                                uint8_t* q, int64_t ldq, float* s, int64_t lds,
+                                uint8_t* qT, int64_t ldqT,
+                                bool pow2, uint8_t* e8, int64_t lde, uint8_t* e8T, int64_t ldeT, void* stream) {
+    FP8B_TRY(check_input(w, wt, D, C, ldw));
+    FP8B_TRY(check_codes(q, D, C, ldq));
+    FP8B_TRY(check_scales(s, cdiv(D, 128), cdiv(C, 128), lds, 4));
+    if (qT != nullptr) FP8B_TRY(check_codes(qT, C, D, ldqT));
+    FP8B_TRY(check_e8(e8, D, C, lde));
+    FP8B_TRY(check_e8(e8T, C, D, ldeT));
+    return hip_status(launch_quant_weight(w, wt == FP8B_BF16, D, C, ldw, q, ldq, s, lds, qT, ldqT,
+                                          pow2, e8, lde, e8T, ldeT, static_cast<hipStream_t>(stream)));
 }
 
 int fp8_quantize_weight_128x128(const void* w, int wt, int64_t D, int64_t C, int64_t ldw,
                                 uint8_t* q, int64_t ldq, float* s, int64_t lds,
                                 uint8_t* qT, int64_t ldqT, void* stream) {
-    FP8B_TRY(check_input(w, wt, D, C, ldw));
-    FP8B_TRY(check_codes(q, D, C, ldq));
-    FP8B_TRY(check_scales(s, cdiv(D, 128), cdiv(C, 128), lds, 4));
-    if (qT != nullptr) FP8B_TRY(check_codes(qT, C, D, ldqT));
-    return hip_status(launch_quant_weight(w, wt == FP8B_BF16, D, C, ldw, q, ldq, s, lds, qT, ldqT,
-                                          static_cast<hipStream_t>(stream)));
+    return quantize_weight_impl(w, wt, D, C, ldw, q, ldq, s, lds, qT, ldqT, false, nullptr, 0, nullptr, 0, stream);
+}
+
+int fp8_quantize_weight_128x128_pow2(const void* w, int wt, int64_t D, int64_t C, int64_t ldw,
+                                     uint8_t* q, int64_t ldq, float* s, int64_t lds,
+                                     uint8_t* qT, int64_t ldqT,
+                                     uint8_t* e8, int64_t lde, uint8_t* e8T, int64_t ldeT, void* stream) {
+    return quantize_weight_impl(w, wt, D, C, ldw, q, ldq, s, lds, qT, ldqT, true, e8, lde, e8T, ldeT, stream);
 }
 
 static int quantize_transposed_impl(const void* x, int xt, int64_t rows, int64_t cols, int64_t ldx,
                                     const int32_t* offsets, int64_t E,
                                     uint8_t* qT, int64_t ldqT, float* sT, int64_t ldsT,
-                                    uint8_t* q, int64_t ldq, float* s, int64_t lds, void* stream) {
+                                    uint8_t* q, int64_t ldq, float* s, int64_t lds,
+                                    bool pow2, uint8_t* e8T, int64_t ldeT, uint8_t* e8, int64_t lde,
+                                    void* stream) {
     FP8B_TRY(check_input(x, xt, rows, cols, ldx));
     const int64_t P = offsets ? rows + 128 * E : rows;    // upper bound of the padded token axis
     FP8B_TRY(check_codes(qT, cols, P, ldqT));
@@ -187,14 +227,26 @@ static int quantize_transposed_impl(const void* x, int xt, int64_t rows, int64_t
         FP8B_TRY(check_codes(q, rows, cols, ldq));
         FP8B_TRY(check_scales(s, rows, cdiv(cols, 128), lds, 4));
     }
+    if (e8 != nullptr && q == nullptr) return FP8B_EINVAL;
+    FP8B_TRY(check_e8(e8T, cols, P, ldeT));
+    FP8B_TRY(check_e8(e8, rows, cols, lde));
     return hip_status(launch_quant_cols(x, xt == FP8B_BF16, rows, cols, ldx, offsets, E, qT, ldqT, sT, ldsT,
-                                        q, ldq, s, lds, static_cast<hipStream_t>(stream)));
+                                        q, ldq, s, lds, pow2, e8T, ldeT, e8, lde, static_cast<hipStream_t>(stream)));
 }
 
 int fp8_quantize_transposed(const void* x, int xt, int64_t rows, int64_t cols, int64_t ldx,
                             uint8_t* qT, int64_t ldqT, float* sT, int64_t ldsT,
                             uint8_t* q, int64_t ldq, float* s, int64_t lds, void* stream) {
-    return quantize_transposed_impl(x, xt, rows, cols, ldx, nullptr, 0, qT, ldqT, sT, ldsT, q, ldq, s, lds, stream);
+    return quantize_transposed_impl(x, xt, rows, cols, ldx, nullptr, 0, qT, ldqT, sT, ldsT, q, ldq, s, lds,
+                                    false, nullptr, 0, nullptr, 0, stream);
+}
+
+int fp8_quantize_transposed_pow2(const void* x, int xt, int64_t rows, int64_t cols, int64_t ldx,
+                                 uint8_t* qT, int64_t ldqT, float* sT, int64_t ldsT, uint8_t* e8T, int64_t ldeT,
+                                 uint8_t* q, int64_t ldq, float* s, int64_t lds, uint8_t* e8, int64_t lde,
+                                 void* stream) {
+    return quantize_transposed_impl(x, xt, rows, cols, ldx, nullptr, 0, qT, ldqT, sT, ldsT, q, ldq, s, lds,
+                                    true, e8T, ldeT, e8, lde, stream);
 }
 
 int fp8_quantize_transposed_grouped(const void* x, int xt, int64_t rows, int64_t cols, int64_t ldx,
@@ -202,7 +254,8 @@ int fp8_quantize_transposed_grouped(const void* x, int xt, int64_t rows, int64_t
                                     uint8_t* qT, int64_t ldqT, float* sT, int64_t ldsT,
                                     uint8_t* q, int64_t ldq, float* s, int64_t lds, void* stream) {
     FP8B_TRY(check_offsets(offsets, E));
-    return quantize_transposed_impl(x, xt, rows, cols, ldx, offsets, E, qT, ldqT, sT, ldsT, q, ldq, s, lds, stream);
+    return quantize_transposed_impl(x, xt, rows, cols, ldx, offsets, E, qT, ldqT, sT, ldsT, q, ldq, s, lds,
+                                    false, nullptr, 0, nullptr, 0, stream);
 }
 
 int fp8b_validate_gemm(int op, const void* a, int64_t lda, const void* sa, int64_t ldsa,

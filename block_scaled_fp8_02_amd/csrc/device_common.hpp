@@ -41,6 +41,32 @@ __device__ __forceinline__ float group_scale(float amax) {
     return (float)((double)amax / 448.0);
 }
 
+// Power-of-two exponent of a block: the smallest k with amax <= 448 * 2^k
+// (the block maximum never clips), clamped to [-127, 127]; -127 for an
+// all-zero block.  With amax = m * 2^e, m in [0.5, 1): 448 = 0.875 * 2^9, so
+// k = e - 9 when m <= 0.875 and k = e - 8 otherwise.  It gives the E8M0
+// scales of MXFP8 (byte k + 127) and the power-of-two FP32 block scales.
+__device__ __forceinline__ int mx_exponent(float amax) {
+    if (amax == 0.0f) return -127;
+    int e;
+    const float m = frexpf(amax, &e);
+    const int k = e - 9 + (m > 0.875f ? 1 : 0);
+    return k < -127 ? -127 : (k > 127 ? 127 : k);
+}
+
+// Block scale of the FP32-scale recipe (P2 = false): fl32(amax / 448); of
+// the power-of-two recipe (P2 = true): 2^k with k = mx_exponent(amax).
+template <bool P2>
+__device__ __forceinline__ float block_scale(float amax) {
+    return P2 ? ldexpf(1.0f, mx_exponent(amax)) : group_scale(amax);
+}
+
+// E8M0 byte of a power-of-two scale's block, replicated over the four
+// 32-wide sub-blocks of one 128-wide group (one little-endian word).
+__device__ __forceinline__ uint32_t e8m0_x4(float amax) {
+    return (uint32_t)(mx_exponent(amax) + 127) * 0x01010101u;
+}
+
 // The quotient fl32(x / S), without the long IEEE division sequence.  With
 // r = RN32(1/S), q0 = RN32(x * r) is within one ulp of x/S; the residual
 // e = q0*S - x is then exact in one FMA, and one Newton step q0 - e*r

@@ -8,27 +8,36 @@
 
 namespace fp8blk {
 
+// Quantizers.  pow2 selects power-of-two block scales (2^k, k the smallest
+// exponent with amax <= 448 * 2^k) and lets the kernels also write the E8M0
+// bytes of every group, replicated over its four 32-wide sub-blocks (e8 for
+// the row-wise codes, e8T for the transposed ones; nullable).
+
 // Row-wise 1x128 quantization (in_bf16: bf16 input, else fp32).
 hipError_t launch_quant_rows(const void* x, bool in_bf16, int64_t rows, int64_t cols, int64_t ldx,
-                             uint8_t* q, int64_t ldq, float* s, int64_t lds, hipStream_t st);
+                             uint8_t* q, int64_t ldq, float* s, int64_t lds,
+                             bool pow2, uint8_t* e8, int64_t lde, hipStream_t st);
 
 // 128x128 weight quantization with optional transposed copy.
 hipError_t launch_quant_weight(const void* w, bool in_bf16, int64_t D, int64_t C, int64_t ldw,
                                uint8_t* q, int64_t ldq, float* s, int64_t lds,
-                               uint8_t* qT, int64_t ldqT, hipStream_t st);
+                               uint8_t* qT, int64_t ldqT,
+                               bool pow2, uint8_t* e8, int64_t lde, uint8_t* e8T, int64_t ldeT, hipStream_t st);
 
 // Token-axis 1x128 quantization written transposed, optionally also the
 // row-wise copy; offsets == nullptr means one segment of all rows.
 hipError_t launch_quant_cols(const void* x, bool in_bf16, int64_t rows, int64_t cols, int64_t ldx,
                              const int32_t* offsets, int64_t E,
                              uint8_t* qT, int64_t ldqT, float* sT, int64_t ldsT,
-                             uint8_t* q, int64_t ldq, float* s, int64_t lds, hipStream_t st);
+                             uint8_t* q, int64_t ldq, float* s, int64_t lds,
+                             bool pow2, uint8_t* e8T, int64_t ldeT, uint8_t* e8, int64_t lde, hipStream_t st);
+
+// Elementwise codec access.
+hipError_t launch_encode(const float* x, const float* s, int64_t n, uint8_t* out, hipStream_t st);
 
 // Compute units of the current device (cached per device).
 int device_cu_count();
 
-// Elementwise codec access.
-hipError_t launch_encode(const float* x, const float* s, int64_t n, uint8_t* out, hipStream_t st);
 
 // Generic block-scaled / MX GEMM:
 //   O[i][j] (+)= sum_k P[i][k] Q[j][k] * scales

@@ -12,17 +12,6 @@
 
 namespace fp8blk {
 
-// Smallest k with amax <= 448 * 2^k, clamped to [-127, 127]; -127 for 0.
-// With amax = m * 2^e, m in [0.5, 1): 448 = 0.875 * 2^9, so k = e - 9 when
-// m <= 0.875 and k = e - 8 otherwise.
-__device__ __forceinline__ int mx_exponent(float amax) {
-    if (amax == 0.0f) return -127;
-    int e;
-    const float m = frexpf(amax, &e);
-    int k = e - 9 + (m > 0.875f ? 1 : 0);
-    return k < -127 ? -127 : (k > 127 ? 127 : k);
-}
-
 __device__ __forceinline__ uint32_t mx_encode4(const float* v, int k) {
     return e4m3_pack4(ldexpf(v[0], -k), ldexpf(v[1], -k), ldexpf(v[2], -k), ldexpf(v[3], -k));
 }

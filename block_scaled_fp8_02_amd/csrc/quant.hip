@@ -23,10 +23,11 @@ namespace fp8blk {
 // 1x128 row-wise.  A 16-lane slot owns one group of 128 elements, 8 per
 // lane; a 256-thread block owns 16 consecutive groups (row-major order).
 // ---------------------------------------------------------------------
-template <typename T>
+template <typename T, bool P2>
 __global__ __launch_bounds__(256) void k_quant_rows(const T* __restrict__ x, int64_t cols, int64_t ldx,
                                                     uint8_t* __restrict__ q, int64_t ldq,
                                                     float* __restrict__ s, int64_t lds,
+                                                    uint8_t* __restrict__ e8, int64_t lde,
                                                     uint32_t groups_per_row, uint32_t total_groups) {
     const uint32_t grp = blockIdx.x * 16u + (threadIdx.x >> 4);
     if (grp >= total_groups) return;                 // whole 16-lane slots exit together
@@ -41,7 +42,7 @@ __global__ __launch_bounds__(256) void k_quant_rows(const T* __restrict__ x, int
 #pragma unroll
     for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(v[i]));
     amax = max16(amax);
-    const float S = group_scale(amax);
+    const float S = block_scale<P2>(amax);
     const float P = prescale(S);
     const float Sp = S * P, r = recip32(Sp);
     float y[8];
@@ -56,7 +57,10 @@ __global__ __launch_bounds__(256) void k_quant_rows(const T* __restrict__ x, int
     out.x = e4m3_pack4_q(y[0], y[1], y[2], y[3]);
     out.y = e4m3_pack4_q(y[4], y[5], y[6], y[7]);
     *reinterpret_cast<uint2*>(q + (int64_t)row * ldq + col0) = out;
-    if (lane16 == 0) s[(int64_t)row * lds + g] = S;
+    if (lane16 == 0) {
+        s[(int64_t)row * lds + g] = S;
+        if (P2 && e8 != nullptr) *reinterpret_cast<uint32_t*>(e8 + (int64_t)row * lde + 4 * (int64_t)g) = e8m0_x4(amax);
+    }
 }
 
 // ---------------------------------------------------------------------
@@ -87,6 +91,8 @@ struct QuantTileArgs {
     const int32_t* offsets; int64_t E;
     uint8_t* q; int64_t ldq; float* s; int64_t lds;
     uint8_t* qT; int64_t ldqT; float* sT; int64_t ldsT;
+    uint8_t* e8; int64_t lde;       // power-of-two scales: E8M0 bytes of q's groups (nullable)
+    uint8_t* e8T; int64_t ldeT;     // and of qT's groups (nullable)
     int64_t col_tiles;
     int64_t tiles;          // dense: exact tile count; grouped: an upper bound
 };
@@ -252,7 +258,7 @@ __device__ __forceinline__ void lds_barrier() {
     asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 
-template <typename T, int MODE>
+template <typename T, int MODE, bool P2>
 __global__ __launch_bounds__(256, 2) void k_quant_tiles(QuantTileArgs A) {
     __shared__ __attribute__((aligned(16))) float red_col[16][128];   // [row slice][column]
     __shared__ __attribute__((aligned(16))) float red_row[16][128];   // [column slice][row]
@@ -296,8 +302,16 @@ __global__ __launch_bounds__(256, 2) void k_quant_tiles(QuantTileArgs A) {
             if (lane == 0) red4[wave] = m;
             lds_barrier();                                           // (1)
             m = fmaxf(fmaxf(red4[0], red4[1]), fmaxf(red4[2], red4[3]));
-            const float S = group_scale(m);
+            const float S = block_scale<P2>(m);
             if (t == 0) A.s[at.rt * A.lds + at.ct] = S;
+            if (P2) {                                                  // E8M0 per row (q) and per column (qT)
+                const uint32_t ew = e8m0_x4(m);
+                if (t < 128) {
+                    if (A.e8 != nullptr && at.a + t < at.b) *reinterpret_cast<uint32_t*>(A.e8 + (at.a + t) * A.lde + 4 * at.ct) = ew;
+                } else if (A.e8T != nullptr && at.cb + t - 128 < A.cols) {
+                    *reinterpret_cast<uint32_t*>(A.e8T + (at.cb + t - 128) * A.ldeT + 4 * at.rt) = ew;
+                }
+            }
             const float P = prescale(S);
             float Sv[8], rv[8], Pv[8];
 #pragma unroll
@@ -335,7 +349,9 @@ __global__ __launch_bounds__(256, 2) void k_quant_tiles(QuantTileArgs A) {
                 float m = red_col[0][t];
 #pragma unroll
                 for (int i = 1; i < 16; ++i) m = fmaxf(m, red_col[i][t]);
-                const float S = group_scale(m), P = prescale(S);
+                const float S = block_scale<P2>(m), P = prescale(S);
+                if (P2 && A.e8T != nullptr && at.cb + t < A.cols)
+                    *reinterpret_cast<uint32_t*>(A.e8T + (at.cb + t) * A.ldeT + at.pos / 32) = e8m0_x4(m);
                 sc_col[0][t] = S * P;
                 sc_col[1][t] = recip32(S * P);
                 sc_col[2][t] = P;
@@ -346,7 +362,9 @@ __global__ __launch_bounds__(256, 2) void k_quant_tiles(QuantTileArgs A) {
                 float m = red_row[0][rr];
 #pragma unroll
                 for (int i = 1; i < 16; ++i) m = fmaxf(m, red_row[i][rr]);
-                const float S = group_scale(m), P = prescale(S);
+                const float S = block_scale<P2>(m), P = prescale(S);
+                if (P2 && A.e8 != nullptr && at.a + rr < at.b)
+                    *reinterpret_cast<uint32_t*>(A.e8 + (at.a + rr) * A.lde + 4 * at.ct) = e8m0_x4(m);
                 sc_row[0][rr] = S * P;
                 sc_row[1][rr] = recip32(S * P);
                 sc_row[2][rr] = P;
@@ -428,23 +446,25 @@ __global__ __launch_bounds__(256) void k_encode(const float* __restrict__ x, con
 // launchers
 // ---------------------------------------------------------------------
 hipError_t launch_quant_rows(const void* x, bool in_bf16, int64_t rows, int64_t cols, int64_t ldx,
-                             uint8_t* q, int64_t ldq, float* s, int64_t lds, hipStream_t st) {
+                             uint8_t* q, int64_t ldq, float* s, int64_t lds,
+                             bool pow2, uint8_t* e8, int64_t lde, hipStream_t st) {
     const int64_t gpr = (cols + 127) / 128;
     const int64_t total = rows * gpr;
     if (total == 0) return hipSuccess;
     if (total > 0xFFFFFFF0ll) return hipErrorInvalidValue;
     const dim3 grid((unsigned)((total + 15) / 16));
-    if (in_bf16)
-        k_quant_rows<uint16_t><<<grid, 256, 0, st>>>(static_cast<const uint16_t*>(x), cols, ldx, q, ldq, s, lds,
-                                                      (uint32_t)gpr, (uint32_t)total);
-    else
-        k_quant_rows<float><<<grid, 256, 0, st>>>(static_cast<const float*>(x), cols, ldx, q, ldq, s, lds,
-                                                   (uint32_t)gpr, (uint32_t)total);
+#define FP8B_ROWS(T_, P2_) \
+    k_quant_rows<T_, P2_><<<grid, 256, 0, st>>>(static_cast<const T_*>(x), cols, ldx, q, ldq, s, lds, e8, lde, \
+                                                 (uint32_t)gpr, (uint32_t)total)
+    if (in_bf16) {
+        if (pow2) FP8B_ROWS(uint16_t, true); else FP8B_ROWS(uint16_t, false);
+    } else {
+        if (pow2) FP8B_ROWS(float, true); else FP8B_ROWS(float, false);
+    }
+#undef FP8B_ROWS
     return hipGetLastError();
 }
 
-// Blocks of the persistent tile quantizer: two per compute unit (its
-// register and LDS budget allows two), never more than there are tiles.
 int device_cu_count() {
     static int cu_count[64];
     int dev = 0;
@@ -463,44 +483,53 @@ static int64_t tile_grid(int64_t tiles) {
 }
 
 template <int MODE>
-static hipError_t launch_tiles(bool in_bf16, const QuantTileArgs& A, hipStream_t st) {
+static hipError_t launch_tiles(bool in_bf16, bool pow2, const QuantTileArgs& A, hipStream_t st) {
     const int64_t blocks = tile_grid(A.tiles);
     if (blocks <= 0) return hipSuccess;
-    if (in_bf16)
-        k_quant_tiles<uint16_t, MODE><<<dim3((unsigned)blocks), 256, 0, st>>>(A);
-    else
-        k_quant_tiles<float, MODE><<<dim3((unsigned)blocks), 256, 0, st>>>(A);
+    const dim3 grid((unsigned)blocks);
+    if (in_bf16) {
+        if (pow2) k_quant_tiles<uint16_t, MODE, true><<<grid, 256, 0, st>>>(A);
+        else k_quant_tiles<uint16_t, MODE, false><<<grid, 256, 0, st>>>(A);
+    } else {
+        if (pow2) k_quant_tiles<float, MODE, true><<<grid, 256, 0, st>>>(A);
+        else k_quant_tiles<float, MODE, false><<<grid, 256, 0, st>>>(A);
+    }
     return hipGetLastError();
 }
 
 hipError_t launch_quant_weight(const void* w, bool in_bf16, int64_t D, int64_t C, int64_t ldw,
                                uint8_t* q, int64_t ldq, float* s, int64_t lds,
-                               uint8_t* qT, int64_t ldqT, hipStream_t st) {
+                               uint8_t* qT, int64_t ldqT,
+                               bool pow2, uint8_t* e8, int64_t lde, uint8_t* e8T, int64_t ldeT, hipStream_t st) {
     if (D == 0 || C == 0) return hipSuccess;
     QuantTileArgs A{};
     A.x = w; A.rows = D; A.cols = C; A.ldx = ldw;
     A.offsets = nullptr; A.E = 0;
     A.q = q; A.ldq = ldq; A.s = s; A.lds = lds;
     A.qT = qT; A.ldqT = ldqT; A.sT = nullptr; A.ldsT = 0;
+    A.e8 = e8; A.lde = lde; A.e8T = e8T; A.ldeT = ldeT;
     A.col_tiles = (C + 127) / 128;
     A.tiles = (D + 127) / 128 * A.col_tiles;
-    return launch_tiles<QT_WEIGHT>(in_bf16, A, st);
+    return launch_tiles<QT_WEIGHT>(in_bf16, pow2, A, st);
 }
 
 hipError_t launch_quant_cols(const void* x, bool in_bf16, int64_t rows, int64_t cols, int64_t ldx,
                              const int32_t* offsets, int64_t E,
                              uint8_t* qT, int64_t ldqT, float* sT, int64_t ldsT,
-                             uint8_t* q, int64_t ldq, float* s, int64_t lds, hipStream_t st) {
+                             uint8_t* q, int64_t ldq, float* s, int64_t lds,
+                             bool pow2, uint8_t* e8T, int64_t ldeT, uint8_t* e8, int64_t lde, hipStream_t st) {
     if (rows == 0 || cols == 0) return hipSuccess;
     QuantTileArgs A{};
     A.x = x; A.rows = rows; A.cols = cols; A.ldx = ldx;
     A.offsets = offsets; A.E = offsets ? E : 0;
     A.q = q; A.ldq = ldq; A.s = s; A.lds = lds;
     A.qT = qT; A.ldqT = ldqT; A.sT = sT; A.ldsT = ldsT;
+    A.e8 = e8; A.lde = lde; A.e8T = e8T; A.ldeT = ldeT;
     A.col_tiles = (cols + 127) / 128;
     // grouped: at most one partial tile per expert beyond rows/128
     A.tiles = ((rows + 127) / 128 + A.E) * A.col_tiles;
-    return q != nullptr ? launch_tiles<QT_COLS_ROWS>(in_bf16, A, st) : launch_tiles<QT_COLS>(in_bf16, A, st);
+    return q != nullptr ? launch_tiles<QT_COLS_ROWS>(in_bf16, pow2, A, st)
+                        : launch_tiles<QT_COLS>(in_bf16, pow2, A, st);
 }
 
 hipError_t launch_encode(const float* x, const float* s, int64_t n, uint8_t* out, hipStream_t st) {

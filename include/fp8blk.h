@@ -135,6 +135,41 @@ FP8B_API int fp8_quantize_transposed_grouped(const void* x, int xt, int64_t rows
                                     uint8_t* qT, int64_t ldqT, float* sT, int64_t ldsT,
                                     uint8_t* q, int64_t ldq, float* s, int64_t lds, void* stream);
 
+/* Power-of-two block scales (the SkyRL section "FP8 quantization with FP32
+ * and power-of-two block scales": FP32 scales constrained to powers of two,
+ * an exponent-only representation, the only kind Blackwell tensor cores
+ * take).  Same groupings, layouts and codes rule as R1-R3, with the scale of
+ * a group S = 2^k, k the smallest integer with max|x| <= 448 * 2^k (rounded
+ * up so the group maximum does not clip; the pages do not state the rounding,
+ * this is the rule they give for E8M0 scales), clamped to [-127, 127]; an
+ * all-zero group has S = 2^-127.  The fp32 scales feed the block-scaled GEMMs
+ * unchanged.  Each call can also write the E8M0 byte k + 127 of every group,
+ * repeated over its four 32-wide sub-blocks, in the layout of the MXFP8
+ * scales (rows x ld bytes, ld >= round_up(K,128)/32, K the codes' padded
+ * contraction axis; pointer and ld multiples of 4; NULL to skip): with those
+ * bytes the MXFP8 GEMMs below compute the same products on the gfx950
+ * scaled MFMA, with no per-block promotion in software. */
+
+/* R1 with power-of-two scales; e8: rows x lde E8M0 bytes (nullable). */
+FP8B_API int fp8_quantize_act_1x128_pow2(const void* x, int xt, int64_t rows, int64_t cols, int64_t ldx,
+                                uint8_t* q, int64_t ldq, float* s, int64_t lds,
+                                uint8_t* e8, int64_t lde, void* stream);
+
+/* R2 with power-of-two scales; e8: D x lde E8M0 bytes of q's rows (the
+ * block's byte repeated for its 128 rows), e8T: C x ldeT bytes of qT's rows
+ * (nullable each; e8T is the scale input of fp8_mx_gemm_dgrad). */
+FP8B_API int fp8_quantize_weight_128x128_pow2(const void* w, int wt, int64_t D, int64_t C, int64_t ldw,
+                                     uint8_t* q, int64_t ldq, float* s, int64_t lds,
+                                     uint8_t* qT, int64_t ldqT,
+                                     uint8_t* e8, int64_t lde, uint8_t* e8T, int64_t ldeT, void* stream);
+
+/* R3 with power-of-two scales; e8T: cols x ldeT bytes of qT's groups, e8:
+ * rows x lde bytes of the row-wise copy (requires q; nullable each). */
+FP8B_API int fp8_quantize_transposed_pow2(const void* x, int xt, int64_t rows, int64_t cols, int64_t ldx,
+                                 uint8_t* qT, int64_t ldqT, float* sT, int64_t ldsT, uint8_t* e8T, int64_t ldeT,
+                                 uint8_t* q, int64_t ldq, float* s, int64_t lds, uint8_t* e8, int64_t lde,
+                                 void* stream);
+
 /* ------------------------------------------------------------------ */
 /* Block-scaled FP8 GEMMs (fp32 accumulation; each 128-wide K block's    */
 /* partial product is scaled by s_a * s_b before it is added)           */

@@ -88,3 +88,20 @@ def test_binding_refuses_cpu_tensors():
     torch = pytest.importorskip("torch")
     with pytest.raises(ValueError):
         fb.fp8_quantize_act_1x128(torch.zeros(4, 128, dtype=torch.bfloat16))
+
+
+def test_pow2_quantizers_reject_bad_e8m0_buffers_on_host():
+    """The power-of-two quantizers check their E8M0 side outputs before any
+    launch (pointers below are never dereferenced: every call fails first)."""
+    L = fb.lib()
+    X, Q, S, E = 0x100000, 0x200000, 0x300000, 0x400000
+    # rows 4, cols 256: e8 needs 4 x 8 bytes, 4-byte aligned pointer and stride
+    assert L.fp8_quantize_act_1x128_pow2(X, 1, 4, 256, 256, Q, 256, S, 2, E + 2, 8, None) == 3
+    assert L.fp8_quantize_act_1x128_pow2(X, 1, 4, 256, 256, Q, 256, S, 2, E, 6, None) == 2
+    assert L.fp8_quantize_act_1x128_pow2(X, 1, 4, 256, 256, Q, 256, S, 2, E, 10, None) == 3
+    # weight: e8T must cover round_up(D,128)/32 bytes per row of W^T
+    assert L.fp8_quantize_weight_128x128_pow2(X, 1, 300, 256, 256, Q, 256, S, 2, Q, 384,
+                                              E, 8, E, 8, None) == 2
+    # transposed: a row-wise E8M0 buffer without the row-wise codes
+    assert L.fp8_quantize_transposed_pow2(X, 1, 256, 64, 64, Q, 256, S, 2, E, 8,
+                                          None, 0, None, 0, E, 4, None) == 1
