@@ -47,6 +47,7 @@ def _load():
     lib.ora_quant_128x128.argtypes = [_p, _i64, _i64, _i64, _p, _i64, _p, _i64, _p, _i64]
     lib.ora_quant_colwise.argtypes = [_p, _i64, _i64, _i64, _p, _i64, _p, _i64, _p, _i64]
     lib.ora_quant_1x128_p2.argtypes = lib.ora_quant_1x128.argtypes
+    lib.ora_requant_colwise.argtypes = [_p, _i64, _p, _i64, _i64, _i64, _p, _i64, _p, _i64, _p, _i64]
     lib.ora_quant_128x128_p2.argtypes = lib.ora_quant_128x128.argtypes
     lib.ora_quant_colwise_p2.argtypes = lib.ora_quant_colwise.argtypes
     lib.ora_mx_exponent.restype = ctypes.c_int
@@ -157,6 +158,30 @@ def quant_colwise(x: np.ndarray, offsets: np.ndarray | None = None, pow2: bool =
     if P > 0:
         fn = lib.ora_quant_colwise_p2 if pow2 else lib.ora_quant_colwise
         fn(_ptr(x), rows, cols, cols, offs_p, E, _ptr(qT), qT.shape[1], _ptr(sT), sT.shape[1])
+    return qT, sT
+
+
+def requant_colwise(q: np.ndarray, s: np.ndarray, cols: int, offsets: np.ndarray | None = None):
+    """Token-axis requantization of saved 1x128 codes q [rows, >= cols] with
+    scales s [rows, ceil(cols/128)]: dequantize in fp32, then quant_colwise.
+    Returns (qT, sT) in quant_colwise's layout."""
+    lib = _load()
+    q = np.ascontiguousarray(q, dtype=np.uint8)
+    s = np.ascontiguousarray(s, dtype=np.float32)
+    rows = q.shape[0]
+    if offsets is None:
+        P = _rup(rows, 128)
+        offs_p, E = None, 0
+    else:
+        offsets = np.ascontiguousarray(offsets, dtype=np.int32)
+        E = offsets.size - 1
+        P = int(padded_offsets(offsets)[-1])
+        offs_p = _ptr(offsets)
+    qT = np.full((cols, max(P, 0)), 0xAA, dtype=np.uint8)
+    sT = np.full((cols, max(P // 128, 0)), np.nan, dtype=np.float32)
+    if P > 0:
+        lib.ora_requant_colwise(_ptr(q), q.shape[1], _ptr(s), s.shape[1], rows, cols, offs_p, E,
+                                _ptr(qT), qT.shape[1], _ptr(sT), sT.shape[1])
     return qT, sT
 
 

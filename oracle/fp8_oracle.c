@@ -312,6 +312,28 @@ ORACLE_API void ora_quant_colwise_p2(const float* x, int64_t rows, int64_t cols,
 /* in double and the E4M3 rounding is the only rounding.                 */
 /* ------------------------------------------------------------------ */
 
+/* Requantization of saved 1x128 FP8 data along the token axis (the
+ * DeepSeek-V3-style flow the Jet-RL pages describe for WGrad's X^T, which
+ * keeps only the FP8 activations): each element is dequantized to fp32 with
+ * one binary32 multiply, fl32(E4M3(q) * s), and the result goes through the
+ * token-axis quantizer above.  The pages do not fix the dequantization
+ * precision; reading used: fp32, the precision the quantizer works in.
+ * q: rows x ldq codes of cols columns, s: rows x lds scales (1x128). */
+ORACLE_API void ora_requant_colwise(const uint8_t* q, int64_t ldq, const float* s, int64_t lds,
+                                    int64_t rows, int64_t cols, const int32_t* offsets, int64_t E,
+                                    uint8_t* qT, int64_t ldqT, float* sT, int64_t ldsT)
+{
+    e4m3_build();
+    float* x = (float*)malloc((size_t)(rows > 0 ? rows : 1) * (size_t)(cols > 0 ? cols : 1) * sizeof(float));
+    if (!x) return;
+    #pragma omp parallel for schedule(static)
+    for (int64_t r = 0; r < rows; ++r)
+        for (int64_t c = 0; c < cols; ++c)
+            x[r * cols + c] = (float)E4M3[q[r * ldq + c]] * s[r * lds + c / 128];
+    quant_colwise(x, rows, cols, cols, offsets, E, qT, ldqT, sT, ldsT, 0);
+    free(x);
+}
+
 ORACLE_API int ora_mx_exponent(float amax) { return mx_exponent(amax); }
 
 /* Row-wise MX: blocks of 32 along the contiguous axis.  q: rows x ldq with
