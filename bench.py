@@ -319,9 +319,10 @@ def main():
             tw[name] = {"error": str(ex)[:120]}
     ceil["fp8_tensorwise_hipblaslt"] = tw
 
-    pow2 = None
+    pow2 = requant = None
     if not args.no_other:
         pow2 = pow2_layer(torch, fb, copies, flops_gemm)
+        requant = requant_layer(torch, fb, copies)
 
     other = None
     if not args.no_other:
@@ -345,6 +346,7 @@ def main():
         "kernels": kernels, "roofline": roofline, "bf16_baseline": bf, "cpu_baseline": cpu,
         "measured_ceilings": ceil,
         "pow2_scales_layer": pow2,
+        "requant_from_fp8_X": requant,
         "other_workloads": other,
     }
     print(json.dumps(out), flush=True)
@@ -422,6 +424,33 @@ def pow2_layer(torch, fb, copies, flops_gemm):
         out[name] = ent
     gemm_us = sum(out[n]["us"] for n in ("fprop", "dgrad", "wgrad"))
     out["gemm_tflops"] = round(3 * flops_gemm / (gemm_us * 1e-6) / 1e12, 1)
+    return out
+
+
+def requant_layer(torch, fb, copies):
+    """X's two FP8 forms for the training layer made from the saved FP8
+    copy: the 1x128 quantizer alone in the forward pass, then the token-axis
+    requantizer in the backward pass, against the dual quantizer reading
+    bf16 X once for both.  Each kernel timed cold against its own HBM
+    roofline; `kept_bytes` is what stays resident between the passes."""
+    Xd = copies[0][0]
+    N, C = Xd.shape
+    cd = lambda a, b: (a + b - 1) // b
+    flush = torch.empty(1 << 28, dtype=torch.float32, device=Xd.device).fill_(1.0)
+    q, s = fb.fp8_quantize_act_1x128(Xd)
+    qT, sT = fb.fp8_requantize_transposed(q, s, C)
+    d = fb.fp8_quantize_transposed(Xd, rowwise=True)
+    rs, ts = N * cd(C, 128) * 4, C * cd(N, 128) * 4               # row-wise / token-axis scale bytes
+    out = {
+        "quant_act_1x128_X": report(time_cold(torch, lambda: fb.fp8_quantize_act_1x128(Xd, q, s), flush),
+                                    2 * N * C + N * C + rs),
+        "requant_X": report(time_cold(torch, lambda: fb.fp8_requantize_transposed(q, s, C, qT, sT), flush),
+                            N * C + rs + N * C + ts),
+        "quant_dual_X": report(time_cold(torch, lambda: fb.fp8_quantize_transposed(
+            Xd, rowwise=True, qT=d[0], sT=d[1], q=d[2], s=d[3]), flush), 2 * N * C + 2 * N * C + rs + ts),
+        "kept_bytes": {"bf16_X": 2 * N * C, "fp8_X": N * C + rs},
+    }
+    del flush
     return out
 
 

@@ -49,6 +49,8 @@ _SIGS = {
                                          _p, _i64, _p, _i64, _p],
     "fp8_quantize_transposed_pow2": [_p, _i32, _i64, _i64, _i64, _p, _i64, _p, _i64, _p, _i64,
                                      _p, _i64, _p, _i64, _p, _i64, _p],
+    "fp8_requantize_transposed": [_p, _i64, _p, _i64, _i64, _i64, _p, _i64, _p, _i64, _p],
+    "fp8_requantize_transposed_grouped": [_p, _i64, _p, _i64, _i64, _i64, _p, _i64, _p, _i64, _p, _i64, _p],
     "fp8_gemm_fprop": [_p, _i64, _p, _i64, _p, _i64, _p, _i64, _p, _i32, _i64, _i64, _i64, _i64, _p],
     "fp8_gemm_dgrad": [_p, _i64, _p, _i64, _p, _i64, _p, _i64, _p, _i32, _i64, _i64, _i64, _i64, _p],
     "fp8_gemm_wgrad": [_p, _i64, _p, _i64, _p, _i64, _p, _i64, _p, _i32, _i64, _i32, _i64, _i64, _i64, _p],
@@ -213,6 +215,32 @@ def fp8_quantize_transposed_grouped(x, offsets, rowwise: bool = False, qT=None, 
           _ptr(q), _ld(q) if q is not None else 0, _ptr(s), _ld(s) if s is not None else 0,
           _stream(x.device))
     return qT, sT, q, s
+
+
+# ----------------------------------------- requantization from FP8
+def fp8_requantize_transposed(q, s, cols: int, qT=None, sT=None):
+    """Token-axis codes from saved 1x128 codes q [rows, >= rup(cols)] and
+    scales s -> (qT [cols, rup(rows)], sT [cols, ceil(rows/128)])."""
+    _check_2d(q, "q")
+    rows = q.shape[0]
+    qT = _new((cols, _rup(rows)), torch.uint8, q.device) if qT is None else qT
+    sT = _new((cols, _cdiv(rows, 128)), torch.float32, q.device) if sT is None else sT
+    _call("fp8_requantize_transposed", _ptr(q), _ld(q), _ptr(s), _ld(s), rows, cols,
+          _ptr(qT), _ld(qT), _ptr(sT), _ld(sT), _stream(q.device))
+    return qT, sT
+
+
+def fp8_requantize_transposed_grouped(q, s, cols: int, offsets):
+    """Grouped form; layout as fp8_quantize_transposed_grouped."""
+    _check_2d(q, "q")
+    rows = q.shape[0]
+    E = offsets.numel() - 1
+    P = grouped_token_capacity(rows, E)
+    qT = _new((cols, P), torch.uint8, q.device)
+    sT = _new((cols, P // 128), torch.float32, q.device)
+    _call("fp8_requantize_transposed_grouped", _ptr(q), _ld(q), _ptr(s), _ld(s), rows, cols,
+          _ptr(offsets), E, _ptr(qT), _ld(qT), _ptr(sT), _ld(sT), _stream(q.device))
+    return qT, sT
 
 
 # ------------------------------------------- power-of-two block scales

@@ -258,6 +258,31 @@ int fp8_quantize_transposed_grouped(const void* x, int xt, int64_t rows, int64_t
                                     false, nullptr, 0, nullptr, 0, stream);
 }
 
+static int requantize_impl(const uint8_t* q, int64_t ldq, const float* s, int64_t lds,
+                           int64_t rows, int64_t cols, const int32_t* offsets, int64_t E,
+                           uint8_t* qT, int64_t ldqT, float* sT, int64_t ldsT, void* stream) {
+    FP8B_TRY(check_codes(q, rows, cols, ldq));
+    FP8B_TRY(check_scales(s, rows, cdiv(cols, 128), lds, 4));
+    const int64_t P = offsets ? rows + 128 * E : rows;
+    FP8B_TRY(check_codes(qT, cols, P, ldqT));
+    FP8B_TRY(check_scales(sT, cols, cdiv(P, 128), ldsT, 4));
+    return hip_status(launch_requant_cols(q, ldq, s, lds, rows, cols, offsets, E, qT, ldqT, sT, ldsT,
+                                          static_cast<hipStream_t>(stream)));
+}
+
+int fp8_requantize_transposed(const uint8_t* q, int64_t ldq, const float* s, int64_t lds,
+                              int64_t rows, int64_t cols,
+                              uint8_t* qT, int64_t ldqT, float* sT, int64_t ldsT, void* stream) {
+    return requantize_impl(q, ldq, s, lds, rows, cols, nullptr, 0, qT, ldqT, sT, ldsT, stream);
+}
+
+int fp8_requantize_transposed_grouped(const uint8_t* q, int64_t ldq, const float* s, int64_t lds,
+                                      int64_t rows, int64_t cols, const int32_t* offsets, int64_t E,
+                                      uint8_t* qT, int64_t ldqT, float* sT, int64_t ldsT, void* stream) {
+    FP8B_TRY(check_offsets(offsets, E));
+    return requantize_impl(q, ldq, s, lds, rows, cols, offsets, E, qT, ldqT, sT, ldsT, stream);
+}
+
 int fp8b_validate_gemm(int op, const void* a, int64_t lda, const void* sa, int64_t ldsa,
                        const void* b, int64_t ldb, const void* sb, int64_t ldsb,
                        const void* out, int out_dtype, int64_t ldo, int beta,

@@ -32,6 +32,12 @@ hipError_t launch_quant_cols(const void* x, bool in_bf16, int64_t rows, int64_t 
                              uint8_t* q, int64_t ldq, float* s, int64_t lds,
                              bool pow2, uint8_t* e8T, int64_t ldeT, uint8_t* e8, int64_t lde, hipStream_t st);
 
+// Token-axis quantization of saved 1x128 FP8 data (codes q, scales s):
+// each element dequantized as fl32(E4M3(q) * s), then as launch_quant_cols.
+hipError_t launch_requant_cols(const uint8_t* q, int64_t ldq, const float* s, int64_t lds,
+                               int64_t rows, int64_t cols, const int32_t* offsets, int64_t E,
+                               uint8_t* qT, int64_t ldqT, float* sT, int64_t ldsT, hipStream_t st);
+
 // Elementwise codec access.
 hipError_t launch_encode(const float* x, const float* s, int64_t n, uint8_t* out, hipStream_t st);
 

@@ -91,6 +91,7 @@ struct QuantTileArgs {
     const int32_t* offsets; int64_t E;
     uint8_t* q; int64_t ldq; float* s; int64_t lds;
     uint8_t* qT; int64_t ldqT; float* sT; int64_t ldsT;
+    const float* xs; int64_t ldxs;  // FP8 input (requantization): 1x128 scales of x's codes
     uint8_t* e8; int64_t lde;       // power-of-two scales: E8M0 bytes of q's groups (nullable)
     uint8_t* e8T; int64_t ldeT;     // and of qT's groups (nullable)
     int64_t col_tiles;
@@ -101,6 +102,15 @@ struct QuantTileArgs {
 template <typename T> struct RawTile;
 template <> struct RawTile<uint16_t> { uint4 w[8]; };
 template <> struct RawTile<float> { uint4 w[16]; };
+// FP8 codes and their row scales, as loaded: masking of rows past the tile
+// and columns past `cols` waits for unpack_row, so that the loads of the
+// next tile stay in flight while this one is quantized.
+template <> struct RawTile<uint8_t> {
+    uint2 w[8];
+    float s[8];
+    uint32_t klo, khi;      // byte mask of the columns inside `cols`
+    uint32_t rows;          // bit p: row p lies inside the tile
+};
 
 __device__ __forceinline__ void load_raw_row(const uint16_t* p, int valid, RawTile<uint16_t>& rt, int i) {
     if (valid == 8) {
@@ -132,6 +142,20 @@ __device__ __forceinline__ void unpack_row(const RawTile<uint16_t>& rt, int i, f
     v[2] = __uint_as_float(w.y << 16); v[3] = __uint_as_float(w.y & 0xFFFF0000u);
     v[4] = __uint_as_float(w.z << 16); v[5] = __uint_as_float(w.z & 0xFFFF0000u);
     v[6] = __uint_as_float(w.w << 16); v[7] = __uint_as_float(w.w & 0xFFFF0000u);
+}
+
+// fl32(E4M3(code) * s): the hardware conversion decodes exactly, one
+// binary32 multiply applies the group scale.
+__device__ __forceinline__ void unpack_row(const RawTile<uint8_t>& rt, int i, float v[8]) {
+    const bool in = (rt.rows >> i) & 1u;
+    const uint2 w = make_uint2(rt.w[i].x & (in ? rt.klo : 0u), rt.w[i].y & (in ? rt.khi : 0u));
+    const float sc = rt.s[i];                          // finite: read from a row of the input
+    const auto a = __builtin_amdgcn_cvt_pk_f32_fp8((int)w.x, false);
+    const auto b = __builtin_amdgcn_cvt_pk_f32_fp8((int)w.x, true);
+    const auto c = __builtin_amdgcn_cvt_pk_f32_fp8((int)w.y, false);
+    const auto d = __builtin_amdgcn_cvt_pk_f32_fp8((int)w.y, true);
+    v[0] = a[0] * sc; v[1] = a[1] * sc; v[2] = b[0] * sc; v[3] = b[1] * sc;
+    v[4] = c[0] * sc; v[5] = c[1] * sc; v[6] = d[0] * sc; v[7] = d[1] * sc;
 }
 
 __device__ __forceinline__ void unpack_row(const RawTile<float>& rt, int i, float v[8]) {
@@ -201,6 +225,28 @@ __device__ __forceinline__ TileAt locate_tile(const QuantTileArgs& A, int64_t k,
     at.b = at.a + 128 < hi ? at.a + 128 : hi;
     at.pos = cur.P + 128 * g;
     return at;
+}
+
+// FP8 input: 8 codes per row (always inside the 128-padded row) and the row's
+// scale of this column tile.  A row past the tile reads the tile's first
+// row instead; unpack_row turns it, and codes past `cols`, into zeros.
+__device__ __forceinline__ void load_tile(const QuantTileArgs& A, const TileAt& at, int rg, int cg,
+                                          RawTile<uint8_t>& raw) {
+    const uint8_t* x = static_cast<const uint8_t*>(A.x);
+    const int64_t c0 = at.cb + cg * 8;
+    const int cvalid = clamp_valid(A.cols - c0);
+    raw.klo = cvalid >= 4 ? ~0u : (1u << (8 * cvalid)) - 1u;
+    raw.khi = cvalid >= 8 ? ~0u : (cvalid <= 4 ? 0u : (1u << (8 * (cvalid - 4))) - 1u);
+    raw.rows = 0;
+#pragma unroll
+    for (int p = 0; p < 8; ++p) {
+        const int64_t r = at.a + rg * 8 + p;
+        const bool in = r < at.b;
+        const int64_t rr = in ? r : at.a;
+        raw.rows |= (in ? 1u : 0u) << p;
+        raw.w[p] = *reinterpret_cast<const uint2*>(x + rr * A.ldx + c0);
+        raw.s[p] = A.xs[rr * A.ldxs + at.ct];
+    }
 }
 
 template <typename T>
@@ -277,19 +323,19 @@ __global__ __launch_bounds__(256, 2) void k_quant_tiles(QuantTileArgs A) {
     int64_t k = blockIdx.x;
     TileAt at = locate_tile(A, k, cur);
     RawTile<T> raw;
-    if (at.valid) load_tile<T>(A, at, rg, cg, raw);
+    if (at.valid) load_tile(A, at, rg, cg, raw);
     lds_barrier();
 
     for (; k < A.tiles; k += gridDim.x) {
         const TileAt nx = locate_tile(A, k + gridDim.x, cur);
         if (!at.valid) {                                           // (grouped) a tile past an expert's end
-            if (nx.valid) load_tile<T>(A, nx, rg, cg, raw);
+            if (nx.valid) load_tile(A, nx, rg, cg, raw);
             at = nx;
             continue;
         }
         TileVals<T> v;
         v.set(raw);
-        if (nx.valid) load_tile<T>(A, nx, rg, cg, raw);            // next tile, while this one is quantized
+        if (nx.valid) load_tile(A, nx, rg, cg, raw);            // next tile, while this one is quantized
 
         uint32_t lo[8], hi[8];
         if (MODE == QT_WEIGHT) {
@@ -530,6 +576,23 @@ hipError_t launch_quant_cols(const void* x, bool in_bf16, int64_t rows, int64_t 
     A.tiles = ((rows + 127) / 128 + A.E) * A.col_tiles;
     return q != nullptr ? launch_tiles<QT_COLS_ROWS>(in_bf16, pow2, A, st)
                         : launch_tiles<QT_COLS>(in_bf16, pow2, A, st);
+}
+
+hipError_t launch_requant_cols(const uint8_t* q, int64_t ldq, const float* s, int64_t lds,
+                               int64_t rows, int64_t cols, const int32_t* offsets, int64_t E,
+                               uint8_t* qT, int64_t ldqT, float* sT, int64_t ldsT, hipStream_t st) {
+    if (rows == 0 || cols == 0) return hipSuccess;
+    QuantTileArgs A{};
+    A.x = q; A.rows = rows; A.cols = cols; A.ldx = ldq;
+    A.xs = s; A.ldxs = lds;
+    A.offsets = offsets; A.E = offsets ? E : 0;
+    A.qT = qT; A.ldqT = ldqT; A.sT = sT; A.ldsT = ldsT;
+    A.col_tiles = (cols + 127) / 128;
+    A.tiles = ((rows + 127) / 128 + A.E) * A.col_tiles;
+    const int64_t blocks = tile_grid(A.tiles);
+    if (blocks <= 0) return hipSuccess;
+    k_quant_tiles<uint8_t, QT_COLS, false><<<dim3((unsigned)blocks), 256, 0, st>>>(A);
+    return hipGetLastError();
 }
 
 hipError_t launch_encode(const float* x, const float* s, int64_t n, uint8_t* out, hipStream_t st) {

@@ -135,6 +135,26 @@ FP8B_API int fp8_quantize_transposed_grouped(const void* x, int xt, int64_t rows
                                     uint8_t* qT, int64_t ldqT, float* sT, int64_t ldsT,
                                     uint8_t* q, int64_t ldq, float* s, int64_t lds, void* stream);
 
+/* Token-axis requantization of saved FP8 activations (the flow the Jet-RL
+ * pages attribute to DeepSeek-V3, which keeps only the FP8 copy of X and
+ * forms WGrad's X^T from it).  Input: R1 output, codes q (rows x ldq bytes,
+ * 1x128 groups along the contiguous axis, cols real columns; bytes past
+ * cols are ignored) and scales s (rows x lds fp32).  Each element is
+ * dequantized as fl32(E4M3(q) * s) (one binary32 multiply; the pages leave
+ * the precision open) and the result is quantized exactly as by
+ * fp8_quantize_transposed: qT cols x ldqT, sT cols x ldsT, same rules.  The
+ * read is 1 byte (+ 4/128) per element instead of the 2 of a bf16 source;
+ * the price is a second rounding. */
+FP8B_API int fp8_requantize_transposed(const uint8_t* q, int64_t ldq, const float* s, int64_t lds,
+                              int64_t rows, int64_t cols,
+                              uint8_t* qT, int64_t ldqT, float* sT, int64_t ldsT, void* stream);
+
+/* The same with the MoE grouping of fp8_quantize_transposed_grouped (device
+ * offsets, token groups restart at every expert). */
+FP8B_API int fp8_requantize_transposed_grouped(const uint8_t* q, int64_t ldq, const float* s, int64_t lds,
+                                      int64_t rows, int64_t cols, const int32_t* offsets, int64_t E,
+                                      uint8_t* qT, int64_t ldqT, float* sT, int64_t ldsT, void* stream);
+
 /* Power-of-two block scales (the SkyRL section "FP8 quantization with FP32
  * and power-of-two block scales": FP32 scales constrained to powers of two,
  * an exponent-only representation, the only kind Blackwell tensor cores

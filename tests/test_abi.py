@@ -105,3 +105,18 @@ def test_pow2_quantizers_reject_bad_e8m0_buffers_on_host():
     # transposed: a row-wise E8M0 buffer without the row-wise codes
     assert L.fp8_quantize_transposed_pow2(X, 1, 256, 64, 64, Q, 256, S, 2, E, 8,
                                           None, 0, None, 0, E, 4, None) == 1
+
+
+def test_requantizer_rejects_bad_arguments_on_host():
+    """Shape, alignment and stride checks of the requantizer (pointers are
+    never dereferenced: each call fails before any launch, and the empty
+    case launches nothing)."""
+    L = fb.lib()
+    Q, S, QT, ST = 0x100000, 0x200000, 0x300000, 0x400000
+    assert L.fp8_requantize_transposed(Q, 200, S, 2, 4, 256, QT, 128, ST, 2, None) == 2   # ldq < 256
+    assert L.fp8_requantize_transposed(Q + 8, 256, S, 2, 4, 256, QT, 128, ST, 2, None) == 3
+    assert L.fp8_requantize_transposed(Q, 256, S, 1, 4, 256, QT, 128, ST, 2, None) == 2   # lds < 2
+    assert L.fp8_requantize_transposed(Q, 256, S, 2, 4, 256, QT, 128, ST, 0, None) == 2   # ldsT < 1
+    assert L.fp8_requantize_transposed(Q, 256, S, 2, 0, 256, QT, 128, ST, 1, None) == 0   # no rows
+    assert L.fp8_requantize_transposed_grouped(Q, 256, S, 2, 4, 256, None, 2,
+                                               QT, 384, ST, 3, None) == 1                 # NULL offsets
