@@ -323,3 +323,25 @@ def rel_row_error(y_test: np.ndarray, y_ref: np.ndarray) -> float:
     if np.any(nz):
         worst = float(np.max(diff[nz] / norms[nz, None]))
     return worst
+
+
+# ------------------------------------------------ fused producers (f1)
+from .fused import (bf16_rne, bf16_rne_from_f64, bf16_to_f32, rmsnorm_bf16,  # noqa: E402
+                    rmsnorm_rstd, rmsnorm_sumsq, silu_mul_bf16, silu_table)
+
+
+def rmsnorm_quant_1x128(x: np.ndarray, w: np.ndarray, eps: float):
+    """RMSNorm to bf16, then the 1x128 quantizer.  x and w are float32 or
+    bf16 bits.  Returns (q, s, r, y): codes and scales as quant_1x128, the
+    per-row r = fl32(1/sqrt(mean(x^2) + eps)) and the bf16 activation bits."""
+    y, r = rmsnorm_bf16(as_f32(x), as_f32(w), eps)
+    q, s = quant_1x128(y)
+    return q, s, r, y
+
+
+def silu_mul_quant_1x128(gate: np.ndarray, up: np.ndarray):
+    """bf16(bf16(silu(gate)) * up), then the 1x128 quantizer.  gate and up
+    are bf16 bits.  Returns (q, s, a) with a the bf16 activation bits."""
+    a = silu_mul_bf16(gate, up)
+    q, s = quant_1x128(a)
+    return q, s, a
