@@ -50,6 +50,8 @@ def parse():
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-other", action="store_true", help="skip the decode / MXFP8 / MoE kernel timings")
+    ap.add_argument("--only-section", choices=["fused", "other"],
+                    help="time one side section alone and print its JSON (no training step)")
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="rough CPU budget of the oracle baseline sample")
     ap.add_argument("--traffic", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
@@ -143,8 +145,8 @@ def main():
         traffic_summary(*args.traffic)
         return
     if args.gpus != 1:
-        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
-              f"(this build runs on a single MI355X).", file=sys.stderr)
+        print(f"bench.py times one GPU's share of the work; --gpus {args.gpus} is not supported "
+              f"(run it with --gpus 1).", file=sys.stderr)
         sys.exit(2)
 
     import torch
@@ -153,6 +155,10 @@ def main():
 
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    if args.only_section:                        # one side section alone (for kernel traces)
+        fn = {"fused": fused_producers, "other": other_workloads}[args.only_section]
+        print(json.dumps({"section": args.only_section, "result": fn(torch, fb, wl, dev, args.seed)}), flush=True)
+        return
     t0 = time.time()
     w = wl.train(args.seed)
     print(f"[bench] inputs drawn in {time.time() - t0:.1f}s", file=sys.stderr, flush=True)
@@ -324,11 +330,12 @@ def main():
         pow2 = pow2_layer(torch, fb, copies, flops_gemm)
         requant = requant_layer(torch, fb, copies)
 
-    other = None
+    other = fused = None
     if not args.no_other:
         del copies, bufs, b
         torch.cuda.empty_cache()
         other = other_workloads(torch, fb, wl, dev, args.seed)
+        fused = fused_producers(torch, fb, wl, dev, args.seed)
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -347,6 +354,7 @@ def main():
         "measured_ceilings": ceil,
         "pow2_scales_layer": pow2,
         "requant_from_fp8_X": requant,
+        "fused_producers": fused,
         "other_workloads": other,
     }
     print(json.dumps(out), flush=True)
@@ -451,6 +459,44 @@ def requant_layer(torch, fb, copies):
         "kept_bytes": {"bf16_X": 2 * N * C, "fp8_X": N * C + rs},
     }
     del flush
+    return out
+
+
+def fused_producers(torch, fb, wl, dev, seed):
+    """The fused producers of the 1x128 quantizer at the training shape
+    (Qwen3-8B: hidden 4096, intermediate 12288, 8192 tokens), each timed cold
+    against its HBM roofline, beside the unfused pair (torch's bf16 operator
+    writing the activation, then the 1x128 quantizer reading it back)."""
+    N, H, I = 8192, 4096, 12288
+    cd = lambda a, b: (a + b - 1) // b
+    flush = torch.empty(1 << 28, dtype=torch.float32, device=dev).fill_(1.0)
+    rng = wl.rng_for(seed + 11)
+    to = lambda bits: torch.from_numpy(bits).view(torch.bfloat16).to(dev)
+    x = to(wl.normal_bf16(rng, (N, H), 1.0))
+    w = to(wl.f32_to_bf16_bits((1 + 0.1 * rng.standard_normal(H)).astype(np.float32)))
+    gu = to(wl.normal_bf16(rng, (N, 2 * I), 1.0))
+    g, u = gu[:, :I], gu[:, I:]
+    out = {}
+    q, s, r, _ = fb.fp8_rmsnorm_quantize_1x128(x, w, 1e-6, rstd=True)
+    rn_bytes = 2 * N * H + 2 * H + N * H + N * cd(H, 128) * 4 + 4 * N
+    out["rmsnorm_quant"] = report(time_cold(torch, lambda: fb.fp8_rmsnorm_quantize_1x128(
+        x, w, 1e-6, rstd=r, q=q, s=s), flush), rn_bytes)
+
+    def unfused_rn():
+        y = torch.nn.functional.rms_norm(x, (H,), w, eps=1e-6)
+        fb.fp8_quantize_act_1x128(y, q, s)
+    out["rmsnorm_then_quant_unfused"] = report(time_cold(torch, unfused_rn, flush), rn_bytes)
+    qa, sa, _ = fb.fp8_silu_mul_quantize_1x128(g, u)
+    sm_bytes = 2 * 2 * N * I + N * I + N * cd(I, 128) * 4
+    out["silu_mul_quant"] = report(time_cold(torch, lambda: fb.fp8_silu_mul_quantize_1x128(
+        g, u, q=qa, s=sa), flush), sm_bytes)
+
+    def unfused_sm():
+        a = torch.nn.functional.silu(g) * u
+        fb.fp8_quantize_act_1x128(a, qa, sa)
+    out["silu_mul_then_quant_unfused"] = report(time_cold(torch, unfused_sm, flush), sm_bytes)
+    del x, gu, flush
+    torch.cuda.synchronize()
     return out
 
 

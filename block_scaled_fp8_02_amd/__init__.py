@@ -49,6 +49,9 @@ _SIGS = {
                                          _p, _i64, _p, _i64, _p],
     "fp8_quantize_transposed_pow2": [_p, _i32, _i64, _i64, _i64, _p, _i64, _p, _i64, _p, _i64,
                                      _p, _i64, _p, _i64, _p, _i64, _p],
+    "fp8_rmsnorm_quantize_1x128": [_p, _i32, _i64, _i64, _i64, _p, _i32, ctypes.c_float,
+                                   _p, _i64, _p, _i64, _p, _p, _i64, _p],
+    "fp8_silu_mul_quantize_1x128": [_p, _i64, _p, _i64, _i64, _i64, _p, _i64, _p, _i64, _p, _i64, _p],
     "fp8_requantize_transposed": [_p, _i64, _p, _i64, _i64, _i64, _p, _i64, _p, _i64, _p],
     "fp8_requantize_transposed_grouped": [_p, _i64, _p, _i64, _i64, _i64, _p, _i64, _p, _i64, _p, _i64, _p],
     "fp8_gemm_fprop": [_p, _i64, _p, _i64, _p, _i64, _p, _i64, _p, _i32, _i64, _i64, _i64, _i64, _p],
@@ -215,6 +218,48 @@ def fp8_quantize_transposed_grouped(x, offsets, rowwise: bool = False, qT=None, 
           _ptr(q), _ld(q) if q is not None else 0, _ptr(s), _ld(s) if s is not None else 0,
           _stream(x.device))
     return qT, sT, q, s
+
+
+# ------------------------------------------ fused activation producers
+def fp8_rmsnorm_quantize_1x128(x, w, eps: float = 1e-6, rstd: bool = False, y: bool = False, q=None, s=None):
+    """RMSNorm rows of x [rows, cols] (bf16 or fp32) with weight w [cols],
+    rounded to bf16 and quantized 1x128 in one pass -> (q, s, rstd or None,
+    y or None); rstd fp32 [rows] (pass True, or a tensor to fill), y the bf16
+    activation."""
+    _check_2d(x, "x")
+    rows, cols = x.shape
+    if w.dim() != 1 or w.shape[0] != cols or not w.is_contiguous():
+        raise ValueError("w must be a contiguous vector of length cols")
+    q = _new((rows, _rup(cols)), torch.uint8, x.device) if q is None else q
+    s = _new((rows, _cdiv(cols, 128)), torch.float32, x.device) if s is None else s
+    if isinstance(rstd, torch.Tensor):
+        r = rstd
+        if r.dtype != torch.float32 or r.numel() < rows or not r.is_contiguous():
+            raise ValueError("rstd must be a contiguous float32 tensor of at least rows elements")
+    else:
+        r = _new((rows,), torch.float32, x.device) if rstd else None
+    yt = _new_out(rows, cols, torch.bfloat16, x.device) if y else None
+    _call("fp8_rmsnorm_quantize_1x128", _ptr(x), _dtype_code(x), rows, cols, _ld(x),
+          _ptr(w), _dtype_code(w), float(eps), _ptr(q), _ld(q), _ptr(s), _ld(s),
+          _ptr(r), _ptr(yt), _ld(yt) if yt is not None else 0, _stream(x.device))
+    return q, s, r, yt
+
+
+def fp8_silu_mul_quantize_1x128(gate, up, a: bool = False, q=None, s=None):
+    """bf16(bf16(silu(gate)) * up) quantized 1x128 in one pass -> (q, s,
+    a or None); gate and up bf16 [rows, cols] (views of one gate+up matrix
+    are fine), a the bf16 activation."""
+    _check_2d(gate, "gate")
+    _check_2d(up, "up")
+    if gate.shape != up.shape or gate.dtype != torch.bfloat16 or up.dtype != torch.bfloat16:
+        raise ValueError("gate and up must be bf16 tensors of one shape")
+    rows, cols = gate.shape
+    q = _new((rows, _rup(cols)), torch.uint8, gate.device) if q is None else q
+    s = _new((rows, _cdiv(cols, 128)), torch.float32, gate.device) if s is None else s
+    at = _new_out(rows, cols, torch.bfloat16, gate.device) if a else None
+    _call("fp8_silu_mul_quantize_1x128", _ptr(gate), _ld(gate), _ptr(up), _ld(up), rows, cols,
+          _ptr(q), _ld(q), _ptr(s), _ld(s), _ptr(at), _ld(at) if at is not None else 0, _stream(gate.device))
+    return q, s, at
 
 
 # ----------------------------------------- requantization from FP8

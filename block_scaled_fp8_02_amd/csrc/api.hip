@@ -283,6 +283,32 @@ int fp8_requantize_transposed_grouped(const uint8_t* q, int64_t ldq, const float
     return requantize_impl(q, ldq, s, lds, rows, cols, offsets, E, qT, ldqT, sT, ldsT, stream);
 }
 
+int fp8_rmsnorm_quantize_1x128(const void* x, int xt, int64_t rows, int64_t cols, int64_t ldx,
+                               const void* w, int wt, float eps,
+                               uint8_t* q, int64_t ldq, float* s, int64_t lds,
+                               float* rstd, uint16_t* y, int64_t ldy, void* stream) {
+    FP8B_TRY(check_input(x, xt, rows, cols, ldx));
+    if (!(eps > 0.0f) || !(eps < __builtin_inff())) return FP8B_EINVAL;
+    FP8B_TRY(check_input(w, wt, cols > 0 && rows > 0 ? 1 : 0, cols, (cols + 7) / 8 * 8));   // one row: only w's alignment
+    FP8B_TRY(check_codes(q, rows, cols, ldq));
+    FP8B_TRY(check_scales(s, rows, cdiv(cols, 128), lds, 4));
+    if (y != nullptr) FP8B_TRY(check_input(y, FP8B_BF16, rows, cols, ldy));
+    return hip_status(launch_rmsnorm_quant(x, xt == FP8B_BF16, rows, cols, ldx, w, wt == FP8B_BF16, eps,
+                                           q, ldq, s, lds, rstd, y, ldy, static_cast<hipStream_t>(stream)));
+}
+
+int fp8_silu_mul_quantize_1x128(const uint16_t* gate, int64_t ldg, const uint16_t* up, int64_t ldu,
+                                int64_t rows, int64_t cols, uint8_t* q, int64_t ldq, float* s, int64_t lds,
+                                uint16_t* a, int64_t lda, void* stream) {
+    FP8B_TRY(check_input(gate, FP8B_BF16, rows, cols, ldg));
+    FP8B_TRY(check_input(up, FP8B_BF16, rows, cols, ldu));
+    FP8B_TRY(check_codes(q, rows, cols, ldq));
+    FP8B_TRY(check_scales(s, rows, cdiv(cols, 128), lds, 4));
+    if (a != nullptr) FP8B_TRY(check_input(a, FP8B_BF16, rows, cols, lda));
+    return hip_status(launch_silu_mul_quant(gate, ldg, up, ldu, rows, cols, q, ldq, s, lds, a, lda,
+                                            static_cast<hipStream_t>(stream)));
+}
+
 int fp8b_validate_gemm(int op, const void* a, int64_t lda, const void* sa, int64_t ldsa,
                        const void* b, int64_t ldb, const void* sb, int64_t ldsb,
                        const void* out, int out_dtype, int64_t ldo, int beta,

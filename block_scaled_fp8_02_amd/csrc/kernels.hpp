@@ -38,6 +38,15 @@ hipError_t launch_requant_cols(const uint8_t* q, int64_t ldq, const float* s, in
                                int64_t rows, int64_t cols, const int32_t* offsets, int64_t E,
                                uint8_t* qT, int64_t ldqT, float* sT, int64_t ldsT, hipStream_t st);
 
+// Fused producers of the 1x128 activation quantizer (fused.hip).
+hipError_t launch_rmsnorm_quant(const void* x, bool x_bf16, int64_t rows, int64_t cols, int64_t ldx,
+                                const void* w, bool w_bf16, float eps,
+                                uint8_t* q, int64_t ldq, float* s, int64_t lds,
+                                float* rstd, uint16_t* y, int64_t ldy, hipStream_t st);
+hipError_t launch_silu_mul_quant(const uint16_t* gate, int64_t ldg, const uint16_t* up, int64_t ldu,
+                                 int64_t rows, int64_t cols, uint8_t* q, int64_t ldq, float* s, int64_t lds,
+                                 uint16_t* a, int64_t lda, hipStream_t st);
+
 // Elementwise codec access.
 hipError_t launch_encode(const float* x, const float* s, int64_t n, uint8_t* out, hipStream_t st);
 

@@ -135,6 +135,42 @@ FP8B_API int fp8_quantize_transposed_grouped(const void* x, int xt, int64_t rows
                                     uint8_t* qT, int64_t ldqT, float* sT, int64_t ldsT,
                                     uint8_t* q, int64_t ldq, float* s, int64_t lds, void* stream);
 
+/* Fused producers of the 1x128 activation quantizer.  The Jet-RL notes
+ * (section 3.4, the quantization kernels and the per-block walk-through of
+ * the attention and MLP blocks) fuse the activation quantizer into the
+ * operator that produces the activation, so the bf16 activation is not
+ * written to HBM and read back.  Both calls produce exactly the codes and
+ * scales that fp8_quantize_act_1x128 gives for the bf16 activation of the
+ * unfused operator, with that operator's arithmetic defined as follows (the
+ * pages leave it open).  Outputs q, s as fp8_quantize_act_1x128. */
+
+/* RMSNorm + 1x128.  x: rows x ldx of dtype xt; w: cols weights of dtype wt
+ * (16-byte aligned); eps > 0 and finite.  Per row: ss = sum of x_j^2, exact
+ * and rounded once to binary64; r = fl32(1 / sqrt(ss / cols + eps)), each
+ * step a binary64 operation; y_j = bf16(fl32(fl32(x_j * r) * w_j)) (round to
+ * nearest even); then the 1x128 quantizer on y.  ss is the exact sum rounded
+ * once whenever the row's nonzero magnitudes lie within a factor 2^30 of
+ * each other (double-double sum); otherwise it is within 2^-100 relative.  Optional outputs (NULL to skip): rstd
+ * [rows] fp32 = r (what the backward pass needs), y rows x ldy bf16 (16-byte
+ * aligned, ldy * 2 a multiple of 16).  The caller keeps |w| * sqrt(cols)
+ * below the bf16 maximum.  Errors: FP8B_EINVAL (NULL, bad dtype, eps <= 0
+ * or not finite), FP8B_ESHAPE, FP8B_EALIGN, FP8B_EHIP. */
+FP8B_API int fp8_rmsnorm_quantize_1x128(const void* x, int xt, int64_t rows, int64_t cols, int64_t ldx,
+                               const void* w, int wt, float eps,
+                               uint8_t* q, int64_t ldq, float* s, int64_t lds,
+                               float* rstd, uint16_t* y, int64_t ldy, void* stream);
+
+/* SiLU(gate) * up + 1x128 (the gated MLP's down-projection input).  gate and
+ * up: rows x cols bf16 with strides ldg, ldu (for a fused gate+up GEMM
+ * output H [rows x 2I]: gate = H, up = H + I, both strides 2I).  Per
+ * element: s = bf16(silu(g)), silu(g) = g / (1 + e^-g) rounded once from its
+ * exact value; a = bf16(fl32(s * u)); then the 1x128 quantizer on a.
+ * Optional output a (NULL to skip): rows x lda bf16, the activation the
+ * backward pass of the down projection may keep.  Errors as above. */
+FP8B_API int fp8_silu_mul_quantize_1x128(const uint16_t* gate, int64_t ldg, const uint16_t* up, int64_t ldu,
+                                int64_t rows, int64_t cols, uint8_t* q, int64_t ldq, float* s, int64_t lds,
+                                uint16_t* a, int64_t lda, void* stream);
+
 /* Token-axis requantization of saved FP8 activations (the flow the Jet-RL
  * pages attribute to DeepSeek-V3, which keeps only the FP8 copy of X and
  * forms WGrad's X^T from it).  Input: R1 output, codes q (rows x ldq bytes,

@@ -120,3 +120,23 @@ def test_requantizer_rejects_bad_arguments_on_host():
     assert L.fp8_requantize_transposed(Q, 256, S, 2, 0, 256, QT, 128, ST, 1, None) == 0   # no rows
     assert L.fp8_requantize_transposed_grouped(Q, 256, S, 2, 4, 256, None, 2,
                                                QT, 384, ST, 3, None) == 1                 # NULL offsets
+
+
+def test_fused_producers_reject_bad_arguments_on_host():
+    """eps, alignment and shape checks of the fused RMSNorm and SiLU*up
+    quantizers (pointers never dereferenced; the empty call launches nothing)."""
+    L = fb.lib()
+    X, W, Q, S = 0x100000, 0x200000, 0x300000, 0x400000
+    assert L.fp8_rmsnorm_quantize_1x128(X, 1, 4, 256, 256, W, 1, 0.0, Q, 256, S, 2, None, None, 0, None) == 1
+    assert L.fp8_rmsnorm_quantize_1x128(X, 1, 4, 256, 256, W, 1, float("inf"), Q, 256, S, 2,
+                                        None, None, 0, None) == 1
+    assert L.fp8_rmsnorm_quantize_1x128(X, 1, 4, 256, 256, W + 2, 1, 1e-6, Q, 256, S, 2,
+                                        None, None, 0, None) == 3
+    assert L.fp8_rmsnorm_quantize_1x128(X, 1, 4, 256, 256, W, 7, 1e-6, Q, 256, S, 2, None, None, 0, None) == 1
+    assert L.fp8_rmsnorm_quantize_1x128(X, 1, 4, 256, 256, W, 1, 1e-6, Q, 200, S, 2, None, None, 0, None) == 2
+    assert L.fp8_rmsnorm_quantize_1x128(X, 1, 4, 256, 256, W, 1, 1e-6, Q, 256, S, 2, None, X, 100, None) == 2
+    assert L.fp8_rmsnorm_quantize_1x128(X, 1, 0, 256, 256, W, 1, 1e-6, Q, 256, S, 2, None, None, 0, None) == 0
+    assert L.fp8_silu_mul_quantize_1x128(X, 256, W, 256, 4, 256, Q, 256, S, 1, None, 0, None) == 2
+    assert L.fp8_silu_mul_quantize_1x128(X + 4, 256, W, 256, 4, 256, Q, 256, S, 2, None, 0, None) == 3
+    assert L.fp8_silu_mul_quantize_1x128(X, 100, W, 256, 4, 256, Q, 256, S, 2, None, 0, None) == 2
+    assert L.fp8_silu_mul_quantize_1x128(X, 256, W, 256, 0, 256, Q, 256, S, 2, None, 0, None) == 0
