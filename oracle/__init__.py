@@ -345,3 +345,29 @@ def silu_mul_quant_1x128(gate: np.ndarray, up: np.ndarray):
     a = silu_mul_bf16(gate, up)
     q, s = quant_1x128(a)
     return q, s, a
+
+
+# ------------------------------------- dequantized backward operands (f4)
+def dequant_bf16_rows(q: np.ndarray, s: np.ndarray, cols: int, group: int = 128) -> np.ndarray:
+    """bf16 bits of fl32(E4M3(q) * s) for codes grouped along the rows
+    (1x128 when group = 128): the exact product (in binary64) rounded to
+    binary32, then to bf16 with nearest-even."""
+    with np.errstate(over="ignore"):
+        return bf16_rne(deq_rowgroups(q, s, cols, group).astype(np.float32))
+
+
+def dequant_bf16_128x128(q: np.ndarray, s: np.ndarray, D: int, C: int) -> np.ndarray:
+    """bf16 bits of fl32(E4M3(q) * s_block) for 128x128-block codes [D, C]."""
+    with np.errstate(over="ignore"):
+        return bf16_rne(deq_128x128(q, s, D, C).astype(np.float32))
+
+
+def dequant_bf16_mx(q: np.ndarray, e: np.ndarray, cols: int) -> np.ndarray:
+    """bf16 bits of fl32(E4M3(q) * 2^(e - 127)) for MX 1x32 codes."""
+    with np.errstate(over="ignore"):
+        return bf16_rne(deq_mx(q, e, cols).astype(np.float32))
+
+
+def bf16_matmul(A_bits: np.ndarray, B_bits: np.ndarray) -> np.ndarray:
+    """A [M, K] @ B [K, N] of bf16 bit arrays, in binary64."""
+    return matmul_f64(bf16_to_f32(A_bits).astype(np.float64), bf16_to_f32(B_bits).astype(np.float64))
