@@ -325,10 +325,11 @@ def main():
             tw[name] = {"error": str(ex)[:120]}
     ceil["fp8_tensorwise_hipblaslt"] = tw
 
-    pow2 = requant = None
+    pow2 = requant = deqbwd = None
     if not args.no_other:
         pow2 = pow2_layer(torch, fb, copies, flops_gemm)
         requant = requant_layer(torch, fb, copies)
+        deqbwd = dequant_backward(torch, fb, copies, flops_gemm)
 
     other = fused = None
     if not args.no_other:
@@ -355,6 +356,7 @@ def main():
         "pow2_scales_layer": pow2,
         "requant_from_fp8_X": requant,
         "fused_producers": fused,
+        "dequantized_backward": deqbwd,
         "other_workloads": other,
     }
     print(json.dumps(out), flush=True)
@@ -459,6 +461,58 @@ def requant_layer(torch, fb, copies):
         "kept_bytes": {"bf16_X": 2 * N * C, "fp8_X": N * C + rs},
     }
     del flush
+    return out
+
+
+def dequant_backward(torch, fb, copies, flops_gemm):
+    """The training layer's backward in the dequantized mode: DGrad and
+    WGrad as bf16 GEMMs (hipBLASLt) on the forward's FP8 W and X codes
+    dequantized to bf16 (each entry point times its dequantization and its
+    GEMM), the dequantization kernels alone, and the bytes each mode keeps
+    between the forward and the backward pass.  Warm operands, 10 launches."""
+    Xd, Wd, Gd = copies[0]
+    N, C = Xd.shape
+    D = Wd.shape[0]
+    cd = lambda a, b: (a + b - 1) // b
+    xq, xs = fb.fp8_quantize_act_1x128(Xd)
+    wq, ws, _ = fb.fp8_quantize_weight_128x128(Wd, transpose=False)
+    bf = dict(dtype=torch.bfloat16, device=Xd.device)
+    workW, workX = torch.empty((D, C), **bf), torch.empty((N, C), **bf)
+    dx, dw = torch.empty((N, C), **bf), torch.empty((D, C), **bf)
+    runs = {
+        "dequant_W": (lambda: fb.fp8_dequantize_bf16(wq, ws, fb.FP8B_SCALE_BLOCKS_128X128, C, out=workW),
+                      D * C + cd(D, 128) * cd(C, 128) * 4 + 2 * D * C, None),
+        "dequant_X": (lambda: fb.fp8_dequantize_bf16(xq, xs, fb.FP8B_SCALE_ROWS_1X128, C, out=workX),
+                      N * C + N * cd(C, 128) * 4 + 2 * N * C, None),
+        "dgrad": (lambda: fb.fp8_dequant_gemm_dgrad(Gd, wq, ws, fb.FP8B_SCALE_BLOCKS_128X128, N, D, C,
+                                                    dx=dx, work=workW), None, flops_gemm),
+        "wgrad": (lambda: fb.fp8_dequant_gemm_wgrad(Gd, xq, xs, fb.FP8B_SCALE_ROWS_1X128, N, D, C,
+                                                    dw=dw, work=workX), None, flops_gemm),
+    }
+    out = {}
+    for name, (fn, nbytes, flops) in runs.items():
+        for _ in range(2):
+            fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(10):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        t = e0.elapsed_time(e1) * 1e-3 / 10
+        ent = {"us": round(t * 1e6, 2)}
+        if nbytes:
+            ent["gbs"] = round(nbytes / t / 1e9, 1)
+            ent["frac_hbm"] = round(nbytes / t / 1e9 / PEAK_HBM_GBS, 4)
+        if flops:
+            ent["tflops"] = round(flops / t / 1e12, 1)
+            ent["frac_bf16_peak"] = round(flops / t / 1e12 / PEAK_BF16_TFLOPS, 4)
+        out[name] = ent
+    fp8_x = N * C + N * cd(C, 128) * 4
+    out["kept_bytes"] = {"fp8_backward": 2 * fp8_x, "dequantized_backward": fp8_x,
+                         "dequantized_transient_workspace": 2 * N * C}
+    del workW, workX, dx, dw
     return out
 
 

@@ -20,6 +20,9 @@ LIB_PATH = os.path.join(_HERE, "libfp8blk.so")
 
 FP8B_F32 = 0
 FP8B_BF16 = 1
+FP8B_SCALE_ROWS_1X128 = 0
+FP8B_SCALE_BLOCKS_128X128 = 1
+FP8B_SCALE_MX_1X32 = 2
 _STATUS = {0: "ok", 1: "invalid argument", 2: "invalid shape", 3: "misaligned",
            4: "unsupported", 5: "HIP launch error"}
 
@@ -53,6 +56,10 @@ _SIGS = {
                                    _p, _i64, _p, _i64, _p, _p, _i64, _p],
     "fp8_silu_mul_quantize_1x128": [_p, _i64, _p, _i64, _i64, _i64, _p, _i64, _p, _i64, _p, _i64, _p],
     "fp8_requantize_transposed": [_p, _i64, _p, _i64, _i64, _i64, _p, _i64, _p, _i64, _p],
+    "fp8_dequantize_bf16": [_p, _i64, _p, _i64, _i32, _i64, _i64, _p, _i64, _p],
+    "fp8_dequant_gemm_dgrad": [_p, _i64, _p, _i64, _p, _i64, _i32, _i64, _i64, _i64, _p, _i64, _p, _i64, _p],
+    "fp8_dequant_gemm_wgrad": [_p, _i64, _p, _i64, _p, _i64, _i32, _i64, _i64, _i64, _p, _i32, _i64, _i32,
+                               _p, _i64, _p],
     "fp8_requantize_transposed_grouped": [_p, _i64, _p, _i64, _i64, _i64, _p, _i64, _p, _i64, _p, _i64, _p],
     "fp8_gemm_fprop": [_p, _i64, _p, _i64, _p, _i64, _p, _i64, _p, _i32, _i64, _i64, _i64, _i64, _p],
     "fp8_gemm_dgrad": [_p, _i64, _p, _i64, _p, _i64, _p, _i64, _p, _i32, _i64, _i64, _i64, _i64, _p],
@@ -260,6 +267,40 @@ def fp8_silu_mul_quantize_1x128(gate, up, a: bool = False, q=None, s=None):
     _call("fp8_silu_mul_quantize_1x128", _ptr(gate), _ld(gate), _ptr(up), _ld(up), rows, cols,
           _ptr(q), _ld(q), _ptr(s), _ld(s), _ptr(at), _ld(at) if at is not None else 0, _stream(gate.device))
     return q, s, at
+
+
+# ------------------------------------------- dequantized backward (f4)
+def fp8_dequantize_bf16(q, s, kind: int, cols: int, out=None):
+    """bf16(fl32(E4M3(q) * scale)) -> out bf16 [rows, cols]; kind is one of
+    FP8B_SCALE_ROWS_1X128, FP8B_SCALE_BLOCKS_128X128, FP8B_SCALE_MX_1X32."""
+    _check_2d(q, "q")
+    rows = q.shape[0]
+    out = _new_out(rows, cols, torch.bfloat16, q.device) if out is None else out
+    _call("fp8_dequantize_bf16", _ptr(q), _ld(q), _ptr(s), _ld(s), int(kind), rows, cols,
+          _ptr(out), _ld(out), _stream(q.device))
+    return out
+
+
+def fp8_dequant_gemm_dgrad(dy, wq, ws, wkind: int, N: int, D: int, C: int, dx=None, work=None):
+    """dX = dY W^ in bf16 (hipBLASLt) with W^ the dequantized weight codes;
+    work (D x C bf16) receives W^."""
+    dx = _new_out(N, C, torch.bfloat16, dy.device) if dx is None else dx
+    work = _new_out(D, C, torch.bfloat16, dy.device) if work is None else work
+    _call("fp8_dequant_gemm_dgrad", _ptr(dy), _ld(dy), _ptr(wq), _ld(wq), _ptr(ws), _ld(ws), int(wkind),
+          N, D, C, _ptr(dx), _ld(dx), _ptr(work), _ld(work), _stream(dy.device))
+    return dx
+
+
+def fp8_dequant_gemm_wgrad(dy, xq, xs, xkind: int, N: int, D: int, C: int, dw=None,
+                           out_dtype=torch.bfloat16, beta: int = 0, work=None):
+    """dW (+)= dY^T X^ in bf16 (hipBLASLt) with X^ the dequantized activation
+    codes; work (N x C bf16) receives X^."""
+    dw = _new_out(D, C, out_dtype, dy.device) if dw is None else dw
+    work = _new_out(N, C, torch.bfloat16, dy.device) if work is None else work
+    _call("fp8_dequant_gemm_wgrad", _ptr(dy), _ld(dy), _ptr(xq), _ld(xq), _ptr(xs), _ld(xs), int(xkind),
+          N, D, C, _ptr(dw), _out_dtype_code(dw.dtype), _ld(dw), int(beta), _ptr(work), _ld(work),
+          _stream(dy.device))
+    return dw
 
 
 # ----------------------------------------- requantization from FP8

@@ -309,6 +309,84 @@ int fp8_silu_mul_quantize_1x128(const uint16_t* gate, int64_t ldg, const uint16_
                                             static_cast<hipStream_t>(stream)));
 }
 
+static int check_fp8_operand(const uint8_t* q, int64_t ldq, const void* sc, int64_t lds, int kind,
+                             int64_t rows, int64_t cols) {
+    if (kind < FP8B_SCALE_ROWS_1X128 || kind > FP8B_SCALE_MX_1X32) return FP8B_EINVAL;
+    FP8B_TRY(check_codes(q, rows, cols, ldq));
+    if (kind == FP8B_SCALE_ROWS_1X128) return check_scales(sc, rows, cdiv(cols, 128), lds, 4);
+    if (kind == FP8B_SCALE_BLOCKS_128X128) return check_scales(sc, cdiv(rows, 128), cdiv(cols, 128), lds, 4);
+    return check_scales(sc, rows, rup128(cols) / 32, lds, 1);
+}
+
+// A bf16 or fp32 matrix only hipBLASLt touches: element alignment, any
+// leading dimension >= cols.
+static int check_blas_matrix(const void* p, int dt, int64_t rows, int64_t cols, int64_t ld) {
+    if (!dtype_ok(dt)) return FP8B_EINVAL;
+    if (rows < 0 || cols < 0 || ld < cols) return FP8B_ESHAPE;
+    if (rows == 0 || cols == 0) return FP8B_OK;
+    if (p == nullptr) return FP8B_EINVAL;
+    if (!aligned(p, (uintptr_t)esize(dt))) return FP8B_EALIGN;
+    return FP8B_OK;
+}
+
+static int lt_status_code(hipError_t e, int lt) {
+    if (lt != 0) {
+        g_last_hip_error = -lt;                 // hipBLASLt status, negated
+        return FP8B_EHIP;
+    }
+    return hip_status(e);
+}
+
+int fp8_dequantize_bf16(const uint8_t* q, int64_t ldq, const void* sc, int64_t lds, int kind,
+                        int64_t rows, int64_t cols, uint16_t* out, int64_t ldo, void* stream) {
+    FP8B_TRY(check_fp8_operand(q, ldq, sc, lds, kind, rows, cols));
+    FP8B_TRY(check_input(out, FP8B_BF16, rows, cols, ldo));
+    return hip_status(launch_dequant_bf16(q, ldq, sc, lds, kind, rows, cols, out, ldo,
+                                          static_cast<hipStream_t>(stream)));
+}
+
+int fp8_dequant_gemm_dgrad(const uint16_t* dy, int64_t lddy, const uint8_t* wq, int64_t ldwq,
+                           const void* ws, int64_t ldws, int wkind, int64_t N, int64_t D, int64_t C,
+                           uint16_t* dx, int64_t lddx, uint16_t* work, int64_t ldwork, void* stream) {
+    if (wkind != FP8B_SCALE_BLOCKS_128X128 && wkind != FP8B_SCALE_MX_1X32) return FP8B_EINVAL;
+    FP8B_TRY(check_blas_matrix(dy, FP8B_BF16, N, D, lddy));
+    FP8B_TRY(check_fp8_operand(wq, ldwq, ws, ldws, wkind, D, C));
+    FP8B_TRY(check_input(work, FP8B_BF16, D, C, ldwork));
+    FP8B_TRY(check_blas_matrix(dx, FP8B_BF16, N, C, lddx));
+    const hipStream_t st = static_cast<hipStream_t>(stream);
+    if (N == 0 || C == 0) return FP8B_OK;
+    if (D == 0) return hip_status(hipMemset2DAsync(dx, lddx * 2, 0, C * 2, N, st));
+    FP8B_TRY(hip_status(launch_dequant_bf16(wq, ldwq, ws, ldws, wkind, D, C, work, ldwork, st)));
+    int lt = 0;
+    const hipError_t e = lt_gemm(false, false, C, N, D, work, ldwork, dy, lddy, dx, lddx, false, 0.0f, st, &lt);
+    return lt_status_code(e, lt);
+}
+
+int fp8_dequant_gemm_wgrad(const uint16_t* dy, int64_t lddy, const uint8_t* xq, int64_t ldxq,
+                           const void* xs, int64_t ldxs, int xkind, int64_t N, int64_t D, int64_t C,
+                           void* dw, int dwt, int64_t lddw, int beta,
+                           uint16_t* work, int64_t ldwork, void* stream) {
+    if (xkind != FP8B_SCALE_ROWS_1X128 && xkind != FP8B_SCALE_MX_1X32) return FP8B_EINVAL;
+    FP8B_TRY(check_blas_matrix(dy, FP8B_BF16, N, D, lddy));
+    FP8B_TRY(check_fp8_operand(xq, ldxq, xs, ldxs, xkind, N, C));
+    FP8B_TRY(check_input(work, FP8B_BF16, N, C, ldwork));
+    if (beta != 0 && beta != 1) return FP8B_EINVAL;
+    if (beta == 1 && dwt != FP8B_F32) return FP8B_EUNSUPPORTED;
+    FP8B_TRY(check_blas_matrix(dw, dwt, D, C, lddw));
+    const hipStream_t st = static_cast<hipStream_t>(stream);
+    if (D == 0 || C == 0) return FP8B_OK;
+    if (N == 0) {
+        if (beta) return FP8B_OK;
+        return hip_status(hipMemset2DAsync(dw, lddw * (dwt == FP8B_F32 ? 4 : 2), 0,
+                                           C * (dwt == FP8B_F32 ? 4 : 2), D, st));
+    }
+    FP8B_TRY(hip_status(launch_dequant_bf16(xq, ldxq, xs, ldxs, xkind, N, C, work, ldwork, st)));
+    int lt = 0;
+    const hipError_t e = lt_gemm(false, true, C, D, N, work, ldwork, dy, lddy, dw, lddw, dwt == FP8B_F32,
+                                 beta ? 1.0f : 0.0f, st, &lt);
+    return lt_status_code(e, lt);
+}
+
 int fp8b_validate_gemm(int op, const void* a, int64_t lda, const void* sa, int64_t ldsa,
                        const void* b, int64_t ldb, const void* sb, int64_t ldsb,
                        const void* out, int out_dtype, int64_t ldo, int beta,

@@ -47,6 +47,15 @@ hipError_t launch_silu_mul_quant(const uint16_t* gate, int64_t ldg, const uint16
                                  int64_t rows, int64_t cols, uint8_t* q, int64_t ldq, float* s, int64_t lds,
                                  uint16_t* a, int64_t lda, hipStream_t st);
 
+// Dequantized-backward mode (dequant.hip): bf16 dequantization of FP8 codes
+// (kind 0: 1x128 row groups, 1: 128x128 blocks, 2: MX 1x32 E8M0) and the
+// plain bf16 GEMM through hipBLASLt (column-major, fp32 accumulation).
+hipError_t launch_dequant_bf16(const uint8_t* q, int64_t ldq, const void* s, int64_t lds, int kind,
+                               int64_t rows, int64_t cols, uint16_t* out, int64_t ldo, hipStream_t st);
+hipError_t lt_gemm(bool ta, bool tb, int64_t m, int64_t n, int64_t k,
+                   const uint16_t* A, int64_t lda, const uint16_t* B, int64_t ldb,
+                   void* D, int64_t ldd, bool out_f32, float beta, hipStream_t st, int* lt_status);
+
 // Elementwise codec access.
 hipError_t launch_encode(const float* x, const float* s, int64_t n, uint8_t* out, hipStream_t st);
 

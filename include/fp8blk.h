@@ -59,7 +59,7 @@ enum fp8b_status_code {
     FP8B_EINVAL = 1,       /* null pointer where one is required, bad enum value */
     FP8B_ESHAPE = 2,       /* dimension < 0, leading dimension too small, bad group count */
     FP8B_EALIGN = 3,       /* pointer or leading dimension not 16-byte aligned */
-    FP8B_EUNSUPPORTED = 4, /* valid request this build does not implement */
+    FP8B_EUNSUPPORTED = 4, /* valid request the library does not implement */
     FP8B_EHIP = 5          /* HIP launch error; see fp8b_last_hip_error() */
 };
 
@@ -68,13 +68,21 @@ enum fp8b_dtype {
     FP8B_BF16 = 1          /* bfloat16 (upper half of binary32), stored as uint16 */
 };
 
+enum fp8b_scale_kind {     /* scale layout of an FP8 operand (codes rows x ldq, K padded to 128) */
+    FP8B_SCALE_ROWS_1X128 = 0,     /* fp32 s[row][k/128] (fp8_quantize_act_1x128) */
+    FP8B_SCALE_BLOCKS_128X128 = 1, /* fp32 s[row/128][k/128] (fp8_quantize_weight_128x128) */
+    FP8B_SCALE_MX_1X32 = 2         /* E8M0 byte e[row][k/32], scale 2^(e-127), row stride >= round_up(K,128)/32 */
+};
+
 /* Version of this ABI (incremented on any incompatible change). */
 FP8B_API int fp8b_abi_version(void);
 
 /* Static, human-readable text for a status code. */
 FP8B_API const char* fp8b_status_string(int status);
 
-/* HIP error code of the last FP8B_EHIP returned on the calling thread. */
+/* HIP error code of the last FP8B_EHIP returned on the calling thread (for
+ * the dequantized-backward GEMMs, a failing hipBLASLt status is returned
+ * negated). */
 FP8B_API int fp8b_last_hip_error(void);
 
 /* ------------------------------------------------------------------ */
@@ -190,6 +198,38 @@ FP8B_API int fp8_requantize_transposed(const uint8_t* q, int64_t ldq, const floa
 FP8B_API int fp8_requantize_transposed_grouped(const uint8_t* q, int64_t ldq, const float* s, int64_t lds,
                                       int64_t rows, int64_t cols, const int32_t* offsets, int64_t E,
                                       uint8_t* qT, int64_t ldqT, float* sT, int64_t ldsT, void* stream);
+
+/* Dequantized-backward mode (the Miles MXFP8/NVFP4 blog's backward-mode
+ * section): the backward GEMMs run in bf16 on bf16 dequantizations of the
+ * exact FP8 operands the forward pass produced (W for DGrad, X for WGrad);
+ * dY stays bf16 and no column-wise FP8 copy is needed.  Dequantization:
+ * out = bf16(fl32(E4M3(q) * scale)), nearest-even at both steps. */
+
+/* Codes q (rows x ldq, K = cols padded to 128) with scales of the given
+ * layout -> out rows x ldo bf16 (16-byte aligned, ldo * 2 a multiple of 16). */
+FP8B_API int fp8_dequantize_bf16(const uint8_t* q, int64_t ldq, const void* s, int64_t lds, int kind,
+                        int64_t rows, int64_t cols, uint16_t* out, int64_t ldo, void* stream);
+
+/* dX [N x C] bf16 = dY [N x D] bf16 * W^ [D x C], W^ the dequantized forward
+ * weight codes (kind FP8B_SCALE_BLOCKS_128X128 or FP8B_SCALE_MX_1X32, K = C).
+ * work: caller-owned D x ldwork bf16 buffer that receives W^.  The GEMM is
+ * hipBLASLt's bf16 GEMM with fp32 accumulation (no workspace); dy and dx
+ * need only element alignment and any leading dimension (hipBLASLt reads and
+ * writes them), work the 16-byte rules of the kernels; the first call
+ * on a device creates a hipBLASLt handle there, and the algorithm is chosen
+ * once per problem shape and cached. */
+FP8B_API int fp8_dequant_gemm_dgrad(const uint16_t* dy, int64_t lddy, const uint8_t* wq, int64_t ldwq,
+                           const void* ws, int64_t ldws, int wkind, int64_t N, int64_t D, int64_t C,
+                           uint16_t* dx, int64_t lddx, uint16_t* work, int64_t ldwork, void* stream);
+
+/* dW [D x C] = dY^T X^ (+ dW when beta = 1; dwt FP8B_F32 required then), X^
+ * the dequantized forward activation codes (kind FP8B_SCALE_ROWS_1X128 or
+ * FP8B_SCALE_MX_1X32, rows N, K = C).  work: caller-owned N x ldwork bf16
+ * buffer that receives X^.  GEMM as above. */
+FP8B_API int fp8_dequant_gemm_wgrad(const uint16_t* dy, int64_t lddy, const uint8_t* xq, int64_t ldxq,
+                           const void* xs, int64_t ldxs, int xkind, int64_t N, int64_t D, int64_t C,
+                           void* dw, int dwt, int64_t lddw, int beta,
+                           uint16_t* work, int64_t ldwork, void* stream);
 
 /* Power-of-two block scales (the SkyRL section "FP8 quantization with FP32
  * and power-of-two block scales": FP32 scales constrained to powers of two,

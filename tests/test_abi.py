@@ -140,3 +140,20 @@ def test_fused_producers_reject_bad_arguments_on_host():
     assert L.fp8_silu_mul_quantize_1x128(X + 4, 256, W, 256, 4, 256, Q, 256, S, 2, None, 0, None) == 3
     assert L.fp8_silu_mul_quantize_1x128(X, 100, W, 256, 4, 256, Q, 256, S, 2, None, 0, None) == 2
     assert L.fp8_silu_mul_quantize_1x128(X, 256, W, 256, 0, 256, Q, 256, S, 2, None, 0, None) == 0
+
+
+def test_dequantized_backward_rejects_bad_arguments_on_host():
+    """Kind, shape and alignment checks of the dequantize and dequantized-
+    backward entry points (nothing is dereferenced or launched)."""
+    L = fb.lib()
+    Q, S, O, Y, W = 0x100000, 0x200000, 0x300000, 0x400000, 0x500000
+    assert L.fp8_dequantize_bf16(Q, 256, S, 2, 3, 4, 256, O, 256, None) == 1          # bad kind
+    assert L.fp8_dequantize_bf16(Q, 128, S, 2, 0, 4, 256, O, 256, None) == 2          # ldq < 256
+    assert L.fp8_dequantize_bf16(Q, 256, S, 1, 0, 4, 256, O, 256, None) == 2          # 2 groups per row
+    assert L.fp8_dequantize_bf16(Q, 256, S, 7, 2, 4, 256, O, 256, None) == 2
+    assert L.fp8_dequantize_bf16(Q, 256, S, 2, 0, 4, 256, O + 8, 256, None) == 3      # misaligned out
+    # DGrad accepts only weight layouts, WGrad only activation layouts
+    assert L.fp8_dequant_gemm_dgrad(Y, 128, Q, 256, S, 2, 0, 8, 128, 256, O, 256, W, 256, None) == 1
+    assert L.fp8_dequant_gemm_wgrad(Y, 128, Q, 256, S, 2, 1, 8, 128, 256, O, 1, 256, 0, W, 256, None) == 1
+    assert L.fp8_dequant_gemm_wgrad(Y, 128, Q, 256, S, 2, 0, 8, 128, 256, O, 1, 256, 1, W, 256, None) == 4
+    assert L.fp8_dequant_gemm_dgrad(Y, 128, Q, 256, S, 2, 1, 8, 128, 256, O, 256, W, 100, None) == 2
