@@ -100,8 +100,10 @@ constexpr int MAX_EPB = 64;
 // are outstanding and leaves the LDS/scalar and export counters alone.
 constexpr int vmcnt_imm(int n) { return (n & 0xF) | ((n >> 4) << 14) | (0x7 << 4) | (0xF << 8); }
 
-// BI x BJ block tile, NW waves, wave tile (16*TI) x (16*TJ), NS LDS stages.
-template <int BI, int BJ, int TI, int TJ, int NW, int SM, int NS>
+// BI x BJ block tile, NW waves, wave tile (16*TI) x (16*TJ), NS LDS stages,
+// GM the grouping (a template argument, so that the dense and row-grouped
+// instances carry none of the expert-boundary code of GROUP_K).
+template <int BI, int BJ, int TI, int TJ, int NW, int SM, int NS, int GM>
 __global__ __launch_bounds__(64 * NW, 1) void k_gemm(GemmArgs g) {
     constexpr int NT = 64 * NW;
     constexpr int WI = 16 * TI, WJ = 16 * TJ;
@@ -141,7 +143,7 @@ __global__ __launch_bounds__(64 * NW, 1) void k_gemm(GemmArgs g) {
     const int64_t nbj = (g.Nn + BJ - 1) / BJ;
     int64_t i0, ihi, j0, kbase = 0, KB = (g.K + 127) / 128;
     int64_t e_first = 0, e_end = 1;                                 // GROUP_K: the block's experts
-    if (g.group_mode == GROUP_ROWS) {
+    if (GM == GROUP_ROWS) {
         if (tid < 64) {                                            // wave 0 locates the row tile
             const SegPos sp = wave_find_tile(g.offsets, g.E, blockIdx.y, BI, SegPos{0, 0, 0});
             if (tid == 0) {
@@ -165,7 +167,7 @@ __global__ __launch_bounds__(64 * NW, 1) void k_gemm(GemmArgs g) {
         i0 = ti * BI;
         ihi = i0 + BI < g.M ? i0 + BI : g.M;
         j0 = tj * BJ;
-        if (g.group_mode == GROUP_K) {
+        if (GM == GROUP_K) {
             // experts [e_first, e_end) in turn, for the same output tile: their
             // K ranges are consecutive in the padded token axis, so the K loop
             // runs through all of them and stores one output tile per expert
@@ -420,7 +422,7 @@ __global__ __launch_bounds__(64 * NW, 1) void k_gemm(GemmArgs g) {
     int buf = 0;                                                     // stage of K block kb
     int nbuf = NS - 1;                                               // stage that receives block kb + NS - 1
     int64_t ecur = e_first;                                          // expert whose K blocks run (GROUP_K)
-    int64_t kend = g.group_mode == GROUP_K ? uniform64(ekb[0]) : KB;
+    int64_t kend = GM == GROUP_K ? uniform64(ekb[0]) : KB;
     int64_t kb = 0;
     for (;;) {
     for (; kb < kend; ++kb) {
@@ -529,7 +531,7 @@ __global__ __launch_bounds__(64 * NW, 1) void k_gemm(GemmArgs g) {
         buf = buf + 1 == NS ? 0 : buf + 1;
         nbuf = nbuf + 1 == NS ? 0 : nbuf + 1;
     }
-    if (g.group_mode != GROUP_K || ecur + 1 >= e_end) break;
+    if (GM != GROUP_K || ecur + 1 >= e_end) break;
     // expert boundary: the next expert's first K block has landed in stage
     // buf and nothing is in flight, so stage nbuf is free: this expert's tile
     // leaves through it in pieces of RH rows (or by direct stores), then the
@@ -554,7 +556,7 @@ __global__ __launch_bounds__(64 * NW, 1) void k_gemm(GemmArgs g) {
     __syncthreads();
 
     // ---------------------------------------------------- epilogue
-    if (g.group_mode == GROUP_K) O += ecur * g.o_estride * o_elem;
+    if (GM == GROUP_K) O += ecur * g.o_estride * o_elem;
     if (STAGED_OUT && !g.out_f32) {
         store_staged(O, smem, 0, BI);                              // every stage is free now
         return;
@@ -562,7 +564,7 @@ __global__ __launch_bounds__(64 * NW, 1) void k_gemm(GemmArgs g) {
     store_direct(O);
 }
 
-template <int BI, int BJ, int TI, int TJ, int NW, int SM, int NS>
+template <int BI, int BJ, int TI, int TJ, int NW, int SM, int NS, int GM>
 static hipError_t launch_cfg(const GemmArgs& args, hipStream_t st) {
     GemmArgs a = args;
     a.epb = 1;
@@ -590,7 +592,7 @@ static hipError_t launch_cfg(const GemmArgs& args, hipStream_t st) {
         if (tiles > 0x7FFFFFFF || z > 65535) return hipErrorInvalidValue;
         grid = dim3((unsigned)tiles, (unsigned)z, 1);
     }
-    k_gemm<BI, BJ, TI, TJ, NW, SM, NS><<<grid, 64 * NW, 0, st>>>(a);
+    k_gemm<BI, BJ, TI, TJ, NW, SM, NS, GM><<<grid, 64 * NW, 0, st>>>(a);
     return hipGetLastError();
 }
 
@@ -601,10 +603,15 @@ static hipError_t launch_sm(const GemmArgs& a, hipStream_t st) {
     // compute unit, and 4 or 8 stages keep enough of it in flight.  The
     // per-element arithmetic is the same in every configuration.
     if (a.M <= 64 && a.group_mode == GROUP_NONE) {
-        if ((a.Nn + 31) / 32 >= 512) return launch_cfg<64, 32, 4, 1, 2, SM, 4>(a, st);
-        return launch_cfg<64, 16, 2, 1, 2, SM, 8>(a, st);
+        if ((a.Nn + 31) / 32 >= 512) return launch_cfg<64, 32, 4, 1, 2, SM, 4, GROUP_NONE>(a, st);
+        return launch_cfg<64, 16, 2, 1, 2, SM, 8, GROUP_NONE>(a, st);
     }
-    return launch_cfg<256, 256, 4, 8, 8, SM, 2>(a, st);       // 8 waves of 64 x 128
+    switch (a.group_mode) {                                   // 8 waves of 64 x 128
+        case GROUP_NONE: return launch_cfg<256, 256, 4, 8, 8, SM, 2, GROUP_NONE>(a, st);
+        case GROUP_ROWS: return launch_cfg<256, 256, 4, 8, 8, SM, 2, GROUP_ROWS>(a, st);
+        case GROUP_K: return launch_cfg<256, 256, 4, 8, 8, SM, 2, GROUP_K>(a, st);
+        default: return hipErrorInvalidValue;
+    }
 }
 
 hipError_t launch_gemm(const GemmArgs& a, hipStream_t st) {
