@@ -4,12 +4,12 @@
 One step = the whole hot path of a training-step linear layer (Qwen3-8B
 down_proj shape, X [8192 x 12288], W [4096 x 12288], dY [8192 x 4096], all
 bf16, seeded synthetic data) on the GPU:
-    128x128 weight quantization (+ transposed codes)        R2
-    dual 1x128 quantization of X  (row-wise + token-axis)   R1 + R3
-    FProp  Y  = X W^T                                        R4
-    dual 1x128 quantization of dY (row-wise + token-axis)   R1 + R3
-    DGrad  dX = dY W                                         R5
-    WGrad  dW = dY^T X                                       R6
+    128x128 weight quantization (+ transposed codes)
+    dual 1x128 quantization of X  (row-wise + token-axis)
+    FProp  Y  = X W^T
+    dual 1x128 quantization of dY (row-wise + token-axis)
+    DGrad  dX = dY W
+    WGrad  dW = dY^T X
 value = 3 * 2*N*D*C FLOP / step time (TFLOP/s), inputs resident in HBM.
 Two copies of every input alternate between steps so nothing is reused
 from the 256 MB Infinity Cache across steps.

@@ -335,7 +335,7 @@ def _e8(rows: int, K: int, dev):
 
 
 def fp8_quantize_act_1x128_pow2(x, e8: bool = True):
-    """R1 with power-of-two scales -> (q, s, e8 [rows, rup(cols)/32] or None)."""
+    """fp8_quantize_act_1x128 with power-of-two scales -> (q, s, e8 [rows, rup(cols)/32] or None)."""
     _check_2d(x, "x")
     rows, cols = x.shape
     q = _new((rows, _rup(cols)), torch.uint8, x.device)
@@ -347,7 +347,7 @@ def fp8_quantize_act_1x128_pow2(x, e8: bool = True):
 
 
 def fp8_quantize_weight_128x128_pow2(w, transpose: bool = True, e8: bool = True):
-    """R2 with power-of-two scales -> (q, s, qT or None, e8 [D, rup(C)/32]
+    """fp8_quantize_weight_128x128 with power-of-two scales -> (q, s, qT or None, e8 [D, rup(C)/32]
     or None, e8T [C, rup(D)/32] or None; e8T only with the transpose)."""
     _check_2d(w, "w")
     D, C = w.shape
@@ -364,7 +364,7 @@ def fp8_quantize_weight_128x128_pow2(w, transpose: bool = True, e8: bool = True)
 
 
 def fp8_quantize_transposed_pow2(x, rowwise: bool = False, e8: bool = True):
-    """R3 with power-of-two scales -> (qT, sT, e8T, q, s, e8); the row-wise
+    """fp8_quantize_transposed with power-of-two scales -> (qT, sT, e8T, q, s, e8); the row-wise
     outputs are None unless rowwise, the E8M0 outputs None unless e8."""
     _check_2d(x, "x")
     rows, cols = x.shape
@@ -408,7 +408,7 @@ def fp8_gemm_wgrad(gqT, gsT, xqT, xsT, N, D, C, dw=None, out_dtype=torch.bfloat1
 
 def fp8_gemm_fprop_grouped(xq, xs, wq, wq_estride, ws, ws_estride, offsets, N, D, C, y=None,
                            out_dtype=torch.bfloat16, ldwq=None, ldws=None):
-    """wq/ws hold all experts (e.g. stacked [E*D, C] from one R2 call);
+    """wq/ws hold all experts (e.g. stacked [E*D, C] from one fp8_quantize_weight_128x128 call);
     ldwq/ldws default to their row strides."""
     y = _new_out(N, D, out_dtype, xq.device) if y is None else y
     E = offsets.numel() - 1

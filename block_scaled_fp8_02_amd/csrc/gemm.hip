@@ -424,6 +424,102 @@ __global__ __launch_bounds__(64 * NW, 1) void k_gemm(GemmArgs g) {
     int64_t ecur = e_first;                                          // expert whose K blocks run (GROUP_K)
     int64_t kend = GM == GROUP_K ? uniform64(ekb[0]) : KB;
     int64_t kb = 0;
+    if constexpr (SM == SCALE_Q_ROW && GM != GROUP_K && TJ >= 2) {
+        // Rotated K loop for per-row scales on both sides (WGrad), whose
+        // promotion costs two VALU operations per output and K block: the
+        // MFMAs of a block's last Q sub-tile are issued after the barrier
+        // that ends the block, from fragments already in registers, so the
+        // matrix cores have work while the next block's first LDS reads are
+        // in flight.  At kb = 0 that tail runs on zero fragments and zero
+        // scales and adds exactly +0.  The arithmetic per output is the same
+        // as in the loop below (measured 3% faster at the WGrad training
+        // shape; no faster for the 128x128-scaled GEMMs, which keep the
+        // plain loop).
+        v8i bf[TI], af = v8i{0, 0, 0, 0, 0, 0, 0, 0};
+        float sp[TI];
+        v4f prev[TI];
+#pragma unroll
+        for (int t = 0; t < TI; ++t) {
+            bf[t] = v8i{0, 0, 0, 0, 0, 0, 0, 0};
+            sp[t] = 0.f;
+            prev[t] = v4f{0.f, 0.f, 0.f, 0.f};
+        }
+        uint4 sqa = make_uint4(0, 0, 0, 0), sqa_prev = sqa;
+        auto promote = [&](int a, const v4f* pv, const float* spb, uint4 sq) {
+#pragma unroll
+            for (int b = 0; b < TI; ++b) {
+                acc[a][b][0] = __builtin_fmaf(pv[b][0], spb[b] * __uint_as_float(sq.x), acc[a][b][0]);
+                acc[a][b][1] = __builtin_fmaf(pv[b][1], spb[b] * __uint_as_float(sq.y), acc[a][b][1]);
+                acc[a][b][2] = __builtin_fmaf(pv[b][2], spb[b] * __uint_as_float(sq.z), acc[a][b][2]);
+                acc[a][b][3] = __builtin_fmaf(pv[b][3], spb[b] * __uint_as_float(sq.w), acc[a][b][3]);
+            }
+        };
+        for (; kb < KB; ++kb) {
+            const int64_t kn = kb + NS - 1 < KB ? kb + NS - 1 : KB - 1;
+            const uint8_t* base = smem + buf * STAGE;
+            const uint32_t* sc = sscale[buf];
+            FP8B_DMA_SCALE(kn, nbuf);
+            // tail of block kb-1: its last Q sub-tile, and the promotion of
+            // the sub-tile before
+            v4f cur[TI];
+#pragma unroll
+            for (int b = 0; b < TI; ++b)
+                cur[b] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(af, bf[b], v4f{0.f, 0.f, 0.f, 0.f},
+                                                                          0, 0, 0, 0, 0, 0);
+            promote(TJ - 2, prev, sp, sqa_prev);
+            float sp_old[TI];
+#pragma unroll
+            for (int b = 0; b < TI; ++b) {
+                prev[b] = cur[b];
+                sp_old[b] = sp[b];
+            }
+            sqa_prev = sqa;
+            __builtin_amdgcn_sched_barrier(0);
+            // block kb: P fragments and scales, first Q fragment
+#pragma unroll
+            for (int t = 0; t < TI; ++t) {
+                bf[t] = lds_frag(base, pfo, t * 16 * 128);
+                sp[t] = __uint_as_float(sc[prow_l + t * 16]);
+            }
+            af = lds_frag(base, qfo, 0);
+            sqa = *reinterpret_cast<const uint4*>(&sc[qrow_l + 4 * (lane >> 4)]);
+            // Q sub-tiles 0 .. TJ-2; step a promotes sub-tile a-1 (step 0 the
+            // last one of block kb-1, with that block's scales)
+#pragma unroll
+            for (int a = 0; a + 1 < TJ; ++a) {
+                if (a * DMA_PER_STEP < NCH)
+                    FP8B_DMA_PART(kn, nbuf, a * DMA_PER_STEP,
+                                  (a + 1) * DMA_PER_STEP < NCH ? (a + 1) * DMA_PER_STEP : NCH);
+                const v8i af_n = lds_frag(base, qfo, (a + 1) * 16 * 128);
+                const uint4 sqa_n = *reinterpret_cast<const uint4*>(&sc[qrow_l + (a + 1) * 16 + 4 * (lane >> 4)]);
+#pragma unroll
+                for (int b = 0; b < TI; ++b)
+                    cur[b] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(af, bf[b], v4f{0.f, 0.f, 0.f, 0.f},
+                                                                              0, 0, 0, 0, 0, 0);
+                if (a == 0) promote(TJ - 1, prev, sp_old, sqa_prev);
+                else promote(a - 1, prev, sp, sqa_prev);
+#pragma unroll
+                for (int b = 0; b < TI; ++b) prev[b] = cur[b];
+                sqa_prev = sqa;
+                af = af_n;
+                sqa = sqa_n;
+                __builtin_amdgcn_sched_barrier(0);
+            }
+            if ((TJ - 1) * DMA_PER_STEP < NCH) FP8B_DMA_PART(kn, nbuf, (TJ - 1) * DMA_PER_STEP, NCH);
+            __builtin_amdgcn_s_waitcnt(vmcnt_imm(INFLIGHT));        // block kb + 1 has landed
+            __syncthreads();                                         // (and af is in registers)
+            buf = buf + 1 == NS ? 0 : buf + 1;
+            nbuf = nbuf + 1 == NS ? 0 : nbuf + 1;
+        }
+        // tail of the last block
+        v4f cur[TI];
+#pragma unroll
+        for (int b = 0; b < TI; ++b)
+            cur[b] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(af, bf[b], v4f{0.f, 0.f, 0.f, 0.f},
+                                                                      0, 0, 0, 0, 0, 0);
+        promote(TJ - 2, prev, sp, sqa_prev);
+        promote(TJ - 1, cur, sp, sqa);
+    } else
     for (;;) {
     for (; kb < kend; ++kb) {
         const int64_t kn = kb + NS - 1 < KB ? kb + NS - 1 : KB - 1;  // past the end the last block is

@@ -19,8 +19,11 @@
  * Conventions shared by every entry point
  * ---------------------------------------
  * - All pointers are DEVICE pointers (except where stated) owned by the
- *   caller.  The library never allocates or frees device memory and keeps
- *   no state between calls apart from lazily loaded code objects.
+ *   caller.  The library's own kernels allocate and free no device memory,
+ *   and it keeps no state between calls apart from lazily loaded code
+ *   objects and, for the two dequantized-backward GEMMs, one hipBLASLt
+ *   handle per device (created on first use; hipBLASLt may allocate inside
+ *   it) and a cache of the algorithms it chose per problem shape.
  * - Every call is asynchronous on `stream` (a hipStream_t passed as void*;
  *   NULL is the default stream).  Buffers must stay valid until the stream
  *   reaches the operation.
@@ -89,7 +92,7 @@ FP8B_API int fp8b_last_hip_error(void);
 /* Quantizers                                                          */
 /* ------------------------------------------------------------------ */
 
-/* R1. 1x128 per-group quantization along the contiguous axis
+/* 1x128 per-group quantization along the contiguous axis
  * (Jet-RL summary, "Activation and gradient quantization: 1x128 per-group";
  * used for X in FProp and for dY along D in DGrad).
  *   x  : rows x cols of dtype xt, row stride ldx >= cols.
@@ -101,7 +104,7 @@ FP8B_API int fp8b_last_hip_error(void);
 FP8B_API int fp8_quantize_act_1x128(const void* x, int xt, int64_t rows, int64_t cols, int64_t ldx,
                            uint8_t* q, int64_t ldq, float* s, int64_t lds, void* stream);
 
-/* R2. 128x128 per-block weight quantization (Jet-RL summary, "Weight
+/* 128x128 per-block weight quantization (Jet-RL summary, "Weight
  * quantization: 128x128 per-block"; redone after every optimizer step).
  *   w  : D x C of dtype wt, row stride ldw >= C.
  *   q  : D x ldq bytes, ldq >= round_up(C,128), ldq % 16 == 0; pad 0x00.
@@ -116,20 +119,21 @@ FP8B_API int fp8_quantize_weight_128x128(const void* w, int wt, int64_t D, int64
                                 uint8_t* q, int64_t ldq, float* s, int64_t lds,
                                 uint8_t* qT, int64_t ldqT, void* stream);
 
-/* R3. 1x128 groups along the token (row) axis, written transposed: the
+/* 1x128 groups along the token (row) axis, written transposed: the
  * WGrad operands dY^T and X^T (Jet-RL notes, section 4.2: WGrad groups its
- * operands along the token axis).  Reads x once and can also emit the R1
- * row-wise quantization of the same tensor from the same read.
+ * operands along the token axis).  Reads x once and can also emit the
+ * row-wise 1x128 quantization of the same tensor from the same read.
  *   x   : rows x cols of dtype xt, row stride ldx.
  *   qT  : cols x ldqT bytes, ldqT >= round_up(rows,128), ldqT % 16 == 0;
  *         qT[c][r] is the code of x[r][c]; pad positions 0x00.
  *   sT  : cols x ldsT fp32, ldsT >= ceil(rows/128).
- *   q, s: optional (both NULL or both set) R1 output with ldq/lds as in R1. */
+ *   q, s: optional (both NULL or both set) output of fp8_quantize_act_1x128,
+ *        with ldq/lds as there. */
 FP8B_API int fp8_quantize_transposed(const void* x, int xt, int64_t rows, int64_t cols, int64_t ldx,
                             uint8_t* qT, int64_t ldqT, float* sT, int64_t ldsT,
                             uint8_t* q, int64_t ldq, float* s, int64_t lds, void* stream);
 
-/* R3, grouped (MoE).  offsets: DEVICE int32[E+1], non-decreasing, offsets[0]
+/* Token-axis quantization, grouped (MoE).  offsets: DEVICE int32[E+1], non-decreasing, offsets[0]
  * = 0, offsets[E] = rows; rows [offsets[e], offsets[e+1]) belong to expert
  * e and token groups restart at every offsets[e].  Expert e occupies qT
  * columns [P_e, P_e + round_up(n_e,128)) with n_e = offsets[e+1]-offsets[e]
@@ -181,7 +185,8 @@ FP8B_API int fp8_silu_mul_quantize_1x128(const uint16_t* gate, int64_t ldg, cons
 
 /* Token-axis requantization of saved FP8 activations (the flow the Jet-RL
  * pages attribute to DeepSeek-V3, which keeps only the FP8 copy of X and
- * forms WGrad's X^T from it).  Input: R1 output, codes q (rows x ldq bytes,
+ * forms WGrad's X^T from it).  Input: the output of fp8_quantize_act_1x128,
+ * codes q (rows x ldq bytes,
  * 1x128 groups along the contiguous axis, cols real columns; bytes past
  * cols are ignored) and scales s (rows x lds fp32).  Each element is
  * dequantized as fl32(E4M3(q) * s) (one binary32 multiply; the pages leave
@@ -234,7 +239,7 @@ FP8B_API int fp8_dequant_gemm_wgrad(const uint16_t* dy, int64_t lddy, const uint
 /* Power-of-two block scales (the SkyRL section "FP8 quantization with FP32
  * and power-of-two block scales": FP32 scales constrained to powers of two,
  * an exponent-only representation, the only kind Blackwell tensor cores
- * take).  Same groupings, layouts and codes rule as R1-R3, with the scale of
+ * take).  Same groupings, layouts and codes rule as the three quantizers above, with the scale of
  * a group S = 2^k, k the smallest integer with max|x| <= 448 * 2^k (rounded
  * up so the group maximum does not clip; the pages do not state the rounding,
  * this is the rule they give for E8M0 scales), clamped to [-127, 127]; an
@@ -246,12 +251,12 @@ FP8B_API int fp8_dequant_gemm_wgrad(const uint16_t* dy, int64_t lddy, const uint
  * bytes the MXFP8 GEMMs below compute the same products on the gfx950
  * scaled MFMA, with no per-block promotion in software. */
 
-/* R1 with power-of-two scales; e8: rows x lde E8M0 bytes (nullable). */
+/* fp8_quantize_act_1x128 with power-of-two scales; e8: rows x lde E8M0 bytes (nullable). */
 FP8B_API int fp8_quantize_act_1x128_pow2(const void* x, int xt, int64_t rows, int64_t cols, int64_t ldx,
                                 uint8_t* q, int64_t ldq, float* s, int64_t lds,
                                 uint8_t* e8, int64_t lde, void* stream);
 
-/* R2 with power-of-two scales; e8: D x lde E8M0 bytes of q's rows (the
+/* fp8_quantize_weight_128x128 with power-of-two scales; e8: D x lde E8M0 bytes of q's rows (the
  * block's byte repeated for its 128 rows), e8T: C x ldeT bytes of qT's rows
  * (nullable each; e8T is the scale input of fp8_mx_gemm_dgrad). */
 FP8B_API int fp8_quantize_weight_128x128_pow2(const void* w, int wt, int64_t D, int64_t C, int64_t ldw,
@@ -259,7 +264,7 @@ FP8B_API int fp8_quantize_weight_128x128_pow2(const void* w, int wt, int64_t D, 
                                      uint8_t* qT, int64_t ldqT,
                                      uint8_t* e8, int64_t lde, uint8_t* e8T, int64_t ldeT, void* stream);
 
-/* R3 with power-of-two scales; e8T: cols x ldeT bytes of qT's groups, e8:
+/* fp8_quantize_transposed with power-of-two scales; e8T: cols x ldeT bytes of qT's groups, e8:
  * rows x lde bytes of the row-wise copy (requires q; nullable each). */
 FP8B_API int fp8_quantize_transposed_pow2(const void* x, int xt, int64_t rows, int64_t cols, int64_t ldx,
                                  uint8_t* qT, int64_t ldqT, float* sT, int64_t ldsT, uint8_t* e8T, int64_t ldeT,
@@ -271,37 +276,37 @@ FP8B_API int fp8_quantize_transposed_pow2(const void* x, int xt, int64_t rows, i
 /* partial product is scaled by s_a * s_b before it is added)           */
 /* ------------------------------------------------------------------ */
 
-/* R4. FProp Y[N x D] = X W^T (Jet-RL notes, section 2.2 FProp; 4.2: the
+/* FProp Y[N x D] = X W^T (Jet-RL notes, section 2.2 FProp; 4.2: the
  * activation 1x128 and the weight 128x128).
- *   xq [N x ldxq] codes, xs [N x ldxs] fp32 (from R1 on X [N x C]);
- *   wq [D x ldwq] codes, ws [ceil(D/128) x ldws] fp32 (from R2);
+ *   xq [N x ldxq] codes, xs [N x ldxs] fp32 (fp8_quantize_act_1x128 of X [N x C]);
+ *   wq [D x ldwq] codes, ws [ceil(D/128) x ldws] fp32 (fp8_quantize_weight_128x128);
  *   y  [N x ldy] of dtype yt (FP8B_BF16: round-to-nearest-even; FP8B_F32). */
 FP8B_API int fp8_gemm_fprop(const uint8_t* xq, int64_t ldxq, const float* xs, int64_t ldxs,
                    const uint8_t* wq, int64_t ldwq, const float* ws, int64_t ldws,
                    void* y, int yt, int64_t ldy, int64_t N, int64_t D, int64_t C, void* stream);
 
-/* R5. DGrad dX[N x C] = dY W (Jet-RL notes, section 2.2 DGrad; 4.2: same
+/* DGrad dX[N x C] = dY W (Jet-RL notes, section 2.2 DGrad; 4.2: same
  * kernel configuration as FProp, the weight only transposed).
- *   gq [N x ldgq] codes, gs [N x ldgs] fp32 (R1 on dY [N x D], groups along D);
- *   wqT [C x ldwqT] codes (R2's transposed copy), ws [ceil(D/128) x ldws]. */
+ *   gq [N x ldgq] codes, gs [N x ldgs] fp32 (fp8_quantize_act_1x128 of dY [N x D], groups along D);
+ *   wqT [C x ldwqT] codes (the transposed copy written by fp8_quantize_weight_128x128), ws [ceil(D/128) x ldws]. */
 FP8B_API int fp8_gemm_dgrad(const uint8_t* gq, int64_t ldgq, const float* gs, int64_t ldgs,
                    const uint8_t* wqT, int64_t ldwqT, const float* ws, int64_t ldws,
                    void* dx, int dxt, int64_t lddx, int64_t N, int64_t D, int64_t C, void* stream);
 
-/* R6. WGrad dW[D x C] = dY^T X (Jet-RL notes, section 2.2 WGrad; 4.2: both
+/* WGrad dW[D x C] = dY^T X (Jet-RL notes, section 2.2 WGrad; 4.2: both
  * operands grouped along the token axis).
- *   gqT [D x ldgqT], gsT [D x ldgsT] (R3 on dY); xqT [C x ldxqT], xsT [C x ldxsT]
- *   (R3 on X); contraction length N (tokens).
+ *   gqT [D x ldgqT], gsT [D x ldgsT] (fp8_quantize_transposed of dY); xqT [C x ldxqT], xsT [C x ldxsT]
+ *   (fp8_quantize_transposed of X); contraction length N (tokens).
  *   beta = 0: dw = result; beta = 1: dw += result (dwt must be FP8B_F32). */
 FP8B_API int fp8_gemm_wgrad(const uint8_t* gqT, int64_t ldgqT, const float* gsT, int64_t ldgsT,
                    const uint8_t* xqT, int64_t ldxqT, const float* xsT, int64_t ldxsT,
                    void* dw, int dwt, int64_t lddw, int beta,
                    int64_t N, int64_t D, int64_t C, void* stream);
 
-/* R7. Grouped (MoE) forms.  offsets: DEVICE int32[E+1] as for the grouped
+/* Grouped (MoE) forms.  offsets: DEVICE int32[E+1] as for the grouped
  * quantizer.  Expert e's weight codes start at w + e*w_estride (bytes) and
  * its scales at ws + e*ws_estride (floats); stacking the experts as one
- * (E*D) x C matrix quantized by R2 gives w_estride = D*ldwq and
+ * (E*D) x C matrix quantized by fp8_quantize_weight_128x128 gives w_estride = D*ldwq and
  * ws_estride = (D/128)*ldws, and for the transposed copy qT [C x E*D]
  * w_estride = D.
  * FProp: rows of expert e of xq times W_e^T -> rows of y.
@@ -319,7 +324,7 @@ FP8B_API int fp8_gemm_dgrad_grouped(const uint8_t* gq, int64_t ldgq, const float
                            const int32_t* offsets, int64_t E, int64_t N, int64_t D, int64_t C,
                            void* stream);
 /* WGrad per expert: dW_e = dY_e^T X_e from the grouped transposed operands
- * (R3 grouped); dW_e is written at dw + e*dw_estride (elements).  An expert
+ * (fp8_quantize_transposed_grouped); dW_e is written at dw + e*dw_estride (elements).  An expert
  * with no rows gets dW_e = 0 (beta = 0) or is left unchanged (beta = 1). */
 FP8B_API int fp8_gemm_wgrad_grouped(const uint8_t* gqT, int64_t ldgqT, const float* gsT, int64_t ldgsT,
                            const uint8_t* xqT, int64_t ldxqT, const float* xsT, int64_t ldxsT,
@@ -331,7 +336,7 @@ FP8B_API int fp8_gemm_wgrad_grouped(const uint8_t* gqT, int64_t ldgqT, const flo
 /* MXFP8 (Miles MXFP8/NVFP4 blog, MXFP8 paragraphs)                    */
 /* ------------------------------------------------------------------ */
 
-/* R9. 1x32 blocks, scale 2^k stored as the E8M0 byte k+127, k the smallest
+/* MXFP8: 1x32 blocks, scale 2^k stored as the E8M0 byte k+127, k the smallest
  * integer with max|block| <= 448*2^k, clamped to [-127,127] (all-zero block:
  * k = -127); codes E4M3(x * 2^-k).  Either output pair may be NULL:
  *   q  [rows x ldq], e [rows x lde]: row-wise (blocks along cols);
@@ -344,7 +349,7 @@ FP8B_API int fp8_mx_quantize_1x32(const void* x, int xt, int64_t rows, int64_t c
                          uint8_t* q, int64_t ldq, uint8_t* e, int64_t lde,
                          uint8_t* qT, int64_t ldqT, uint8_t* eT, int64_t ldeT, void* stream);
 
-/* R10. MX GEMMs on gfx950 scaled MFMA.  All three are
+/* MX GEMMs on gfx950 scaled MFMA.  All three are
  *   out[i][j] = sum_k (a[i][k] 2^(ea[i][k/32]-127)) (b[j][k] 2^(eb[j][k/32]-127))
  * with both operands K-contiguous:
  *   FProp: a = X row-wise [N x C], b = W row-wise [D x C]          -> y [N x D]
