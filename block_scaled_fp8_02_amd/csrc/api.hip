@@ -63,6 +63,11 @@ int check_output(const void* o, int dt, int64_t rows, int64_t cols, int64_t ld, 
     return FP8B_OK;
 }
 
+// Largest leading dimensions the GEMMs take: FP8 code rows in bytes, scale
+// rows in elements.
+constexpr int64_t kMaxGemmCodeLd = (int64_t)1 << 24;
+constexpr int64_t kMaxGemmScaleLd = (int64_t)1 << 22;
+
 #define FP8B_TRY(expr)                  \
     do {                                \
         const int _st = (expr);         \
@@ -86,6 +91,10 @@ int validate_gemm(int op, const void* a, int64_t lda, const void* sa, int64_t ld
     else if (base == 1) { M = N; Nn = C; K = D; }
     else { M = D; Nn = C; K = N; }
     if (base != 2 && beta != 0) return FP8B_EINVAL;
+    // the kernels address a tile's 256 rows (codes and scale rows) with
+    // 32-bit offsets from a per-tile base
+    if (lda > kMaxGemmCodeLd || ldb > kMaxGemmCodeLd || ldsa > kMaxGemmScaleLd || ldsb > kMaxGemmScaleLd)
+        return FP8B_EUNSUPPORTED;
     FP8B_TRY(check_codes(a, M, K, lda));
     FP8B_TRY(check_codes(b, Nn, K, ldb));
     const int64_t kb = mx ? rup128(K) / 32 : cdiv(K, 128);

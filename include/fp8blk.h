@@ -276,6 +276,11 @@ FP8B_API int fp8_quantize_transposed_pow2(const void* x, int xt, int64_t rows, i
 /* partial product is scaled by s_a * s_b before it is added)           */
 /* ------------------------------------------------------------------ */
 
+/* Limits shared by every GEMM below (block-scaled and MX, dense and grouped):
+ * the leading dimensions of the FP8 code operands are at most 2^24 bytes and
+ * those of their scale operands at most 2^22 elements; larger ones return
+ * FP8B_EUNSUPPORTED (the kernels address a tile's rows with 32-bit offsets). */
+
 /* FProp Y[N x D] = X W^T (Jet-RL notes, section 2.2 FProp; 4.2: the
  * activation 1x128 and the weight 128x128).
  *   xq [N x ldxq] codes, xs [N x ldxs] fp32 (fp8_quantize_act_1x128 of X [N x C]);

@@ -78,6 +78,17 @@ def test_validate_dgrad_and_wgrad():
     assert v(2, lda=256, ldb=256, ldsa=2, ldsb=2, ldo=512, beta=2) == 1
 
 
+def test_validate_gemm_leading_dimension_limits():
+    # FP8 code rows up to 2^24 bytes and scale rows up to 2^22 elements: the
+    # kernels address a tile's rows with 32-bit offsets
+    assert v(0, lda=1 << 24) == 0
+    assert v(0, lda=(1 << 24) + 16) == 4
+    assert v(1, lda=384, ldb=(1 << 24) + 16, ldsa=3, ldsb=4, ldo=512) == 4
+    assert v(2, lda=256, ldb=256, ldsa=(1 << 22) + 1, ldsb=2, ldo=512) == 4
+    assert v(0, ldsb=1 << 22) == 0
+    assert v(0, ldsb=(1 << 22) + 1) == 4
+
+
 def test_validate_mx():
     # MX: E8M0 scales per 32 along the padded K (alignment 1)
     assert v(3, ldsa=16, ldsb=16, sa=SA + 1, sb=SB + 3) == 0
