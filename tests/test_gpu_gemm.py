@@ -189,15 +189,15 @@ def test_unified_forward_is_batch_invariant():
     banner("batch invariance 64 vs 8192 rows")
     wq, ws, _ = fb.fp8_quantize_weight_128x128(dev(w["W"]), transpose=False)
     xq, xs = fb.fp8_quantize_act_1x128(dev(X))
-    y_big = fb.fp8_gemm_fprop(xq, xs, wq, ws, 8192, 24576, 4096)
-    xq64, xs64 = fb.fp8_quantize_act_1x128(dev(X[:64]))
-    y_small = fb.fp8_gemm_fprop(xq64, xs64, wq, ws, 64, 24576, 4096)
-    for m in (1, 17, 100, 256):
-        xqm, xsm = fb.fp8_quantize_act_1x128(dev(X[:m]))
-        ym = fb.fp8_gemm_fprop(xqm, xsm, wq, ws, m, 24576, 4096)
-        assert torch.equal(ym, y_big[:m]), m
-    assert torch.equal(y_small, y_big[:64])
-    y_again = fb.fp8_gemm_fprop(xq, xs, wq, ws, 8192, 24576, 4096)
+    # the full weight and a ragged one (its last tile 88 rows): the decode
+    # tiles (64 x 128, 64 x 32, 64 x 16) against the 256 x 256 training tile
+    for D in (24576, 24536, 16384, 4000):
+        y_big = fb.fp8_gemm_fprop(xq, xs, wq[:D], ws, 8192, D, 4096)
+        for m in (1, 17, 64, 100, 256):
+            xqm, xsm = fb.fp8_quantize_act_1x128(dev(X[:m]))
+            ym = fb.fp8_gemm_fprop(xqm, xsm, wq[:D], ws, m, D, 4096)
+            assert torch.equal(ym, y_big[:m]), (D, m)
+    y_again = fb.fp8_gemm_fprop(xq, xs, wq[:D], ws, 8192, D, 4096)
     assert torch.equal(y_again, y_big)
 
 

@@ -111,3 +111,21 @@ def test_mx_gemm_ragged(N, D, C):
         banner(f"mx ragged {name} N={N} D={D} C={C}: {err:.3e}, |err|/sum|ab| {ratio:.3e}")
         assert err <= TOL
         assert ratio <= 2.0 ** -12          # fp8 MFMA dot-product accumulation scale
+
+
+def test_mx_forward_is_batch_invariant():
+    """MX FProp rows do not depend on how many rows are in the call: the
+    decode tiles (64 x 128 for this weight, 64 x 16 for a narrow one) give
+    the 256 x 256 training tile's rows bit for bit."""
+    w = wl.mx(0)
+    rng = wl.rng_for(11)
+    X = wl.f32_to_bf16_bits(wl.normal(rng, (512, 4096), 1.0))
+    banner("mx batch invariance 1/17/64 vs 512 rows")
+    wq, we, _, _ = fb.fp8_mx_quantize_1x32(dev(w["W"]), colwise=False)
+    xq, xe, _, _ = fb.fp8_mx_quantize_1x32(dev(X), colwise=False)
+    for D in (24576, 4000):
+        y_big = fb.fp8_mx_gemm_fprop(xq, xe, wq[:D], we[:D], 512, D, 4096)
+        for m in (1, 17, 64):
+            xqm, xem, _, _ = fb.fp8_mx_quantize_1x32(dev(X[:m]), colwise=False)
+            ym = fb.fp8_mx_gemm_fprop(xqm, xem, wq[:D], we[:D], m, D, 4096)
+            assert torch.equal(ym, y_big[:m]), (D, m)
