@@ -1,0 +1,148 @@
+"""GPU parity past 2^31 elements: every quantizer and the GEMMs on tensors
+whose element (or code) count exceeds what a 32-bit index can address,
+checked against the oracle on sampled rows, columns and blocks (the oracle
+cannot take the whole tensors in reasonable time).  Inputs are drawn on the
+device from a seeded generator; the sampled slices are copied to the host
+exactly (bf16 bits) for the oracle."""
+import numpy as np
+import pytest
+import torch
+
+import block_scaled_fp8_02_amd as fb
+import oracle
+from gpu_util import TOL, assert_bytes_equal, assert_scales_equal, banner
+
+pytestmark = pytest.mark.gpu
+
+
+def seeded_bf16(rows: int, cols: int, seed: int, std: float = 1.0) -> torch.Tensor:
+    """rows x cols bf16 view with the row stride padded to 16 bytes."""
+    g = torch.Generator(device="cuda")
+    g.manual_seed(seed)
+    ld = (cols + 7) // 8 * 8
+    buf = torch.randn(rows, ld, generator=g, device="cuda", dtype=torch.bfloat16)
+    buf.mul_(std)
+    return buf[:, :cols]
+
+
+def bits(t: torch.Tensor) -> np.ndarray:
+    """bf16 device tensor -> host uint16 bits (exact)."""
+    return t.detach().contiguous().to("cpu").view(torch.int16).numpy().view(np.uint16)
+
+
+def u8(t: torch.Tensor) -> np.ndarray:
+    return t.detach().contiguous().to("cpu").numpy()
+
+
+def f32(t: torch.Tensor) -> np.ndarray:
+    return t.detach().contiguous().to("cpu").numpy()
+
+
+def free_cache():
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+
+
+ROWS, COLS = 65539, 32773                  # 2.148e9 elements, ragged both ways
+
+
+def test_act_and_token_axis_quantizers_past_2_31():
+    assert ROWS * COLS > 2**31
+    banner(f"large: act 1x128 and dual token-axis quantizers on {ROWS}x{COLS}")
+    x = seeded_bf16(ROWS, COLS, 101)
+    q, s = fb.fp8_quantize_act_1x128(x)
+    qT, sT, q2, s2 = fb.fp8_quantize_transposed(x, rowwise=True)
+    torch.cuda.synchronize()
+    assert torch.equal(q2, q) and torch.equal(s2.view(torch.int32), s.view(torch.int32))
+    rows = [0, 1, 32768, ROWS - 3, ROWS - 1]
+    xr = bits(x[rows])
+    oq, os_ = oracle.quant_1x128(xr)
+    assert_bytes_equal(u8(q[rows]), oq, "1x128 codes (sampled rows)")
+    assert_scales_equal(f32(s[rows]), os_, "1x128 scales (sampled rows)")
+    cols = [0, 7, 16386, COLS - 2, COLS - 1]
+    xc = bits(x[:, cols])
+    oqT, osT = oracle.quant_colwise(xc)
+    assert_bytes_equal(u8(qT[cols]), oqT, "token-axis codes (sampled columns)")
+    assert_scales_equal(f32(sT[cols]), osT, "token-axis scales (sampled columns)")
+    banner("large: MX 1x32 quantizer on the same tensor")
+    mq, me, mqT, meT = fb.fp8_mx_quantize_1x32(x)
+    torch.cuda.synchronize()
+    omq, ome = oracle.mx_quant_rows(xr)
+    assert_bytes_equal(u8(mq[rows]), omq, "MX row codes (sampled rows)")
+    assert_bytes_equal(u8(me[rows]), ome, "MX row scales (sampled rows)")
+    omqT, omeT = oracle.mx_quant_cols(xc)
+    assert_bytes_equal(u8(mqT[cols]), omqT, "MX column codes (sampled columns)")
+    assert_bytes_equal(u8(meT[cols]), omeT, "MX column scales (sampled columns)")
+    del x, q, s, qT, sT, q2, s2, mq, me, mqT, meT
+    free_cache()
+
+
+def test_weight_quantizer_past_2_31():
+    D, C = 50003, 45061                     # 2.253e9 elements, ragged 128x128 blocks at both edges
+    assert D * C > 2**31
+    banner(f"large: 128x128 weight quantizer (+ transposed codes) on {D}x{C}")
+    w = seeded_bf16(D, C, 102, std=0.02)
+    q, s, qT = fb.fp8_quantize_weight_128x128(w)
+    torch.cuda.synchronize()
+    for br, bc in [(0, 0), (0, (C - 1) // 128), ((D - 1) // 128, 0), ((D - 1) // 128, (C - 1) // 128), (200, 171)]:
+        r0, c0 = br * 128, bc * 128
+        r1, c1 = min(r0 + 128, D), min(c0 + 128, C)
+        ob_q, ob_s, ob_qT = oracle.quant_128x128(bits(w[r0:r1, c0:c1]))
+        assert_bytes_equal(u8(q[r0:r1, c0:c0 + 128]), ob_q, f"block ({br},{bc}) codes")
+        assert_scales_equal(f32(s[br:br + 1, bc:bc + 1]), ob_s, f"block ({br},{bc}) scale")
+        assert_bytes_equal(u8(qT[c0:c1, r0:r0 + 128]), ob_qT, f"block ({br},{bc}) transposed codes")
+    del w, q, s, qT
+    free_cache()
+
+
+def test_fprop_with_activation_codes_past_2_31():
+    N, C, D = 140003, 16384, 512            # X codes: 2.29e9 bytes
+    assert N * C > 2**31
+    banner(f"large: FProp {N}x{D}x{C}")
+    x = seeded_bf16(N, C, 103)
+    w = seeded_bf16(D, C, 104, std=0.02)
+    xq, xs = fb.fp8_quantize_act_1x128(x)
+    wq, ws, _ = fb.fp8_quantize_weight_128x128(w, transpose=False)
+    y = fb.fp8_gemm_fprop(xq, xs, wq, ws, N, D, C)
+    torch.cuda.synchronize()
+    rows = [0, 70001, N - 1]
+    oxq, oxs = oracle.quant_1x128(bits(x[rows]))
+    owq, ows, _ = oracle.quant_128x128(bits(w), with_transpose=False)
+    y_ref = oracle.fprop(oxq, oxs, owq, ows, C)
+    yr = y[rows].float().cpu().numpy()
+    err = oracle.rel_row_error(yr, y_ref)
+    banner(f"  sampled rows err {err:.3e}")
+    assert err <= TOL
+    del x, w, xq, xs, wq, ws, y
+    free_cache()
+
+
+def test_wgrad_with_token_axis_codes_past_2_31():
+    N, D, C = 524413, 4096, 4096            # dY^T and X^T codes: 2.15e9 bytes each, K = N
+    assert D * (N + 127) // 128 * 128 > 2**31
+    banner(f"large: WGrad {D}x{C}, K = {N} tokens")
+    dy = seeded_bf16(N, D, 105, std=1e-3)
+    gqT, gsT, _, _ = fb.fp8_quantize_transposed(dy)
+    ds = [0, 2049, D - 1]
+    dy_s = bits(dy[:, ds])
+    del dy
+    free_cache()
+    x = seeded_bf16(N, C, 106)
+    xqT, xsT, _, _ = fb.fp8_quantize_transposed(x)
+    cs = sorted({0, C - 1} | set(np.random.default_rng(107).choice(C, 62, replace=False).tolist()))
+    x_s = bits(x[:, cs])
+    del x
+    free_cache()
+    dw = fb.fp8_gemm_wgrad(gqT, gsT, xqT, xsT, N, D, C, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    ogqT, ogsT = oracle.quant_colwise(dy_s)
+    oxqT, oxsT = oracle.quant_colwise(x_s)
+    ref = oracle.wgrad(ogqT, ogsT, oxqT, oxsT, N)                # [3, 64]
+    got = dw[ds][:, cs].cpu().numpy()
+    # the norm of the full dW row is not available to the sampled check: the
+    # entries are measured against the norm of their 64 sampled columns
+    err = oracle.rel_row_error(got, ref)
+    banner(f"  sampled entries err {err:.3e}")
+    assert err <= TOL
+    del gqT, gsT, xqT, xsT, dw
+    free_cache()
