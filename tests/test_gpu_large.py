@@ -146,3 +146,48 @@ def test_wgrad_with_token_axis_codes_past_2_31():
     assert err <= TOL
     del gqT, gsT, xqT, xsT, dw
     free_cache()
+
+
+def test_fused_requant_dequant_past_2_31():
+    rows, cols = 70001, 32773                # 2.294e9 elements
+    assert rows * cols > 2**31
+    banner(f"large: RMSNorm + 1x128 on {rows}x{cols}")
+    x = seeded_bf16(rows, cols, 108)
+    w = seeded_bf16(1, cols, 109, std=0.5)[0]
+    w = w.contiguous()
+    q, s, r, _ = fb.fp8_rmsnorm_quantize_1x128(x, w, 1e-6, rstd=True)
+    torch.cuda.synchronize()
+    sr = [0, 35000, rows - 1]
+    oq, os_, orr, _ = oracle.rmsnorm_quant_1x128(bits(x[sr]), bits(w), 1e-6)
+    assert_bytes_equal(u8(q[sr]), oq, "RMSNorm codes (sampled rows)")
+    assert_scales_equal(f32(s[sr]), os_, "RMSNorm scales (sampled rows)")
+    assert_scales_equal(f32(r[sr]), np.asarray(orr, dtype=np.float32), "RMSNorm rstd (sampled rows)")
+
+    banner("large: token-axis requantization of those codes")
+    qT, sT = fb.fp8_requantize_transposed(q, s, cols)
+    torch.cuda.synchronize()
+    for g in (0, 128, (cols - 1) // 128):                     # whole 128-column groups, the last one ragged
+        c0, c1 = g * 128, min(g * 128 + 128, cols)
+        oqT, osT = oracle.requant_colwise(u8(q[:, c0:c0 + 128]), f32(s[:, g:g + 1]), c1 - c0)
+        assert_bytes_equal(u8(qT[c0:c1]), oqT, f"requantized codes, group {g}")
+        assert_scales_equal(f32(sT[c0:c1]), osT, f"requantized scales, group {g}")
+    del qT, sT
+    free_cache()
+
+    banner("large: bf16 dequantization of those codes")
+    deq = fb.fp8_dequantize_bf16(q, s, fb.FP8B_SCALE_ROWS_1X128, cols)
+    torch.cuda.synchronize()
+    assert_bytes_equal(bits(deq[sr]), oracle.dequant_bf16_rows(u8(q[sr]), f32(s[sr]), cols), "dequantized rows")
+    del x, q, s, r, deq
+    free_cache()
+
+    banner(f"large: SiLU(gate) * up + 1x128 on {rows}x{cols}")
+    gate = seeded_bf16(rows, cols, 110, std=3.0)
+    up = seeded_bf16(rows, cols, 111)
+    q, s, _ = fb.fp8_silu_mul_quantize_1x128(gate, up)
+    torch.cuda.synchronize()
+    oq, os_, _ = oracle.silu_mul_quant_1x128(bits(gate[sr]), bits(up[sr]))
+    assert_bytes_equal(u8(q[sr]), oq, "SiLU codes (sampled rows)")
+    assert_scales_equal(f32(s[sr]), os_, "SiLU scales (sampled rows)")
+    del gate, up, q, s
+    free_cache()
