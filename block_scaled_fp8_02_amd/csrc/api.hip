@@ -364,7 +364,7 @@ int fp8_dequant_gemm_dgrad(const uint16_t* dy, int64_t lddy, const uint8_t* wq, 
     FP8B_TRY(check_blas_matrix(dx, FP8B_BF16, N, C, lddx));
     const hipStream_t st = static_cast<hipStream_t>(stream);
     if (N == 0 || C == 0) return FP8B_OK;
-    if (D == 0) return hip_status(hipMemset2DAsync(dx, lddx * 2, 0, C * 2, N, st));
+    if (D == 0) return hip_status(launch_zero_2d(dx, lddx * 2, C * 2, N, st));
     FP8B_TRY(hip_status(launch_dequant_bf16(wq, ldwq, ws, ldws, wkind, D, C, work, ldwork, st)));
     int lt = 0;
     const hipError_t e = lt_gemm(false, false, C, N, D, work, ldwork, dy, lddy, dx, lddx, false, 0.0f, st, &lt);
@@ -386,8 +386,7 @@ int fp8_dequant_gemm_wgrad(const uint16_t* dy, int64_t lddy, const uint8_t* xq, 
     if (D == 0 || C == 0) return FP8B_OK;
     if (N == 0) {
         if (beta) return FP8B_OK;
-        return hip_status(hipMemset2DAsync(dw, lddw * (dwt == FP8B_F32 ? 4 : 2), 0,
-                                           C * (dwt == FP8B_F32 ? 4 : 2), D, st));
+        return hip_status(launch_zero_2d(dw, lddw * (dwt == FP8B_F32 ? 4 : 2), C * (dwt == FP8B_F32 ? 4 : 2), D, st));
     }
     FP8B_TRY(hip_status(launch_dequant_bf16(xq, ldxq, xs, ldxs, xkind, N, C, work, ldwork, st)));
     int lt = 0;

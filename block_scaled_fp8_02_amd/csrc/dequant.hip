@@ -82,6 +82,29 @@ hipError_t launch_dequant_bf16(const uint8_t* q, int64_t ldq, const void* s, int
     return hipGetLastError();
 }
 
+// Zero rows x row_bytes bytes with row stride ld_bytes (a GEMM output whose
+// contraction is empty).  A kernel rather than a memset, so that a caller
+// capturing the stream into a graph records no memset node.
+__global__ __launch_bounds__(256) void k_zero_2d(uint8_t* __restrict__ p, int64_t ld_bytes, int64_t row_bytes,
+                                                 int64_t rows) {
+    const int64_t total = rows * row_bytes;
+    const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < total; i += stride) {
+        const int64_t r = i / row_bytes;
+        p[r * ld_bytes + (i - r * row_bytes)] = 0;
+    }
+}
+
+hipError_t launch_zero_2d(void* p, int64_t ld_bytes, int64_t row_bytes, int64_t rows, hipStream_t st) {
+    const int64_t total = rows * row_bytes;
+    if (total == 0) return hipSuccess;
+    int64_t blocks = (total + 255) / 256;
+    const int64_t cap = 8 * (int64_t)device_cu_count();
+    if (blocks > cap) blocks = cap;
+    k_zero_2d<<<dim3((unsigned)blocks), 256, 0, st>>>(static_cast<uint8_t*>(p), ld_bytes, row_bytes, rows);
+    return hipGetLastError();
+}
+
 // ---------------------------------------------------------------------
 // hipBLASLt bf16 GEMM, column-major: D[m x n] = op(A)[m x k] op(B)[k x n]
 // (+ beta D).  One handle per device, created on first use; the chosen

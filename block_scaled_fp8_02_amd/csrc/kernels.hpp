@@ -50,6 +50,8 @@ hipError_t launch_silu_mul_quant(const uint16_t* gate, int64_t ldg, const uint16
 // Dequantized-backward mode (dequant.hip): bf16 dequantization of FP8 codes
 // (kind 0: 1x128 row groups, 1: 128x128 blocks, 2: MX 1x32 E8M0) and the
 // plain bf16 GEMM through hipBLASLt (column-major, fp32 accumulation).
+// Zero a rows x row_bytes region with row stride ld_bytes (a kernel, not a memset).
+hipError_t launch_zero_2d(void* p, int64_t ld_bytes, int64_t row_bytes, int64_t rows, hipStream_t st);
 hipError_t launch_dequant_bf16(const uint8_t* q, int64_t ldq, const void* s, int64_t lds, int kind,
                                int64_t rows, int64_t cols, uint16_t* out, int64_t ldo, hipStream_t st);
 hipError_t lt_gemm(bool ta, bool tb, int64_t m, int64_t n, int64_t k,

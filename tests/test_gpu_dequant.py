@@ -148,3 +148,25 @@ def test_dequantized_backward_error_against_fp8_backward():
          "wgrad_deq": oracle.rel_row_error(dwb[drows], exact_dw)}
     banner("max row error vs exact: " + ", ".join(f"{k} {v:.3e}" for k, v in e.items()))
     assert e["dgrad_deq"] <= e["dgrad_fp8"] and e["wgrad_deq"] <= e["wgrad_fp8"], e
+
+
+def test_dequant_backward_empty_contraction_writes_zeros():
+    """An empty contraction (D = 0 for DGrad, N = 0 for WGrad) writes zeros
+    (with a fill kernel, not a memset) and leaves dW as it is with beta = 1."""
+    N, D, C = 130, 200, 300
+    banner("dequantized backward with an empty contraction")
+    dx = torch.full((N, C), 7.0, dtype=torch.bfloat16, device="cuda")
+    fb.fp8_dequant_gemm_dgrad(torch.empty((N, 0), dtype=torch.bfloat16, device="cuda"),
+                              torch.empty((0, 384), dtype=torch.uint8, device="cuda"),
+                              torch.empty((0, 3), dtype=torch.float32, device="cuda"),
+                              fb.FP8B_SCALE_BLOCKS_128X128, N, 0, C, dx=dx)
+    assert torch.all(dx == 0)
+    dy0 = torch.empty((0, D), dtype=torch.bfloat16, device="cuda")
+    xq0 = torch.empty((0, 384), dtype=torch.uint8, device="cuda")
+    xs0 = torch.empty((0, 3), dtype=torch.float32, device="cuda")
+    dw = torch.full((D, C), 7.0, dtype=torch.bfloat16, device="cuda")
+    fb.fp8_dequant_gemm_wgrad(dy0, xq0, xs0, fb.FP8B_SCALE_ROWS_1X128, 0, D, C, dw=dw)
+    assert torch.all(dw == 0)
+    dw32 = torch.full((D, C), 7.0, dtype=torch.float32, device="cuda")
+    fb.fp8_dequant_gemm_wgrad(dy0, xq0, xs0, fb.FP8B_SCALE_ROWS_1X128, 0, D, C, dw=dw32, beta=1)
+    assert torch.all(dw32 == 7.0)
