@@ -442,16 +442,20 @@ def fp8_gemm_wgrad_grouped(gqT, gsT, xqT, xsT, offsets, N, D, C, dw=None, out_dt
 
 
 # ---------------------------------------------------------------- MXFP8
-def fp8_mx_quantize_1x32(x, rowwise: bool = True, colwise: bool = True):
+def fp8_mx_quantize_1x32(x, rowwise: bool = True, colwise: bool = True, q=None, e=None, qT=None, eT=None):
     """-> (q [rows, rup(cols)], e [rows, rup(cols)/32], qT [cols, rup(rows)],
-    eT [cols, rup(rows)/32]); unrequested outputs are None."""
+    eT [cols, rup(rows)/32]); unrequested outputs are None.  Requested
+    outputs not passed in are allocated."""
     _check_2d(x, "x")
     rows, cols = x.shape
-    q = e = qT = eT = None
-    if rowwise:
+    if not rowwise:
+        q = e = None
+    elif q is None or e is None:
         q = _new((rows, _rup(cols)), torch.uint8, x.device)
         e = _new((rows, _rup(cols) // 32), torch.uint8, x.device)
-    if colwise:
+    if not colwise:
+        qT = eT = None
+    elif qT is None or eT is None:
         qT = _new((cols, _rup(rows)), torch.uint8, x.device)
         eT = _new((cols, _rup(rows) // 32), torch.uint8, x.device)
     _call("fp8_mx_quantize_1x32", _ptr(x), _dtype_code(x), rows, cols, _ld(x),
