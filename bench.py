@@ -577,6 +577,25 @@ def other_workloads(torch, fb, wl, dev, seed):
     dec["fprop"] = report(time_cold(torch, lambda: fb.fp8_gemm_fprop(xq, xs, wq, ws, N, D, C, y=y), flush),
                           N * C + D * C + N * cd(C, 128) * 4 + cd(D, 128) * cd(C, 128) * 4 + N * D * 2,
                           2.0 * N * D * C)
+    # the rollout step (quantize the activation, then FProp) as two eager
+    # launches and as one HIP graph replay of the same two kernels
+    def step():
+        fb.fp8_quantize_act_1x128(X, xq, xs)
+        fb.fp8_gemm_fprop(xq, xs, wq, ws, N, D, C, y=y)
+    step_bytes = (N * C * 2 + 2 * (N * C + N * cd(C, 128) * 4) + D * C + cd(D, 128) * cd(C, 128) * 4
+                  + N * D * 2)
+    dec["step_eager"] = report(time_cold(torch, step, flush), step_bytes, 2.0 * N * D * C)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        step()
+    dec["step_graph"] = report(time_cold(torch, graph.replay, flush), step_bytes, 2.0 * N * D * C)
+    del graph
     out["decode_1x128"] = dec
 
     # the same tensors through the MXFP8 path (plus dY [64 x 24576])
