@@ -145,6 +145,65 @@ def _ld(t):
     return t.stride(0) if t.shape[0] > 0 else max(t.shape[1], 1)
 
 
+_U8, _F32, _BF16 = (torch.uint8,), (torch.float32,), (torch.bfloat16,)
+_FLOAT_IO = (torch.bfloat16, torch.float32)
+
+
+def _need(t, name, rows, cols, dtypes, dev):
+    """t must be a row-major 2-D tensor on dev, of one of dtypes, with at
+    least rows x cols elements in its view: the library reads or writes
+    rows x cols at t's row stride, so a smaller view would be overrun."""
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a tensor")
+    _check_2d(t, name)
+    if t.device != dev:
+        raise ValueError(f"{name} is on {t.device}, expected {dev}")
+    if t.dtype not in dtypes:
+        raise TypeError(f"{name} has dtype {t.dtype}, expected one of {dtypes}")
+    if t.shape[0] < rows or t.shape[1] < cols:
+        raise ValueError(f"{name} is {tuple(t.shape)}, needs at least [{rows}, {cols}]")
+    return t
+
+
+def _need_scales(t, name, kind, rows, cols, dev):
+    """Scales of rows x cols codes in the layout `kind` (FP8B_SCALE_*)."""
+    if kind == FP8B_SCALE_ROWS_1X128:
+        return _need(t, name, rows, _cdiv(cols, 128), _F32, dev)
+    if kind == FP8B_SCALE_BLOCKS_128X128:
+        return _need(t, name, _cdiv(rows, 128), _cdiv(cols, 128), _F32, dev)
+    if kind == FP8B_SCALE_MX_1X32:
+        return _need(t, name, rows, _rup(cols) // 32, _U8, dev)
+    raise ValueError(f"unknown scale layout {kind}")
+
+
+def _extent(t) -> int:
+    """Elements addressable from t's first element (1 + the largest offset)."""
+    if t.numel() == 0:
+        return 0
+    return 1 + sum((n - 1) * st for n, st in zip(t.shape, t.stride()))
+
+
+def _need_stacked(t, name, E, estride, rows, ld, cols, dtypes, dev):
+    """E experts of rows x cols at row stride ld, estride elements apart."""
+    if not isinstance(t, torch.Tensor) or not t.is_cuda or t.device != dev:
+        raise ValueError(f"{name} must be a tensor on {dev}")
+    if t.dtype not in dtypes:
+        raise TypeError(f"{name} has dtype {t.dtype}, expected one of {dtypes}")
+    if E > 0 and rows > 0 and cols > 0:
+        need = (E - 1) * estride + (rows - 1) * ld + cols
+        if estride < 0 or ld < cols or need > _extent(t):
+            raise ValueError(f"{name} holds {_extent(t)} elements; {E} experts of {rows} x {cols} "
+                             f"(ld {ld}, stride {estride}) need {need}")
+    return t
+
+
+def _need_offsets(offsets, dev):
+    if (not isinstance(offsets, torch.Tensor) or offsets.device != dev or offsets.dtype != torch.int32
+            or offsets.dim() != 1 or not offsets.is_contiguous() or offsets.numel() < 2):
+        raise ValueError("offsets must be a contiguous int32 vector [E+1] on the device of the data")
+    return offsets.numel() - 1
+
+
 def _new(shape, dtype, dev):
     return torch.empty(shape, dtype=dtype, device=dev)
 
@@ -165,6 +224,8 @@ def fp8_quantize_act_1x128(x, q=None, s=None):
     rows, cols = x.shape
     q = _new((rows, _rup(cols)), torch.uint8, x.device) if q is None else q
     s = _new((rows, _cdiv(cols, 128)), torch.float32, x.device) if s is None else s
+    _need(q, "q", rows, _rup(cols), _U8, x.device)
+    _need(s, "s", rows, _cdiv(cols, 128), _F32, x.device)
     _call("fp8_quantize_act_1x128", _ptr(x), _dtype_code(x), rows, cols, _ld(x),
           _ptr(q), _ld(q), _ptr(s), _ld(s), _stream(x.device))
     return q, s
@@ -179,6 +240,10 @@ def fp8_quantize_weight_128x128(w, transpose: bool = True, q=None, s=None, qT=No
     s = _new((_cdiv(D, 128), _cdiv(C, 128)), torch.float32, w.device) if s is None else s
     if transpose and qT is None:
         qT = _new((C, _rup(D)), torch.uint8, w.device)
+    _need(q, "q", D, _rup(C), _U8, w.device)
+    _need(s, "s", _cdiv(D, 128), _cdiv(C, 128), _F32, w.device)
+    if qT is not None:
+        _need(qT, "qT", C, _rup(D), _U8, w.device)
     _call("fp8_quantize_weight_128x128", _ptr(w), _dtype_code(w), D, C, _ld(w),
           _ptr(q), _ld(q), _ptr(s), _ld(s), _ptr(qT), _ld(qT) if qT is not None else 0,
           _stream(w.device))
@@ -195,6 +260,11 @@ def fp8_quantize_transposed(x, rowwise: bool = False, qT=None, sT=None, q=None, 
     if rowwise and q is None:
         q = _new((rows, _rup(cols)), torch.uint8, x.device)
         s = _new((rows, _cdiv(cols, 128)), torch.float32, x.device)
+    _need(qT, "qT", cols, _rup(rows), _U8, x.device)
+    _need(sT, "sT", cols, _cdiv(rows, 128), _F32, x.device)
+    if q is not None or s is not None:
+        _need(q, "q", rows, _rup(cols), _U8, x.device)
+        _need(s, "s", rows, _cdiv(cols, 128), _F32, x.device)
     _call("fp8_quantize_transposed", _ptr(x), _dtype_code(x), rows, cols, _ld(x),
           _ptr(qT), _ld(qT), _ptr(sT), _ld(sT),
           _ptr(q), _ld(q) if q is not None else 0, _ptr(s), _ld(s) if s is not None else 0,
@@ -213,13 +283,18 @@ def fp8_quantize_transposed_grouped(x, offsets, rowwise: bool = False, qT=None, 
     expert's padded span are not written)."""
     _check_2d(x, "x")
     rows, cols = x.shape
-    E = offsets.numel() - 1
+    E = _need_offsets(offsets, x.device)
     P = grouped_token_capacity(rows, E)
     qT = _new((cols, P), torch.uint8, x.device) if qT is None else qT
     sT = _new((cols, P // 128), torch.float32, x.device) if sT is None else sT
     if rowwise and q is None:
         q = _new((rows, _rup(cols)), torch.uint8, x.device)
         s = _new((rows, _cdiv(cols, 128)), torch.float32, x.device)
+    _need(qT, "qT", cols, P, _U8, x.device)
+    _need(sT, "sT", cols, P // 128, _F32, x.device)
+    if q is not None or s is not None:
+        _need(q, "q", rows, _rup(cols), _U8, x.device)
+        _need(s, "s", rows, _cdiv(cols, 128), _F32, x.device)
     _call("fp8_quantize_transposed_grouped", _ptr(x), _dtype_code(x), rows, cols, _ld(x),
           _ptr(offsets), E, _ptr(qT), _ld(qT), _ptr(sT), _ld(sT),
           _ptr(q), _ld(q) if q is not None else 0, _ptr(s), _ld(s) if s is not None else 0,
@@ -235,14 +310,19 @@ def fp8_rmsnorm_quantize_1x128(x, w, eps: float = 1e-6, rstd: bool = False, y: b
     activation."""
     _check_2d(x, "x")
     rows, cols = x.shape
-    if w.dim() != 1 or w.shape[0] != cols or not w.is_contiguous():
-        raise ValueError("w must be a contiguous vector of length cols")
+    if (not isinstance(w, torch.Tensor) or w.dim() != 1 or w.shape[0] != cols or not w.is_contiguous()
+            or w.device != x.device):
+        raise ValueError("w must be a contiguous vector of length cols on the device of x")
     q = _new((rows, _rup(cols)), torch.uint8, x.device) if q is None else q
     s = _new((rows, _cdiv(cols, 128)), torch.float32, x.device) if s is None else s
+    _need(q, "q", rows, _rup(cols), _U8, x.device)
+    _need(s, "s", rows, _cdiv(cols, 128), _F32, x.device)
     if isinstance(rstd, torch.Tensor):
         r = rstd
-        if r.dtype != torch.float32 or r.numel() < rows or not r.is_contiguous():
-            raise ValueError("rstd must be a contiguous float32 tensor of at least rows elements")
+        if (r.dtype != torch.float32 or r.numel() < rows or not r.is_contiguous()
+                or r.device != x.device):
+            raise ValueError("rstd must be a contiguous float32 tensor of at least rows elements "
+                             "on the device of x")
     else:
         r = _new((rows,), torch.float32, x.device) if rstd else None
     yt = _new_out(rows, cols, torch.bfloat16, x.device) if y else None
@@ -258,11 +338,14 @@ def fp8_silu_mul_quantize_1x128(gate, up, a: bool = False, q=None, s=None):
     are fine), a the bf16 activation."""
     _check_2d(gate, "gate")
     _check_2d(up, "up")
-    if gate.shape != up.shape or gate.dtype != torch.bfloat16 or up.dtype != torch.bfloat16:
-        raise ValueError("gate and up must be bf16 tensors of one shape")
+    if (gate.shape != up.shape or gate.dtype != torch.bfloat16 or up.dtype != torch.bfloat16
+            or gate.device != up.device):
+        raise ValueError("gate and up must be bf16 tensors of one shape on one device")
     rows, cols = gate.shape
     q = _new((rows, _rup(cols)), torch.uint8, gate.device) if q is None else q
     s = _new((rows, _cdiv(cols, 128)), torch.float32, gate.device) if s is None else s
+    _need(q, "q", rows, _rup(cols), _U8, gate.device)
+    _need(s, "s", rows, _cdiv(cols, 128), _F32, gate.device)
     at = _new_out(rows, cols, torch.bfloat16, gate.device) if a else None
     _call("fp8_silu_mul_quantize_1x128", _ptr(gate), _ld(gate), _ptr(up), _ld(up), rows, cols,
           _ptr(q), _ld(q), _ptr(s), _ld(s), _ptr(at), _ld(at) if at is not None else 0, _stream(gate.device))
@@ -275,7 +358,10 @@ def fp8_dequantize_bf16(q, s, kind: int, cols: int, out=None):
     FP8B_SCALE_ROWS_1X128, FP8B_SCALE_BLOCKS_128X128, FP8B_SCALE_MX_1X32."""
     _check_2d(q, "q")
     rows = q.shape[0]
+    _need(q, "q", rows, _rup(cols), _U8, q.device)
+    _need_scales(s, "s", kind, rows, cols, q.device)
     out = _new_out(rows, cols, torch.bfloat16, q.device) if out is None else out
+    _need(out, "out", rows, cols, _BF16, q.device)
     _call("fp8_dequantize_bf16", _ptr(q), _ld(q), _ptr(s), _ld(s), int(kind), rows, cols,
           _ptr(out), _ld(out), _stream(q.device))
     return out
@@ -284,8 +370,14 @@ def fp8_dequantize_bf16(q, s, kind: int, cols: int, out=None):
 def fp8_dequant_gemm_dgrad(dy, wq, ws, wkind: int, N: int, D: int, C: int, dx=None, work=None):
     """dX = dY W^ in bf16 (hipBLASLt) with W^ the dequantized weight codes;
     work (D x C bf16) receives W^."""
-    dx = _new_out(N, C, torch.bfloat16, dy.device) if dx is None else dx
-    work = _new_out(D, C, torch.bfloat16, dy.device) if work is None else work
+    dev = dy.device
+    _need(dy, "dy", N, D, _BF16, dev)
+    _need(wq, "wq", D, _rup(C), _U8, dev)
+    _need_scales(ws, "ws", wkind, D, C, dev)
+    dx = _new_out(N, C, torch.bfloat16, dev) if dx is None else dx
+    work = _new_out(D, C, torch.bfloat16, dev) if work is None else work
+    _need(dx, "dx", N, C, _BF16, dev)
+    _need(work, "work", D, C, _BF16, dev)
     _call("fp8_dequant_gemm_dgrad", _ptr(dy), _ld(dy), _ptr(wq), _ld(wq), _ptr(ws), _ld(ws), int(wkind),
           N, D, C, _ptr(dx), _ld(dx), _ptr(work), _ld(work), _stream(dy.device))
     return dx
@@ -295,8 +387,14 @@ def fp8_dequant_gemm_wgrad(dy, xq, xs, xkind: int, N: int, D: int, C: int, dw=No
                            out_dtype=torch.bfloat16, beta: int = 0, work=None):
     """dW (+)= dY^T X^ in bf16 (hipBLASLt) with X^ the dequantized activation
     codes; work (N x C bf16) receives X^."""
-    dw = _new_out(D, C, out_dtype, dy.device) if dw is None else dw
-    work = _new_out(N, C, torch.bfloat16, dy.device) if work is None else work
+    dev = dy.device
+    _need(dy, "dy", N, D, _BF16, dev)
+    _need(xq, "xq", N, _rup(C), _U8, dev)
+    _need_scales(xs, "xs", xkind, N, C, dev)
+    dw = _new_out(D, C, out_dtype, dev) if dw is None else dw
+    work = _new_out(N, C, torch.bfloat16, dev) if work is None else work
+    _need(dw, "dw", D, C, _FLOAT_IO, dev)
+    _need(work, "work", N, C, _BF16, dev)
     _call("fp8_dequant_gemm_wgrad", _ptr(dy), _ld(dy), _ptr(xq), _ld(xq), _ptr(xs), _ld(xs), int(xkind),
           N, D, C, _ptr(dw), _out_dtype_code(dw.dtype), _ld(dw), int(beta), _ptr(work), _ld(work),
           _stream(dy.device))
@@ -309,8 +407,12 @@ def fp8_requantize_transposed(q, s, cols: int, qT=None, sT=None):
     scales s -> (qT [cols, rup(rows)], sT [cols, ceil(rows/128)])."""
     _check_2d(q, "q")
     rows = q.shape[0]
+    _need(q, "q", rows, _rup(cols), _U8, q.device)
+    _need(s, "s", rows, _cdiv(cols, 128), _F32, q.device)
     qT = _new((cols, _rup(rows)), torch.uint8, q.device) if qT is None else qT
     sT = _new((cols, _cdiv(rows, 128)), torch.float32, q.device) if sT is None else sT
+    _need(qT, "qT", cols, _rup(rows), _U8, q.device)
+    _need(sT, "sT", cols, _cdiv(rows, 128), _F32, q.device)
     _call("fp8_requantize_transposed", _ptr(q), _ld(q), _ptr(s), _ld(s), rows, cols,
           _ptr(qT), _ld(qT), _ptr(sT), _ld(sT), _stream(q.device))
     return qT, sT
@@ -320,7 +422,9 @@ def fp8_requantize_transposed_grouped(q, s, cols: int, offsets):
     """Grouped form; layout as fp8_quantize_transposed_grouped."""
     _check_2d(q, "q")
     rows = q.shape[0]
-    E = offsets.numel() - 1
+    _need(q, "q", rows, _rup(cols), _U8, q.device)
+    _need(s, "s", rows, _cdiv(cols, 128), _F32, q.device)
+    E = _need_offsets(offsets, q.device)
     P = grouped_token_capacity(rows, E)
     qT = _new((cols, P), torch.uint8, q.device)
     sT = _new((cols, P // 128), torch.float32, q.device)
@@ -384,22 +488,48 @@ def fp8_quantize_transposed_pow2(x, rowwise: bool = False, e8: bool = True):
 
 
 # ---------------------------------------------------------------- GEMMs
+def _need_gemm(dev, a, sa, b, sb, M, Nn, K, a_name, b_name, b_blocks=False, mx=False):
+    """Operands of O [M x Nn] = A [M x K] B [Nn x K]^T: codes padded to
+    round_up(K, 128); scales per row (1x128 or MX 1x32), or for a 128x128
+    weight the grid over (Nn, K) (FProp) given as rows x cols here."""
+    _need(a, a_name, M, _rup(K), _U8, dev)
+    _need(b, b_name, Nn, _rup(K), _U8, dev)
+    if mx:
+        _need(sa, a_name + " scales", M, _rup(K) // 32, _U8, dev)
+        _need(sb, b_name + " scales", Nn, _rup(K) // 32, _U8, dev)
+    else:
+        _need(sa, a_name + " scales", M, _cdiv(K, 128), _F32, dev)
+        if not b_blocks:
+            _need(sb, b_name + " scales", Nn, _cdiv(K, 128), _F32, dev)
+
+
 def fp8_gemm_fprop(xq, xs, wq, ws, N, D, C, y=None, out_dtype=torch.bfloat16):
-    y = _new_out(N, D, out_dtype, xq.device) if y is None else y
+    dev = xq.device
+    _need_gemm(dev, xq, xs, wq, ws, N, D, C, "xq", "wq", b_blocks=True)
+    _need(ws, "ws", _cdiv(D, 128), _cdiv(C, 128), _F32, dev)
+    y = _new_out(N, D, out_dtype, dev) if y is None else y
+    _need(y, "y", N, D, _FLOAT_IO, dev)
     _call("fp8_gemm_fprop", _ptr(xq), _ld(xq), _ptr(xs), _ld(xs), _ptr(wq), _ld(wq), _ptr(ws), _ld(ws),
           _ptr(y), _out_dtype_code(y.dtype), _ld(y), N, D, C, _stream(xq.device))
     return y
 
 
 def fp8_gemm_dgrad(gq, gs, wqT, ws, N, D, C, dx=None, out_dtype=torch.bfloat16):
-    dx = _new_out(N, C, out_dtype, gq.device) if dx is None else dx
+    dev = gq.device
+    _need_gemm(dev, gq, gs, wqT, ws, N, C, D, "gq", "wqT", b_blocks=True)
+    _need(ws, "ws", _cdiv(D, 128), _cdiv(C, 128), _F32, dev)
+    dx = _new_out(N, C, out_dtype, dev) if dx is None else dx
+    _need(dx, "dx", N, C, _FLOAT_IO, dev)
     _call("fp8_gemm_dgrad", _ptr(gq), _ld(gq), _ptr(gs), _ld(gs), _ptr(wqT), _ld(wqT), _ptr(ws), _ld(ws),
           _ptr(dx), _out_dtype_code(dx.dtype), _ld(dx), N, D, C, _stream(gq.device))
     return dx
 
 
 def fp8_gemm_wgrad(gqT, gsT, xqT, xsT, N, D, C, dw=None, out_dtype=torch.bfloat16, beta: int = 0):
-    dw = _new_out(D, C, out_dtype, gqT.device) if dw is None else dw
+    dev = gqT.device
+    _need_gemm(dev, gqT, gsT, xqT, xsT, D, C, N, "gqT", "xqT")
+    dw = _new_out(D, C, out_dtype, dev) if dw is None else dw
+    _need(dw, "dw", D, C, _FLOAT_IO, dev)
     _call("fp8_gemm_wgrad", _ptr(gqT), _ld(gqT), _ptr(gsT), _ld(gsT), _ptr(xqT), _ld(xqT),
           _ptr(xsT), _ld(xsT), _ptr(dw), _out_dtype_code(dw.dtype), _ld(dw), beta, N, D, C,
           _stream(gqT.device))
@@ -410,8 +540,14 @@ def fp8_gemm_fprop_grouped(xq, xs, wq, wq_estride, ws, ws_estride, offsets, N, D
                            out_dtype=torch.bfloat16, ldwq=None, ldws=None):
     """wq/ws hold all experts (e.g. stacked [E*D, C] from one fp8_quantize_weight_128x128 call);
     ldwq/ldws default to their row strides."""
-    y = _new_out(N, D, out_dtype, xq.device) if y is None else y
-    E = offsets.numel() - 1
+    dev = xq.device
+    E = _need_offsets(offsets, dev)
+    _need(xq, "xq", N, _rup(C), _U8, dev)
+    _need(xs, "xs", N, _cdiv(C, 128), _F32, dev)
+    _need_stacked(wq, "wq", E, wq_estride, D, ldwq or _ld(wq), _rup(C), _U8, dev)
+    _need_stacked(ws, "ws", E, ws_estride, _cdiv(D, 128), ldws or _ld(ws), _cdiv(C, 128), _F32, dev)
+    y = _new_out(N, D, out_dtype, dev) if y is None else y
+    _need(y, "y", N, D, _FLOAT_IO, dev)
     _call("fp8_gemm_fprop_grouped", _ptr(xq), _ld(xq), _ptr(xs), _ld(xs),
           _ptr(wq), ldwq or _ld(wq), wq_estride, _ptr(ws), ldws or _ld(ws), ws_estride,
           _ptr(y), _out_dtype_code(y.dtype), _ld(y), _ptr(offsets), E, N, D, C, _stream(xq.device))
@@ -420,8 +556,14 @@ def fp8_gemm_fprop_grouped(xq, xs, wq, wq_estride, ws, ws_estride, offsets, N, D
 
 def fp8_gemm_dgrad_grouped(gq, gs, wqT, wqT_estride, ws, ws_estride, offsets, N, D, C, dx=None,
                            out_dtype=torch.bfloat16, ldwqT=None, ldws=None):
-    dx = _new_out(N, C, out_dtype, gq.device) if dx is None else dx
-    E = offsets.numel() - 1
+    dev = gq.device
+    E = _need_offsets(offsets, dev)
+    _need(gq, "gq", N, _rup(D), _U8, dev)
+    _need(gs, "gs", N, _cdiv(D, 128), _F32, dev)
+    _need_stacked(wqT, "wqT", E, wqT_estride, C, ldwqT or _ld(wqT), _rup(D), _U8, dev)
+    _need_stacked(ws, "ws", E, ws_estride, _cdiv(D, 128), ldws or _ld(ws), _cdiv(C, 128), _F32, dev)
+    dx = _new_out(N, C, out_dtype, dev) if dx is None else dx
+    _need(dx, "dx", N, C, _FLOAT_IO, dev)
     _call("fp8_gemm_dgrad_grouped", _ptr(gq), _ld(gq), _ptr(gs), _ld(gs),
           _ptr(wqT), ldwqT or _ld(wqT), wqT_estride, _ptr(ws), ldws or _ld(ws), ws_estride,
           _ptr(dx), _out_dtype_code(dx.dtype), _ld(dx), _ptr(offsets), E, N, D, C, _stream(gq.device))
@@ -431,10 +573,20 @@ def fp8_gemm_dgrad_grouped(gq, gs, wqT, wqT_estride, ws, ws_estride, offsets, N,
 def fp8_gemm_wgrad_grouped(gqT, gsT, xqT, xsT, offsets, N, D, C, dw=None, out_dtype=torch.bfloat16,
                            beta: int = 0):
     """dW for every expert -> dw [E, D, C]."""
-    E = offsets.numel() - 1
+    dev = gqT.device
+    E = _need_offsets(offsets, dev)
+    P = grouped_token_capacity(N, E)
+    _need(gqT, "gqT", D, P, _U8, dev)
+    _need(gsT, "gsT", D, P // 128, _F32, dev)
+    _need(xqT, "xqT", C, P, _U8, dev)
+    _need(xsT, "xsT", C, P // 128, _F32, dev)
     if dw is None:
         per16 = 16 // (2 if out_dtype == torch.bfloat16 else 4)
-        dw = torch.empty((E, D, max(_rup(C, per16), per16)), dtype=out_dtype, device=gqT.device)[:, :, :C]
+        dw = torch.empty((E, D, max(_rup(C, per16), per16)), dtype=out_dtype, device=dev)[:, :, :C]
+    if (not isinstance(dw, torch.Tensor) or dw.dim() != 3 or dw.device != dev or dw.dtype not in _FLOAT_IO
+            or dw.shape[0] < E or dw.shape[1] < D or dw.shape[2] < C
+            or (dw.shape[2] > 1 and dw.stride(2) != 1)):
+        raise ValueError(f"dw must be a row-major [>= {E}, >= {D}, >= {C}] bf16 or float32 tensor on {dev}")
     _call("fp8_gemm_wgrad_grouped", _ptr(gqT), _ld(gqT), _ptr(gsT), _ld(gsT), _ptr(xqT), _ld(xqT),
           _ptr(xsT), _ld(xsT), _ptr(dw), _out_dtype_code(dw.dtype), dw.stride(1), dw.stride(0), beta,
           _ptr(offsets), E, N, D, C, _stream(gqT.device))
@@ -458,6 +610,12 @@ def fp8_mx_quantize_1x32(x, rowwise: bool = True, colwise: bool = True, q=None, 
     elif qT is None or eT is None:
         qT = _new((cols, _rup(rows)), torch.uint8, x.device)
         eT = _new((cols, _rup(rows) // 32), torch.uint8, x.device)
+    if q is not None:
+        _need(q, "q", rows, _rup(cols), _U8, x.device)
+        _need(e, "e", rows, _rup(cols) // 32, _U8, x.device)
+    if qT is not None:
+        _need(qT, "qT", cols, _rup(rows), _U8, x.device)
+        _need(eT, "eT", cols, _rup(rows) // 32, _U8, x.device)
     _call("fp8_mx_quantize_1x32", _ptr(x), _dtype_code(x), rows, cols, _ld(x),
           _ptr(q), _ld(q) if q is not None else 0, _ptr(e), _ld(e) if e is not None else 0,
           _ptr(qT), _ld(qT) if qT is not None else 0, _ptr(eT), _ld(eT) if eT is not None else 0,
@@ -466,21 +624,30 @@ def fp8_mx_quantize_1x32(x, rowwise: bool = True, colwise: bool = True, q=None, 
 
 
 def fp8_mx_gemm_fprop(xq, xe, wq, we, N, D, C, y=None, out_dtype=torch.bfloat16):
-    y = _new_out(N, D, out_dtype, xq.device) if y is None else y
+    dev = xq.device
+    _need_gemm(dev, xq, xe, wq, we, N, D, C, "xq", "wq", mx=True)
+    y = _new_out(N, D, out_dtype, dev) if y is None else y
+    _need(y, "y", N, D, _FLOAT_IO, dev)
     _call("fp8_mx_gemm_fprop", _ptr(xq), _ld(xq), _ptr(xe), _ld(xe), _ptr(wq), _ld(wq), _ptr(we), _ld(we),
           _ptr(y), _out_dtype_code(y.dtype), _ld(y), N, D, C, _stream(xq.device))
     return y
 
 
 def fp8_mx_gemm_dgrad(gq, ge, wqT, weT, N, D, C, dx=None, out_dtype=torch.bfloat16):
-    dx = _new_out(N, C, out_dtype, gq.device) if dx is None else dx
+    dev = gq.device
+    _need_gemm(dev, gq, ge, wqT, weT, N, C, D, "gq", "wqT", mx=True)
+    dx = _new_out(N, C, out_dtype, dev) if dx is None else dx
+    _need(dx, "dx", N, C, _FLOAT_IO, dev)
     _call("fp8_mx_gemm_dgrad", _ptr(gq), _ld(gq), _ptr(ge), _ld(ge), _ptr(wqT), _ld(wqT), _ptr(weT),
           _ld(weT), _ptr(dx), _out_dtype_code(dx.dtype), _ld(dx), N, D, C, _stream(gq.device))
     return dx
 
 
 def fp8_mx_gemm_wgrad(gqT, geT, xqT, xeT, N, D, C, dw=None, out_dtype=torch.bfloat16, beta: int = 0):
-    dw = _new_out(D, C, out_dtype, gqT.device) if dw is None else dw
+    dev = gqT.device
+    _need_gemm(dev, gqT, geT, xqT, xeT, D, C, N, "gqT", "xqT", mx=True)
+    dw = _new_out(D, C, out_dtype, dev) if dw is None else dw
+    _need(dw, "dw", D, C, _FLOAT_IO, dev)
     _call("fp8_mx_gemm_wgrad", _ptr(gqT), _ld(gqT), _ptr(geT), _ld(geT), _ptr(xqT), _ld(xqT), _ptr(xeT),
           _ld(xeT), _ptr(dw), _out_dtype_code(dw.dtype), _ld(dw), beta, N, D, C, _stream(gqT.device))
     return dw
@@ -488,7 +655,14 @@ def fp8_mx_gemm_wgrad(gqT, geT, xqT, xeT, N, D, C, dw=None, out_dtype=torch.bflo
 
 # ----------------------------------------------------------------- misc
 def fp8b_e4m3_encode(x, s=None, out=None):
+    if not isinstance(x, torch.Tensor) or not x.is_cuda or x.dtype != torch.float32 or not x.is_contiguous():
+        raise ValueError("x must be a contiguous float32 GPU tensor")
+    if s is not None and (s.device != x.device or s.dtype != torch.float32 or not s.is_contiguous()
+                          or s.numel() < x.numel()):
+        raise ValueError("s must be a contiguous float32 tensor with one divisor per element of x")
     out = _new(x.shape, torch.uint8, x.device) if out is None else out
+    if out.device != x.device or out.dtype != torch.uint8 or not out.is_contiguous() or out.numel() < x.numel():
+        raise ValueError("out must be a contiguous uint8 tensor with one byte per element of x")
     _call("fp8b_e4m3_encode", _ptr(x), _ptr(s), x.numel(), _ptr(out), _stream(x.device))
     return out
 
