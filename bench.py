@@ -567,7 +567,7 @@ def other_workloads(torch, fb, wl, dev, seed):
     N, C, D = w["N"], w["C"], w["D"]
     X, W, dY = to(w["X"]), to(w["W"]), to(w["dY"])
     xq, xs = fb.fp8_quantize_act_1x128(X)
-    wq, ws, _ = fb.fp8_quantize_weight_128x128(W, transpose=False)
+    wq, ws, wqT = fb.fp8_quantize_weight_128x128(W, transpose=True)
     y = torch.empty((N, D), dtype=torch.bfloat16, device=dev)
     dec = {}
     dec["quant_act_1x128"] = report(time_cold(torch, lambda: fb.fp8_quantize_act_1x128(X, xq, xs), flush),
@@ -596,6 +596,21 @@ def other_workloads(torch, fb, wl, dev, seed):
         step()
     dec["step_graph"] = report(time_cold(torch, graph.replay, flush), step_bytes, 2.0 * N * D * C)
     del graph
+    # the backward GEMMs of the same 64-token layer on the 1x128 / 128x128
+    # path (the MXFP8 section below times the same three GEMMs): DGrad with
+    # dY [64 x 24576] quantized along D (split along K, 64 rows), WGrad with
+    # both operands quantized along the 64-token axis (one partial group)
+    gq, gs = fb.fp8_quantize_act_1x128(dY)
+    gqT, gsT, _, _ = fb.fp8_quantize_transposed(dY)
+    xqT, xsT, _, _ = fb.fp8_quantize_transposed(X)
+    dx1 = torch.empty((N, C), dtype=torch.bfloat16, device=dev)
+    dw1 = torch.empty((D, C), dtype=torch.bfloat16, device=dev)
+    dec["dgrad"] = report(time_cold(torch, lambda: fb.fp8_gemm_dgrad(gq, gs, wqT, ws, N, D, C, dx=dx1), flush),
+                          N * D + D * C + N * cd(D, 128) * 4 + cd(D, 128) * cd(C, 128) * 4 + N * C * 2,
+                          2.0 * N * D * C)
+    dec["wgrad"] = report(time_cold(torch, lambda: fb.fp8_gemm_wgrad(gqT, gsT, xqT, xsT, N, D, C, dw=dw1), flush),
+                          (D + C) * 128 + (D + C) * 4 + D * C * 2, 2.0 * N * D * C)
+    del gq, gqT, xqT, dx1, dw1, wqT
     out["decode_1x128"] = dec
 
     # the same tensors through the MXFP8 path (plus dY [64 x 24576])

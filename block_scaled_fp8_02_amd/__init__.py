@@ -63,6 +63,9 @@ _SIGS = {
     "fp8_requantize_transposed_grouped": [_p, _i64, _p, _i64, _i64, _i64, _p, _i64, _p, _i64, _p, _i64, _p],
     "fp8_gemm_fprop": [_p, _i64, _p, _i64, _p, _i64, _p, _i64, _p, _i32, _i64, _i64, _i64, _i64, _p],
     "fp8_gemm_dgrad": [_p, _i64, _p, _i64, _p, _i64, _p, _i64, _p, _i32, _i64, _i64, _i64, _i64, _p],
+    "fp8_gemm_dgrad_split_bytes": [_i64, _i64, _i64],
+    "fp8_gemm_dgrad_split": [_p, _i64, _p, _i64, _p, _i64, _p, _i64, _p, _i32, _i64, _i64, _i64, _i64,
+                             _p, _i64, _p],
     "fp8_gemm_wgrad": [_p, _i64, _p, _i64, _p, _i64, _p, _i64, _p, _i32, _i64, _i32, _i64, _i64, _i64, _p],
     "fp8_gemm_fprop_grouped": [_p, _i64, _p, _i64, _p, _i64, _i64, _p, _i64, _i64, _p, _i32, _i64,
                                _p, _i64, _i64, _i64, _i64, _p],
@@ -73,6 +76,8 @@ _SIGS = {
     "fp8_mx_quantize_1x32": [_p, _i32, _i64, _i64, _i64, _p, _i64, _p, _i64, _p, _i64, _p, _i64, _p],
     "fp8_mx_gemm_fprop": [_p, _i64, _p, _i64, _p, _i64, _p, _i64, _p, _i32, _i64, _i64, _i64, _i64, _p],
     "fp8_mx_gemm_dgrad": [_p, _i64, _p, _i64, _p, _i64, _p, _i64, _p, _i32, _i64, _i64, _i64, _i64, _p],
+    "fp8_mx_gemm_dgrad_split": [_p, _i64, _p, _i64, _p, _i64, _p, _i64, _p, _i32, _i64, _i64, _i64, _i64,
+                                _p, _i64, _p],
     "fp8_mx_gemm_wgrad": [_p, _i64, _p, _i64, _p, _i64, _p, _i64, _p, _i32, _i64, _i32, _i64, _i64, _i64, _p],
     "fp8b_e4m3_encode": [_p, _p, _i64, _p, _p],
     "fp8b_validate_gemm": [_i32, _p, _i64, _p, _i64, _p, _i64, _p, _i64, _p, _i32, _i64, _i32,
@@ -95,7 +100,8 @@ def lib():
         for name, args in _SIGS.items():
             fn = getattr(L, name)
             fn.argtypes = args
-            fn.restype = ctypes.c_char_p if name == "fp8b_status_string" else ctypes.c_int
+            fn.restype = {"fp8b_status_string": ctypes.c_char_p,
+                          "fp8_gemm_dgrad_split_bytes": ctypes.c_int64}.get(name, ctypes.c_int)
         _lib = L
     return _lib
 
@@ -520,9 +526,23 @@ def fp8_gemm_dgrad(gq, gs, wqT, ws, N, D, C, dx=None, out_dtype=torch.bfloat16):
     _need(ws, "ws", _cdiv(D, 128), _cdiv(C, 128), _F32, dev)
     dx = _new_out(N, C, out_dtype, dev) if dx is None else dx
     _need(dx, "dx", N, C, _FLOAT_IO, dev)
-    _call("fp8_gemm_dgrad", _ptr(gq), _ld(gq), _ptr(gs), _ld(gs), _ptr(wqT), _ld(wqT), _ptr(ws), _ld(ws),
-          _ptr(dx), _out_dtype_code(dx.dtype), _ld(dx), N, D, C, _stream(gq.device))
+    args = (_ptr(gq), _ld(gq), _ptr(gs), _ld(gs), _ptr(wqT), _ld(wqT), _ptr(ws), _ld(ws),
+            _ptr(dx), _out_dtype_code(dx.dtype), _ld(dx), N, D, C)
+    work = dgrad_split_workspace(N, D, C, dev)
+    if work is None:
+        _call("fp8_gemm_dgrad", *args, _stream(gq.device))
+    else:
+        _call("fp8_gemm_dgrad_split", *args, _ptr(work), work.numel(), _stream(gq.device))
     return dx
+
+
+def dgrad_split_workspace(N: int, D: int, C: int, dev):
+    """fp32 partial-sum workspace of the K-split DGrad for this shape (a
+    uint8 tensor from torch's allocator, live until the caller drops it), or
+    None when no split applies."""
+    with torch.cuda.device(dev):
+        nbytes = lib().fp8_gemm_dgrad_split_bytes(N, D, C)
+    return None if nbytes <= 0 else torch.empty((nbytes,), dtype=torch.uint8, device=dev)
 
 
 def fp8_gemm_wgrad(gqT, gsT, xqT, xsT, N, D, C, dw=None, out_dtype=torch.bfloat16, beta: int = 0):
@@ -638,8 +658,13 @@ def fp8_mx_gemm_dgrad(gq, ge, wqT, weT, N, D, C, dx=None, out_dtype=torch.bfloat
     _need_gemm(dev, gq, ge, wqT, weT, N, C, D, "gq", "wqT", mx=True)
     dx = _new_out(N, C, out_dtype, dev) if dx is None else dx
     _need(dx, "dx", N, C, _FLOAT_IO, dev)
-    _call("fp8_mx_gemm_dgrad", _ptr(gq), _ld(gq), _ptr(ge), _ld(ge), _ptr(wqT), _ld(wqT), _ptr(weT),
-          _ld(weT), _ptr(dx), _out_dtype_code(dx.dtype), _ld(dx), N, D, C, _stream(gq.device))
+    args = (_ptr(gq), _ld(gq), _ptr(ge), _ld(ge), _ptr(wqT), _ld(wqT), _ptr(weT), _ld(weT),
+            _ptr(dx), _out_dtype_code(dx.dtype), _ld(dx), N, D, C)
+    work = dgrad_split_workspace(N, D, C, dev)
+    if work is None:
+        _call("fp8_mx_gemm_dgrad", *args, _stream(gq.device))
+    else:
+        _call("fp8_mx_gemm_dgrad_split", *args, _ptr(work), work.numel(), _stream(gq.device))
     return dx
 
 

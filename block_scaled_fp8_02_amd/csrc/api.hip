@@ -411,6 +411,55 @@ static int gemm_dense(int op, const void* a, int64_t lda, const void* sa, int64_
     return hip_status(launch_gemm(g, static_cast<hipStream_t>(stream)));
 }
 
+// K split of a few-row DGrad (op 1 or 4): number of K ranges (1: none) and
+// K blocks per range.  About one block per compute unit over the 128-column
+// output tiles, at least 8 K blocks per range.
+static void dgrad_split_plan(int64_t N, int64_t D, int64_t C, int64_t* S, int64_t* kbs) {
+    *S = 1;
+    *kbs = 0;
+    if (N <= 0 || N > 64 || C <= 0 || D <= 0) return;
+    const int64_t KB = cdiv(D, 128), nbj = cdiv(C, 128), cus = device_cu_count();
+    if (KB < 16 || 2 * nbj > cus) return;
+    int64_t s = cus / nbj;
+    if (s > KB / 8) s = KB / 8;
+    if (s < 2) return;
+    const int64_t k = cdiv(KB, s);
+    *S = cdiv(KB, k);
+    *kbs = k;
+}
+
+// fp32 partial rows of the split: row stride rounded up to 4 floats (16 bytes).
+static inline int64_t split_ld(int64_t C) { return (C + 3) / 4 * 4; }
+
+static int64_t dgrad_split_bytes(int64_t N, int64_t D, int64_t C) {
+    int64_t S, kbs;
+    dgrad_split_plan(N, D, C, &S, &kbs);
+    return S < 2 ? 0 : S * N * split_ld(C) * 4;
+}
+
+static int gemm_dgrad_split(int op, const void* a, int64_t lda, const void* sa, int64_t ldsa,
+                     const void* b, int64_t ldb, const void* sb, int64_t ldsb,
+                     void* out, int odt, int64_t ldo, int64_t N, int64_t D, int64_t C,
+                     void* work, int64_t work_bytes, void* stream) {
+    FP8B_TRY(validate_gemm(op, a, lda, sa, ldsa, b, ldb, sb, ldsb, out, odt, ldo, 0, N, D, C));
+    const hipStream_t st = static_cast<hipStream_t>(stream);
+    const GemmArgs g = dense_args(op, a, lda, sa, ldsa, b, ldb, sb, ldsb, out, odt, ldo, 0, N, D, C);
+    int64_t S, kbs;
+    dgrad_split_plan(N, D, C, &S, &kbs);
+    if (S < 2) return hip_status(launch_gemm(g, st));
+    if (work == nullptr) return FP8B_EINVAL;
+    if (!aligned(work, 16)) return FP8B_EALIGN;
+    const int64_t ldp = split_ld(C);
+    if (work_bytes < S * N * ldp * 4) return FP8B_ESHAPE;
+    GemmArgs p = g;
+    p.O = work; p.out_f32 = true; p.ldo = ldp; p.beta = 0;
+    p.o_estride = N * ldp;
+    p.ksplit = S; p.kb_split = kbs;
+    FP8B_TRY(hip_status(launch_gemm(p, st)));
+    return hip_status(launch_split_sum(static_cast<const float*>(work), S, N * ldp, ldp, N, C,
+                                       out, odt == FP8B_F32, ldo, st));
+}
+
 int fp8_gemm_fprop(const uint8_t* xq, int64_t ldxq, const float* xs, int64_t ldxs,
                    const uint8_t* wq, int64_t ldwq, const float* ws, int64_t ldws,
                    void* y, int yt, int64_t ldy, int64_t N, int64_t D, int64_t C, void* stream) {
@@ -421,6 +470,16 @@ int fp8_gemm_dgrad(const uint8_t* gq, int64_t ldgq, const float* gs, int64_t ldg
                    const uint8_t* wqT, int64_t ldwqT, const float* ws, int64_t ldws,
                    void* dx, int dxt, int64_t lddx, int64_t N, int64_t D, int64_t C, void* stream) {
     return gemm_dense(1, gq, ldgq, gs, ldgs, wqT, ldwqT, ws, ldws, dx, dxt, lddx, 0, N, D, C, stream);
+}
+
+int64_t fp8_gemm_dgrad_split_bytes(int64_t N, int64_t D, int64_t C) { return dgrad_split_bytes(N, D, C); }
+
+int fp8_gemm_dgrad_split(const uint8_t* gq, int64_t ldgq, const float* gs, int64_t ldgs,
+                         const uint8_t* wqT, int64_t ldwqT, const float* ws, int64_t ldws,
+                         void* dx, int dxt, int64_t lddx, int64_t N, int64_t D, int64_t C,
+                         void* work, int64_t work_bytes, void* stream) {
+    return gemm_dgrad_split(1, gq, ldgq, gs, ldgs, wqT, ldwqT, ws, ldws, dx, dxt, lddx, N, D, C,
+                            work, work_bytes, stream);
 }
 
 int fp8_gemm_wgrad(const uint8_t* gqT, int64_t ldgqT, const float* gsT, int64_t ldgsT,
@@ -514,6 +573,14 @@ int fp8_mx_gemm_dgrad(const uint8_t* gq, int64_t ldgq, const uint8_t* ge, int64_
                       const uint8_t* wqT, int64_t ldwqT, const uint8_t* weT, int64_t ldweT,
                       void* dx, int dxt, int64_t lddx, int64_t N, int64_t D, int64_t C, void* stream) {
     return gemm_dense(4, gq, ldgq, ge, ldge, wqT, ldwqT, weT, ldweT, dx, dxt, lddx, 0, N, D, C, stream);
+}
+
+int fp8_mx_gemm_dgrad_split(const uint8_t* gq, int64_t ldgq, const uint8_t* ge, int64_t ldge,
+                            const uint8_t* wqT, int64_t ldwqT, const uint8_t* weT, int64_t ldweT,
+                            void* dx, int dxt, int64_t lddx, int64_t N, int64_t D, int64_t C,
+                            void* work, int64_t work_bytes, void* stream) {
+    return gemm_dgrad_split(4, gq, ldgq, ge, ldge, wqT, ldwqT, weT, ldweT, dx, dxt, lddx, N, D, C,
+                            work, work_bytes, stream);
 }
 
 int fp8_mx_gemm_wgrad(const uint8_t* gqT, int64_t ldgqT, const uint8_t* geT, int64_t ldgeT,

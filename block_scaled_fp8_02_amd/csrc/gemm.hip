@@ -196,6 +196,13 @@ __global__ __launch_bounds__(64 * NW, 1) void k_gemm(GemmArgs g) {
             kbase = uniform64(tinfo[0]);
             KB = uniform64(tinfo[1]);
         }
+        if (GM == GROUP_NONE && g.ksplit > 1) {
+            // K split: block row y runs K blocks [y * kb_split, (y + 1) * kb_split)
+            // (ascending) into its own fp32 slice of partial sums
+            kbase = (int64_t)blockIdx.y * g.kb_split;
+            KB = KB - kbase < g.kb_split ? KB - kbase : g.kb_split;
+            O += (int64_t)blockIdx.y * g.o_estride * (int64_t)o_elem;
+        }
     }
     const int64_t jhi = j0 + BJ < g.Nn ? j0 + BJ : g.Nn;
 
@@ -684,6 +691,7 @@ static hipError_t launch_cfg(const GemmArgs& args, hipStream_t st) {
             a.epb = epb;
             z = (a.E + epb - 1) / epb;
         }
+        if (a.group_mode == GROUP_NONE && a.ksplit > 1) z = a.ksplit;
         if (tiles == 0 || z == 0) return hipSuccess;
         if (tiles > 0x7FFFFFFF || z > 65535) return hipErrorInvalidValue;
         grid = dim3((unsigned)tiles, (unsigned)z, 1);
@@ -703,6 +711,9 @@ static hipError_t launch_sm(const GemmArgs& a, hipStream_t st) {
     // least one block per compute unit, with 4 or 8 stages in flight.  The
     // per-element arithmetic is the same in every configuration.
     if (a.M <= 64 && a.group_mode == GROUP_NONE) {
+        // K split into ranges (few-row DGrad, where the output has too few
+        // tiles to occupy the chip): 128-row weight tiles as for a large weight
+        if (a.ksplit > 1) return launch_cfg<64, 128, 4, 1, 8, SM, 4, GROUP_NONE>(a, st);
         if ((a.Nn + 127) / 128 >= 192) return launch_cfg<64, 128, 4, 1, 8, SM, 4, GROUP_NONE>(a, st);
         if ((a.Nn + 31) / 32 >= 512) return launch_cfg<64, 32, 4, 1, 2, SM, 4, GROUP_NONE>(a, st);
         return launch_cfg<64, 16, 2, 1, 2, SM, 8, GROUP_NONE>(a, st);
@@ -713,6 +724,54 @@ static hipError_t launch_sm(const GemmArgs& a, hipStream_t st) {
         case GROUP_K: return launch_cfg<256, 256, 4, 8, 8, SM, 2, GROUP_K>(a, st);
         default: return hipErrorInvalidValue;
     }
+}
+
+// Sum of the K ranges' fp32 partial outputs, ascending in the range index:
+// four consecutive outputs of one row per thread.
+__global__ __launch_bounds__(256) void k_split_sum(const float* __restrict__ part, int64_t S, int64_t slice,
+                                                   int64_t ldp, int64_t M, int64_t Nn, void* __restrict__ out,
+                                                   bool out_f32, int64_t ldo) {
+    const int64_t n4 = (Nn + 3) / 4;
+    const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (idx >= M * n4) return;
+    const int64_t i = idx / n4, j = (idx - i * n4) * 4;
+    const int nv = Nn - j < 4 ? (int)(Nn - j) : 4;
+    float acc[4] = {0.f, 0.f, 0.f, 0.f};
+    for (int64_t s = 0; s < S; ++s) {
+        const float* p = part + s * slice + i * ldp + j;
+        float v[4] = {0.f, 0.f, 0.f, 0.f};
+        if (nv == 4) {                                              // ldp and slice are multiples of 4
+            const float4 w = *reinterpret_cast<const float4*>(p);
+            v[0] = w.x; v[1] = w.y; v[2] = w.z; v[3] = w.w;
+        } else {
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+                if (q < nv) v[q] = p[q];
+        }
+#pragma unroll
+        for (int q = 0; q < 4; ++q) acc[q] = s == 0 ? v[q] : acc[q] + v[q];
+    }
+    if (out_f32) {
+        float* o = static_cast<float*>(out) + i * ldo + j;
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+            if (q < nv) o[q] = acc[q];
+    } else {
+        uint16_t* o = static_cast<uint16_t*>(out) + i * ldo + j;
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+            if (q < nv) o[q] = (uint16_t)f32_to_bf16(acc[q]);
+    }
+}
+
+hipError_t launch_split_sum(const float* part, int64_t S, int64_t slice, int64_t ldp, int64_t M, int64_t Nn,
+                            void* out, bool out_f32, int64_t ldo, hipStream_t st) {
+    const int64_t items = M * ((Nn + 3) / 4);
+    if (items == 0) return hipSuccess;
+    const int64_t blocks = (items + 255) / 256;
+    if (blocks > 0x7FFFFFFF) return hipErrorInvalidValue;
+    k_split_sum<<<dim3((unsigned)blocks), 256, 0, st>>>(part, S, slice, ldp, M, Nn, out, out_f32, ldo);
+    return hipGetLastError();
 }
 
 hipError_t launch_gemm(const GemmArgs& a, hipStream_t st) {

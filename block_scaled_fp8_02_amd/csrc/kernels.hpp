@@ -92,9 +92,16 @@ struct GemmArgs {
     const int32_t* offsets; int64_t E;
     int64_t q_estride, sq_estride, o_estride;
     int64_t epb;          // GROUP_K: experts per block (set by the launcher)
+    int64_t ksplit;       // GROUP_NONE, M <= 64: K ranges run by block rows (0 or 1: none)
+    int64_t kb_split;     // K blocks per range; range y writes fp32 O + y * o_estride
 };
 
 hipError_t launch_gemm(const GemmArgs& a, hipStream_t st);
+
+// out[i][j] = sum over s = 0 .. S-1, in that order, of part[s * slice + i * ldp + j]
+// (fp32), stored as bf16 (nearest-even) or fp32 at row stride ldo.
+hipError_t launch_split_sum(const float* part, int64_t S, int64_t slice, int64_t ldp, int64_t M, int64_t Nn,
+                            void* out, bool out_f32, int64_t ldo, hipStream_t st);
 
 // MXFP8 1x32 quantization (row-wise and/or column-wise).
 hipError_t launch_mx_quant(const void* x, bool in_bf16, int64_t rows, int64_t cols, int64_t ldx,

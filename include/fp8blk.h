@@ -298,6 +298,33 @@ FP8B_API int fp8_gemm_dgrad(const uint8_t* gq, int64_t ldgq, const float* gs, in
                    const uint8_t* wqT, int64_t ldwqT, const float* ws, int64_t ldws,
                    void* dx, int dxt, int64_t lddx, int64_t N, int64_t D, int64_t C, void* stream);
 
+/* DGrad for few token rows (N <= 64) with the contraction D split into
+ * consecutive ranges of 128-wide K blocks.  Such an output has too few
+ * 128-column tiles to occupy every compute unit, and each tile would re-read
+ * all of dY; here block row y of the grid runs the K blocks of range y in
+ * ascending order into fp32 partial sums in `work`, and a second kernel adds
+ * the ranges in ascending order and rounds once.  Every output element is
+ * still a fixed, deterministic sum: per range as in fp8_gemm_dgrad, then the
+ * ranges in order (the summation order differs from fp8_gemm_dgrad's, so the
+ * two agree to the GEMM tolerance, not bit for bit).
+ *   fp8_gemm_dgrad_split_bytes: bytes of `work` the split needs for this
+ *   shape on the current device; 0 when no split applies (N > 64, fewer
+ *   than 16 K blocks, or enough output tiles already), and then
+ *   fp8_gemm_dgrad_split is fp8_gemm_dgrad (work may be NULL).  At most
+ *   (compute units) * 64 * 128 * 4 bytes (8 MiB on 256 compute units).
+ *   Negative sizes return 0.
+ *   work: DEVICE buffer of at least that many bytes, 16-byte aligned, owned
+ *   by the caller, not read before it is written; it must not be used by
+ *   other work until the call's kernels have finished on `stream`.
+ *   Errors as fp8_gemm_dgrad, plus FP8B_EINVAL (work NULL), FP8B_EALIGN,
+ *   FP8B_ESHAPE (work_bytes too small) when a split applies.
+ * fp8_mx_gemm_dgrad_split is the same for fp8_mx_gemm_dgrad's operands. */
+FP8B_API int64_t fp8_gemm_dgrad_split_bytes(int64_t N, int64_t D, int64_t C);
+FP8B_API int fp8_gemm_dgrad_split(const uint8_t* gq, int64_t ldgq, const float* gs, int64_t ldgs,
+                         const uint8_t* wqT, int64_t ldwqT, const float* ws, int64_t ldws,
+                         void* dx, int dxt, int64_t lddx, int64_t N, int64_t D, int64_t C,
+                         void* work, int64_t work_bytes, void* stream);
+
 /* WGrad dW[D x C] = dY^T X (Jet-RL notes, section 2.2 WGrad; 4.2: both
  * operands grouped along the token axis).
  *   gqT [D x ldgqT], gsT [D x ldgsT] (fp8_quantize_transposed of dY); xqT [C x ldxqT], xsT [C x ldxsT]
@@ -366,6 +393,10 @@ FP8B_API int fp8_mx_gemm_fprop(const uint8_t* xq, int64_t ldxq, const uint8_t* x
 FP8B_API int fp8_mx_gemm_dgrad(const uint8_t* gq, int64_t ldgq, const uint8_t* ge, int64_t ldge,
                       const uint8_t* wqT, int64_t ldwqT, const uint8_t* weT, int64_t ldweT,
                       void* dx, int dxt, int64_t lddx, int64_t N, int64_t D, int64_t C, void* stream);
+FP8B_API int fp8_mx_gemm_dgrad_split(const uint8_t* gq, int64_t ldgq, const uint8_t* ge, int64_t ldge,
+                            const uint8_t* wqT, int64_t ldwqT, const uint8_t* weT, int64_t ldweT,
+                            void* dx, int dxt, int64_t lddx, int64_t N, int64_t D, int64_t C,
+                            void* work, int64_t work_bytes, void* stream);
 FP8B_API int fp8_mx_gemm_wgrad(const uint8_t* gqT, int64_t ldgqT, const uint8_t* geT, int64_t ldgeT,
                       const uint8_t* xqT, int64_t ldxqT, const uint8_t* xeT, int64_t ldxeT,
                       void* dw, int dwt, int64_t lddw, int beta,

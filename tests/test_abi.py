@@ -168,3 +168,34 @@ def test_dequantized_backward_rejects_bad_arguments_on_host():
     assert L.fp8_dequant_gemm_wgrad(Y, 128, Q, 256, S, 2, 1, 8, 128, 256, O, 1, 256, 0, W, 256, None) == 1
     assert L.fp8_dequant_gemm_wgrad(Y, 128, Q, 256, S, 2, 0, 8, 128, 256, O, 1, 256, 1, W, 256, None) == 4
     assert L.fp8_dequant_gemm_dgrad(Y, 128, Q, 256, S, 2, 1, 8, 128, 256, O, 256, W, 100, None) == 2
+
+
+def test_dgrad_split_workspace_and_host_checks():
+    """K-split DGrad (few token rows, long contraction): the workspace size
+    for a few shapes on 256 compute units (fp32 partial rows padded to 16
+    bytes, one slice per K range), no split where it does not apply, and the
+    host-side rejections of the split entry point (each call fails before
+    any launch)."""
+    L = fb.lib()
+    if L.fp8_gemm_dgrad_split_bytes(64, 24576, 4096) == 0:
+        pytest.skip("device reports too few compute units for a split")
+    assert L.fp8_gemm_dgrad_split_bytes(64, 24576, 4096) == 8 * 64 * 4096 * 4   # 8 ranges of 24 K blocks
+    assert L.fp8_gemm_dgrad_split_bytes(64, 4096, 512) == 4 * 64 * 512 * 4      # 4 ranges of 8
+    assert L.fp8_gemm_dgrad_split_bytes(37, 2304, 300) == 2 * 37 * 300 * 4      # 2 ranges of 9
+    assert L.fp8_gemm_dgrad_split_bytes(65, 4096, 512) == 0                     # more than 64 rows
+    assert L.fp8_gemm_dgrad_split_bytes(64, 1920, 512) == 0                     # 15 K blocks
+    assert L.fp8_gemm_dgrad_split_bytes(64, 24576, 16385) == 0                  # 129 column tiles
+    assert L.fp8_gemm_dgrad_split_bytes(-1, 4096, 512) == 0
+    GQ, GS, WT, WS, DX, WK = 0x100000, 0x200000, 0x300000, 0x400000, 0x500000, 0x600000
+    need = 4 * 64 * 512 * 4
+
+    def call(fn, work, nbytes):
+        return getattr(L, fn)(GQ, 4096, GS, 32, WT, 4096, WS, 4, DX, 1, 512, 64, 4096, 512, work, nbytes, None)
+    for fn in ("fp8_gemm_dgrad_split", "fp8_mx_gemm_dgrad_split"):
+        if fn.startswith("fp8_mx"):
+            def call(fn, work, nbytes):     # noqa: F811  (MX scales: 4096 / 32 E8M0 bytes per row)
+                return getattr(L, fn)(GQ, 4096, GS, 128, WT, 4096, WS, 128, DX, 1, 512, 64, 4096, 512,
+                                      work, nbytes, None)
+        assert call(fn, None, need) == 1            # no workspace
+        assert call(fn, WK + 8, need) == 3          # misaligned workspace
+        assert call(fn, WK, need - 16) == 2         # too small

@@ -124,6 +124,37 @@ def test_ragged_layers(N, D, C):
         check_f32(g, r, m, f"ragged {name}")
 
 
+@pytest.mark.parametrize("N,D,C", [(64, 4096, 512), (37, 2304, 300), (1, 3000, 4100), (64, 24576, 384)])
+def test_dgrad_k_split(N, D, C):
+    """Few token rows with a long contraction: DGrad runs as K ranges of
+    fp32 partial sums plus an ordered sum of the ranges.  fp32 and bf16
+    outputs against the oracle (the same bounds as every GEMM), the plain
+    single-range entry point against the oracle too, and the split form
+    repeated bit for bit."""
+    banner(f"dgrad K split N={N} D={D} C={C}")
+    assert fb.lib().fp8_gemm_dgrad_split_bytes(N, D, C) > 0
+    rng = np.random.default_rng(N * 5 + D + C * 11)
+    X = rng.standard_normal((N, C)).astype(np.float32)
+    W = (rng.standard_normal((D, C)) * 0.02).astype(np.float32)
+    dY = (rng.standard_normal((N, D)) * np.exp(rng.uniform(-4, 2, (1, D)))).astype(np.float32)
+    ogq, ogs = oracle.quant_1x128(dY)
+    owq, ows, _ = oracle.quant_128x128(W, with_transpose=False)
+    want = oracle.dgrad(ogq, ogs, owq, ows, D, C)
+    mag = abs_products(X, W, dY)[1]
+    gq, gs = fb.fp8_quantize_act_1x128(dev(dY))
+    wq, ws, wqT = fb.fp8_quantize_weight_128x128(dev(W))
+    f32 = torch.float32
+    dx = fb.fp8_gemm_dgrad(gq, gs, wqT, ws, N, D, C, out_dtype=f32)
+    check_f32(host(dx), want, mag, "split dgrad f32")
+    again = fb.fp8_gemm_dgrad(gq, gs, wqT, ws, N, D, C, out_dtype=f32)
+    assert torch.equal(dx, again), "split dgrad is not repeatable"
+    check(host(fb.fp8_gemm_dgrad(gq, gs, wqT, ws, N, D, C)), want, TOL, "split dgrad bf16")
+    plain = torch.empty((N, C), dtype=f32, device="cuda")
+    fb._call("fp8_gemm_dgrad", fb._ptr(gq), fb._ld(gq), fb._ptr(gs), fb._ld(gs), fb._ptr(wqT), fb._ld(wqT),
+             fb._ptr(ws), fb._ld(ws), fb._ptr(plain), 0, fb._ld(plain), N, D, C, fb._stream(gq.device))
+    check_f32(host(plain), want, mag, "single-range dgrad f32")
+
+
 def test_zero_contraction_gives_zero():
     """C = 0: every output is an empty sum."""
     xq = torch.zeros((5, 16), dtype=torch.uint8, device="cuda")[:, :0]
