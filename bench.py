@@ -52,8 +52,8 @@ def parse():
     ap.add_argument("--no-other", action="store_true", help="skip the decode / MXFP8 / MoE kernel timings")
     ap.add_argument("--only-section", choices=["fused", "other"],
                     help="time one side section alone and print its JSON (no training step)")
-    ap.add_argument("--cpu-seconds", type=float, default=15.0,
-                    help="rough CPU budget of the oracle baseline sample")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0,
+                    help="minimum duration of the timed oracle baseline sample (seconds)")
     ap.add_argument("--traffic", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="no GPU work: turn two rocprofv3 --pmc counter_collection.csv files "
                          "(FETCH_SIZE, WRITE_SIZE) of this benchmark into profiles/traffic_gemm_train.json")
@@ -691,7 +691,7 @@ def cpu_baseline(w, budget_s: float):
     import oracle
     threads = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
     rng = np.random.default_rng(99)
-    rows = 16
+    rows = 256
     t0 = time.perf_counter()
     while True:
         ridx = np.sort(rng.choice(N, rows, replace=False))
@@ -706,7 +706,9 @@ def cpu_baseline(w, budget_s: float):
         xqT, xsT = oracle.quant_colwise(w["X"])
         oracle.wgrad(gqT, gsT, xqT, xsT, N)
         dt = time.perf_counter() - ts
-        if dt > budget_s / 3 or time.perf_counter() - t0 > budget_s or rows >= 256:
+        # one timed sample of at least budget_s seconds of CPU work, doubling
+        # the sampled rows; at most 4 x budget_s in all
+        if dt >= budget_s or time.perf_counter() - t0 > 4 * budget_s or rows >= 4096:
             break
         rows *= 2
     flops = 2.0 * rows * D * C + 2.0 * rows * C * D + 2.0 * rows * C * N
