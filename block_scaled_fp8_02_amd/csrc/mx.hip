@@ -16,7 +16,8 @@ __device__ __forceinline__ uint32_t mx_encode4(const float* v, int k) {
     return e4m3_pack4(ldexpf(v[0], -k), ldexpf(v[1], -k), ldexpf(v[2], -k), ldexpf(v[3], -k));
 }
 
-// Tile 128 rows x 128 cols; thread t holds rows 8*(t/16)..+7, cols
+// Tile 128 rows x 128 cols, one per block, numbered row-tile-major; thread
+// t holds rows 8*(t/16)..+7, cols
 // 8*(t%16)..+7.  A 32-column row block spans 4 consecutive lanes; a 32-row
 // column block spans the 4 row-slices of one wavefront.
 template <typename T>
@@ -28,7 +29,10 @@ __global__ __launch_bounds__(256) void k_mx_quant(const T* __restrict__ x, int64
     __shared__ __attribute__((aligned(16))) uint8_t tileT[128 * 128];
     const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
     const int rg = t >> 4, cg = t & 15;
-    const int64_t rb = (int64_t)blockIdx.x * 128, cb = (int64_t)blockIdx.y * 128;
+    // consecutive blocks walk along a row of tiles: the tiles in flight at
+    // one time read whole input rows and write whole code rows
+    const int64_t nct = (cols + 127) / 128;
+    const int64_t rb = ((int64_t)blockIdx.x / nct) * 128, cb = ((int64_t)blockIdx.x % nct) * 128;
     const int64_t r0 = rb + rg * 8, c0 = cb + cg * 8;
     const int cvalid = clamp_valid(cols - c0);
 
@@ -119,8 +123,8 @@ hipError_t launch_mx_quant(const void* x, bool in_bf16, int64_t rows, int64_t co
                            uint8_t* qT, int64_t ldqT, uint8_t* eT, int64_t ldeT, hipStream_t st) {
     if (rows == 0 || cols == 0) return hipSuccess;
     const int64_t rt = (rows + 127) / 128, ct = (cols + 127) / 128;
-    if (rt > 0x7FFFFFFF || ct > 65535) return hipErrorInvalidValue;
-    const dim3 grid((unsigned)rt, (unsigned)ct);
+    if (rt * ct > 0x7FFFFFFF) return hipErrorInvalidValue;
+    const dim3 grid((unsigned)(rt * ct));
     if (in_bf16)
         k_mx_quant<uint16_t><<<grid, 256, 0, st>>>(static_cast<const uint16_t*>(x), rows, cols, ldx, q, ldq, e, lde, qT, ldqT, eT, ldeT);
     else
