@@ -182,12 +182,14 @@ struct TileAt {
     bool valid;
 };
 
-// Tiles are numbered in bands of QT_BAND row tiles walked column by
-// column, so that the tiles in flight at one time (one per resident block,
-// consecutive numbers) cover QT_BAND row tiles x a few column tiles: the
-// input, the row-wise codes and the transposed codes are all touched in runs
-// of several KB rather than one of them in 128-byte pieces.
-constexpr int64_t QT_BAND = 32;
+// Tiles are numbered in bands of QT_BAND row tiles walked column by column.
+// With one row tile per band the tiles in flight at one time (one per
+// resident block, consecutive numbers) cover whole rows of the input and of
+// the row-wise codes, and each transposed code row in 128-byte pieces; wider
+// bands trade input-row runs for transposed-row runs and measured slower
+// (token-axis quantization of X [8192 x 12288]: 71 us with bands of 1 row
+// tile, 76 us with 32).
+constexpr int64_t QT_BAND = 1;
 
 __device__ __forceinline__ TileAt locate_tile(const QuantTileArgs& A, int64_t k, SegPos& cur) {
     TileAt at;
