@@ -737,7 +737,8 @@ __global__ __launch_bounds__(256) void k_split_sum(const float* __restrict__ par
     const int64_t i = idx / n4, j = (idx - i * n4) * 4;
     const int nv = Nn - j < 4 ? (int)(Nn - j) : 4;
     float acc[4] = {0.f, 0.f, 0.f, 0.f};
-    for (int64_t s = 0; s < S; ++s) {
+#pragma unroll 8
+    for (int64_t s = 0; s < S; ++s) {                               // loads issued ahead, sums in order
         const float* p = part + s * slice + i * ldp + j;
         float v[4] = {0.f, 0.f, 0.f, 0.f};
         if (nv == 4) {                                              // ldp and slice are multiples of 4
