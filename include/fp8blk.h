@@ -298,8 +298,9 @@ FP8B_API int fp8_gemm_dgrad(const uint8_t* gq, int64_t ldgq, const float* gs, in
                    const uint8_t* wqT, int64_t ldwqT, const float* ws, int64_t ldws,
                    void* dx, int dxt, int64_t lddx, int64_t N, int64_t D, int64_t C, void* stream);
 
-/* DGrad for few token rows (N <= 64) with the contraction D split into
- * consecutive ranges of 128-wide K blocks.  Such an output has too few
+/* DGrad dX = dY W (Jet-RL notes, section 2.2 DGrad; 4.2: dY grouped 1x128
+ * along D, W in 128x128 blocks), for few token rows (N <= 64), with the
+ * contraction D split into consecutive ranges of 128-wide K blocks.  Such an output has too few
  * 128-column tiles to occupy every compute unit, and each tile would re-read
  * all of dY; here block row y of the grid runs the K blocks of range y in
  * ascending order into fp32 partial sums in `work`, and a second kernel adds
