@@ -155,6 +155,31 @@ def test_dgrad_k_split(N, D, C):
     check_f32(host(plain), want, mag, "single-range dgrad f32")
 
 
+@pytest.mark.parametrize("N,D,C", [(65, 4096, 512), (64, 1920, 512)])
+def test_dgrad_split_entry_without_split_is_plain_dgrad(N, D, C):
+    """Where no split applies (more than 64 rows; fewer than 16 K blocks)
+    the split entry points run the plain DGrad: bit for bit the same output,
+    with no workspace at all."""
+    banner(f"dgrad split entry, no split: N={N} D={D} C={C}")
+    assert fb.lib().fp8_gemm_dgrad_split_bytes(N, D, C) == 0
+    rng = np.random.default_rng(N + D + C)
+    W = (rng.standard_normal((D, C)) * 0.02).astype(np.float32)
+    dY = (rng.standard_normal((N, D)) * 1e-3).astype(np.float32)
+    gq, gs = fb.fp8_quantize_act_1x128(dev(dY))
+    wq, ws, wqT = fb.fp8_quantize_weight_128x128(dev(W))
+    gmq, gme, _, _ = fb.fp8_mx_quantize_1x32(dev(dY), rowwise=True, colwise=False)
+    _, _, wmqT, wmeT = fb.fp8_mx_quantize_1x32(dev(W), rowwise=False, colwise=True)
+    for plain_fn, split_fn, a, sa, b, sb in (("fp8_gemm_dgrad", "fp8_gemm_dgrad_split", gq, gs, wqT, ws),
+                                             ("fp8_mx_gemm_dgrad", "fp8_mx_gemm_dgrad_split", gmq, gme, wmqT, wmeT)):
+        outs = []
+        for fn, extra in ((plain_fn, ()), (split_fn, (None, 0))):
+            dx = torch.full((N, C), float("nan"), dtype=torch.float32, device="cuda")
+            fb._call(fn, fb._ptr(a), fb._ld(a), fb._ptr(sa), fb._ld(sa), fb._ptr(b), fb._ld(b),
+                     fb._ptr(sb), fb._ld(sb), fb._ptr(dx), 0, fb._ld(dx), N, D, C, *extra, fb._stream(a.device))
+            outs.append(dx)
+        assert torch.equal(outs[0], outs[1]), f"{split_fn} without a split differs from {plain_fn}"
+
+
 def test_zero_contraction_gives_zero():
     """C = 0: every output is an empty sum."""
     xq = torch.zeros((5, 16), dtype=torch.uint8, device="cuda")[:, :0]
