@@ -412,13 +412,18 @@ static int gemm_dense(int op, const void* a, int64_t lda, const void* sa, int64_
 }
 
 // K split of a few-row DGrad (op 1 or 4): number of K ranges (1: none) and
-// K blocks per range.  About one block per compute unit over the 128-column
-// output tiles, at least 8 K blocks per range.
+// K blocks per range.  About 256 blocks (one per compute unit of an MI355X)
+// over the 128-column output tiles, at least 8 K blocks per range.  The plan
+// is a fixed function of (N, D, C), never of the device it runs on, so the
+// partition, and with it every output bit, is the same on any device or
+// compute-unit partition.
+constexpr int64_t kSplitBlocks = 256;
+
 static void dgrad_split_plan(int64_t N, int64_t D, int64_t C, int64_t* S, int64_t* kbs) {
     *S = 1;
     *kbs = 0;
     if (N <= 0 || N > 64 || C <= 0 || D <= 0) return;
-    const int64_t KB = cdiv(D, 128), nbj = cdiv(C, 128), cus = device_cu_count();
+    const int64_t KB = cdiv(D, 128), nbj = cdiv(C, 128), cus = kSplitBlocks;
     if (KB < 16 || 2 * nbj > cus) return;
     int64_t s = cus / nbj;
     if (s > KB / 8) s = KB / 8;

@@ -32,9 +32,13 @@
 //
 // The reduction order of an output element is fixed: ascending K blocks,
 // one MFMA per block, one FMA per block (one scaled MFMA per block for MX).
-// It does not depend on the tile shape or on M, which makes row i of the
-// output a function of row i of P alone (rollout and training forward
-// agree bit for bit).
+// In every launch without a K split (every FProp, every WGrad, DGrad with
+// more than 64 rows or a short contraction) it does not depend on the tile
+// shape or on M, which makes row i of the output a function of row i of P
+// alone (rollout and training forward agree bit for bit).  A K-split launch
+// (few-row DGrad) sums ascending K ranges, each reduced as above, in
+// ascending order: a different but equally fixed order, chosen from
+// (M, Nn, K) alone.
 #include "device_common.hpp"
 #include "kernels.hpp"
 

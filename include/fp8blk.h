@@ -38,9 +38,12 @@
  *   fp8b_last_hip_error() (thread-local).  Nothing aborts the process and
  *   no C++ exception crosses this boundary.
  * - Inputs must be finite; this is not checked on the device.
- * - Results are deterministic, and every GEMM row depends only on its own
- *   input row: the reduction order of an output element does not depend on
- *   the number of rows in the call (unified rollout/training forward).
+ * - Results are deterministic and the same on every device.  Every FProp
+ *   and WGrad output row depends only on its own input row: the reduction
+ *   order of an output element does not depend on the number of rows in
+ *   the call (unified rollout/training forward).  DGrad with at most 64 rows
+ *   and a long contraction runs the K-split order of fp8_gemm_dgrad_split
+ *   (fixed by N, D and C alone); DGrad rows are otherwise row-local too.
  */
 #ifndef FP8BLK_H
 #define FP8BLK_H
@@ -309,11 +312,12 @@ FP8B_API int fp8_gemm_dgrad(const uint8_t* gq, int64_t ldgq, const float* gs, in
  * ranges in order (the summation order differs from fp8_gemm_dgrad's, so the
  * two agree to the GEMM tolerance, not bit for bit).
  *   fp8_gemm_dgrad_split_bytes: bytes of `work` the split needs for this
- *   shape on the current device; 0 when no split applies (N > 64, fewer
- *   than 16 K blocks, or enough output tiles already), and then
- *   fp8_gemm_dgrad_split is fp8_gemm_dgrad (work may be NULL).  At most
- *   (compute units) * 64 * 128 * 4 bytes (8 MiB on 256 compute units).
- *   Negative sizes return 0.
+ *   shape; 0 when no split applies (N > 64, fewer than 16 K blocks, or more
+ *   than 128 output tiles of 128 columns), and then fp8_gemm_dgrad_split is
+ *   fp8_gemm_dgrad (work may be NULL).  The partition (about 256 blocks of at
+ *   least 8 K blocks each) and this size depend on N, D and C only, never on
+ *   the device, so the output bits are the same on every device.  At most
+ *   256 * 64 * 128 * 4 bytes = 8 MiB.  Negative sizes return 0.
  *   work: DEVICE buffer of at least that many bytes, 16-byte aligned, owned
  *   by the caller, not read before it is written; it must not be used by
  *   other work until the call's kernels have finished on `stream`.

@@ -172,16 +172,18 @@ def test_dequantized_backward_rejects_bad_arguments_on_host():
 
 def test_dgrad_split_workspace_and_host_checks():
     """K-split DGrad (few token rows, long contraction): the workspace size
-    for a few shapes on 256 compute units (fp32 partial rows padded to 16
-    bytes, one slice per K range), no split where it does not apply, and the
-    host-side rejections of the split entry point (each call fails before
-    any launch)."""
+    for a few shapes (fp32 partial rows padded to 16 bytes, one slice per K
+    range; the partition is a function of the shape alone, the same with or
+    without a GPU), no split where it does not apply, and the host-side
+    rejections of the split entry point (each call fails before any
+    launch)."""
     L = fb.lib()
-    if L.fp8_gemm_dgrad_split_bytes(64, 24576, 4096) == 0:
-        pytest.skip("device reports too few compute units for a split")
     assert L.fp8_gemm_dgrad_split_bytes(64, 24576, 4096) == 8 * 64 * 4096 * 4   # 8 ranges of 24 K blocks
     assert L.fp8_gemm_dgrad_split_bytes(64, 4096, 512) == 4 * 64 * 512 * 4      # 4 ranges of 8
     assert L.fp8_gemm_dgrad_split_bytes(37, 2304, 300) == 2 * 37 * 300 * 4      # 2 ranges of 9
+    assert L.fp8_gemm_dgrad_split_bytes(37, 2304, 301) == 2 * 37 * 304 * 4      # rows padded to 4 floats
+    assert L.fp8_gemm_dgrad_split_bytes(1, 3000, 4099) == 3 * 1 * 4100 * 4      # 3 ranges of 8 (33 tiles)
+    assert L.fp8_gemm_dgrad_split_bytes(5, 2050, 130) == 2 * 5 * 132 * 4        # 2 ranges of 9 (17 K blocks)
     assert L.fp8_gemm_dgrad_split_bytes(65, 4096, 512) == 0                     # more than 64 rows
     assert L.fp8_gemm_dgrad_split_bytes(64, 1920, 512) == 0                     # 15 K blocks
     assert L.fp8_gemm_dgrad_split_bytes(64, 24576, 16385) == 0                  # 129 column tiles

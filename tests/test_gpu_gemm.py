@@ -8,8 +8,9 @@ of the fp8 MFMA dot product), a bound that stays meaningful for short or
 cancelling rows.
 
 Full-size launches use exactly the kernels and tile configurations the
-benchmark times; where the oracle cannot cover a full-size output in
-seconds, it computes a seeded sample of rows.
+benchmark times, and the oracle covers every output: the training layer
+(8192 x 4096 x 12288, three GEMMs), the decode FProp, and all 128 experts
+of the MoE layer.
 """
 import numpy as np
 import pytest
@@ -124,13 +125,19 @@ def test_ragged_layers(N, D, C):
         check_f32(g, r, m, f"ragged {name}")
 
 
-@pytest.mark.parametrize("N,D,C", [(64, 4096, 512), (37, 2304, 300), (1, 3000, 4100), (64, 24576, 384)])
+SPLIT_SHAPES = [(64, 4096, 512), (37, 2304, 300), (1, 3000, 4100), (64, 24576, 384),
+                # C % 4 != 0 (the ordered sum's partial-quad tail) and ragged D
+                (37, 2304, 301), (1, 3000, 4099), (5, 2050, 130), (64, 24576, 4096)]
+
+
+@pytest.mark.parametrize("N,D,C", SPLIT_SHAPES)
 def test_dgrad_k_split(N, D, C):
     """Few token rows with a long contraction: DGrad runs as K ranges of
     fp32 partial sums plus an ordered sum of the ranges.  fp32 and bf16
     outputs against the oracle (the same bounds as every GEMM), the plain
     single-range entry point against the oracle too, and the split form
-    repeated bit for bit."""
+    repeated bit for bit.  The split partition is a function of the shape
+    alone, so it applies to these shapes on any device."""
     banner(f"dgrad K split N={N} D={D} C={C}")
     assert fb.lib().fp8_gemm_dgrad_split_bytes(N, D, C) > 0
     rng = np.random.default_rng(N * 5 + D + C * 11)
@@ -141,18 +148,40 @@ def test_dgrad_k_split(N, D, C):
     owq, ows, _ = oracle.quant_128x128(W, with_transpose=False)
     want = oracle.dgrad(ogq, ogs, owq, ows, D, C)
     mag = abs_products(X, W, dY)[1]
-    gq, gs = fb.fp8_quantize_act_1x128(dev(dY))
-    wq, ws, wqT = fb.fp8_quantize_weight_128x128(dev(W))
+    gq, gs = fb.fp8_quantize_act_1x128(dev_strided(dY))
+    wq, ws, wqT = fb.fp8_quantize_weight_128x128(dev_strided(W))
     f32 = torch.float32
     dx = fb.fp8_gemm_dgrad(gq, gs, wqT, ws, N, D, C, out_dtype=f32)
     check_f32(host(dx), want, mag, "split dgrad f32")
     again = fb.fp8_gemm_dgrad(gq, gs, wqT, ws, N, D, C, out_dtype=f32)
     assert torch.equal(dx, again), "split dgrad is not repeatable"
     check(host(fb.fp8_gemm_dgrad(gq, gs, wqT, ws, N, D, C)), want, TOL, "split dgrad bf16")
-    plain = torch.empty((N, C), dtype=f32, device="cuda")
+    plain = fb._new_out(N, C, f32, gq.device)
     fb._call("fp8_gemm_dgrad", fb._ptr(gq), fb._ld(gq), fb._ptr(gs), fb._ld(gs), fb._ptr(wqT), fb._ld(wqT),
              fb._ptr(ws), fb._ld(ws), fb._ptr(plain), 0, fb._ld(plain), N, D, C, fb._stream(gq.device))
     check_f32(host(plain), want, mag, "single-range dgrad f32")
+
+
+@pytest.mark.parametrize("N,D,C", SPLIT_SHAPES)
+def test_mx_dgrad_k_split(N, D, C):
+    """The MX DGrad on the same few-row shapes, split along K: against the
+    MX oracle with the row-norm bar and the fp32 accumulation bound, and
+    repeated bit for bit."""
+    banner(f"mx dgrad K split N={N} D={D} C={C}")
+    rng = np.random.default_rng(N * 3 + D * 7 + C)
+    W = (rng.standard_normal((D, C)) * 0.02).astype(np.float32)
+    dY = (rng.standard_normal((N, D)) * np.exp(rng.uniform(-4, 2, (1, D)))).astype(np.float32)
+    ogq, oge = oracle.mx_quant_rows(dY)
+    owqT, oweT = oracle.mx_quant_cols(W)
+    want = oracle.mx_gemm(ogq, oge, owqT, oweT, D)
+    mag = oracle.matmul_f64(np.abs(oracle.deq_mx(ogq, oge, D)), np.abs(oracle.deq_mx(owqT, oweT, D)).T)
+    gq, ge, _, _ = fb.fp8_mx_quantize_1x32(dev_strided(dY), rowwise=True, colwise=False)
+    _, _, wqT, weT = fb.fp8_mx_quantize_1x32(dev_strided(W), rowwise=False, colwise=True)
+    dx = fb.fp8_mx_gemm_dgrad(gq, ge, wqT, weT, N, D, C, out_dtype=torch.float32)
+    check_f32(host(dx), want, mag, "mx split dgrad f32")
+    again = fb.fp8_mx_gemm_dgrad(gq, ge, wqT, weT, N, D, C, out_dtype=torch.float32)
+    assert torch.equal(dx, again), "mx split dgrad is not repeatable"
+    check(host(fb.fp8_mx_gemm_dgrad(gq, ge, wqT, weT, N, D, C)), want, TOL, "mx split dgrad bf16")
 
 
 @pytest.mark.parametrize("N,D,C", [(65, 4096, 512), (64, 1920, 512)])
@@ -165,15 +194,15 @@ def test_dgrad_split_entry_without_split_is_plain_dgrad(N, D, C):
     rng = np.random.default_rng(N + D + C)
     W = (rng.standard_normal((D, C)) * 0.02).astype(np.float32)
     dY = (rng.standard_normal((N, D)) * 1e-3).astype(np.float32)
-    gq, gs = fb.fp8_quantize_act_1x128(dev(dY))
-    wq, ws, wqT = fb.fp8_quantize_weight_128x128(dev(W))
+    gq, gs = fb.fp8_quantize_act_1x128(dev_strided(dY))
+    wq, ws, wqT = fb.fp8_quantize_weight_128x128(dev_strided(W))
     gmq, gme, _, _ = fb.fp8_mx_quantize_1x32(dev(dY), rowwise=True, colwise=False)
     _, _, wmqT, wmeT = fb.fp8_mx_quantize_1x32(dev(W), rowwise=False, colwise=True)
     for plain_fn, split_fn, a, sa, b, sb in (("fp8_gemm_dgrad", "fp8_gemm_dgrad_split", gq, gs, wqT, ws),
                                              ("fp8_mx_gemm_dgrad", "fp8_mx_gemm_dgrad_split", gmq, gme, wmqT, wmeT)):
         outs = []
         for fn, extra in ((plain_fn, ()), (split_fn, (None, 0))):
-            dx = torch.full((N, C), float("nan"), dtype=torch.float32, device="cuda")
+            dx = fb._new_out(N, C, torch.float32, a.device).fill_(float("nan"))
             fb._call(fn, fb._ptr(a), fb._ld(a), fb._ptr(sa), fb._ld(sa), fb._ptr(b), fb._ld(b),
                      fb._ptr(sb), fb._ld(sb), fb._ptr(dx), 0, fb._ld(dx), N, D, C, *extra, fb._stream(a.device))
             outs.append(dx)
@@ -204,9 +233,11 @@ def test_decode_fprop_full():
     check(y, oracle.fprop(oxq, oxs, owq, ows, 4096), TOL, "decode fprop")
 
 
-def test_train_layer_full_size_sampled():
-    """The three training GEMMs at full size (8192 x 4096 x 12288), checked
-    on seeded samples of output rows against the oracle."""
+@pytest.fixture(scope="module")
+def train_full():
+    """The three training GEMMs at full size (8192 x 4096 x 12288) from the
+    GPU's own quantizers, in the launch configuration the benchmark times;
+    outputs kept on the host for the full-size oracle comparisons below."""
     w = wl.train(0)
     X, W, dY = w["X"], w["W"], w["dY"]
     N, C, D = 8192, 12288, 4096
@@ -215,22 +246,39 @@ def test_train_layer_full_size_sampled():
     xqT, xsT, xq, xs = fb.fp8_quantize_transposed(xd, rowwise=True)
     gqT, gsT, gq, gs = fb.fp8_quantize_transposed(gd, rowwise=True)
     wq, ws, wqT = fb.fp8_quantize_weight_128x128(wd)
-    y = fb.fp8_gemm_fprop(xq, xs, wq, ws, N, D, C)
-    dx = fb.fp8_gemm_dgrad(gq, gs, wqT, ws, N, D, C)
-    dw = fb.fp8_gemm_wgrad(gqT, gsT, xqT, xsT, N, D, C)
-    torch.cuda.synchronize()
-    rng = np.random.default_rng(2024)
-    rows = np.sort(rng.choice(N, 48, replace=False))
-    drows = np.sort(rng.choice(D, 24, replace=False))
-    banner("train: oracle on sampled rows")
-    owq, ows, _ = oracle.quant_128x128(W, with_transpose=False)
-    oxq, oxs = oracle.quant_1x128(X[rows])
-    check(host(y)[rows], oracle.fprop(oxq, oxs, owq, ows, C), TOL, "train fprop (sampled rows)")
-    ogq, ogs = oracle.quant_1x128(dY[rows])
-    check(host(dx)[rows], oracle.dgrad(ogq, ogs, owq, ows, D, C), TOL, "train dgrad (sampled rows)")
-    ogqT, ogsT = oracle.quant_colwise(np.ascontiguousarray(dY[:, drows]))
-    oxqT, oxsT = oracle.quant_colwise(X)
-    check(host(dw)[drows], oracle.wgrad(ogqT, ogsT, oxqT, oxsT, N), TOL, "train wgrad (sampled rows)")
+    y = host(fb.fp8_gemm_fprop(xq, xs, wq, ws, N, D, C))
+    dx = host(fb.fp8_gemm_dgrad(gq, gs, wqT, ws, N, D, C))
+    dw = host(fb.fp8_gemm_wgrad(gqT, gsT, xqT, xsT, N, D, C))
+    del xd, wd, gd, xqT, xsT, xq, xs, gqT, gsT, gq, gs, wq, ws, wqT
+    torch.cuda.empty_cache()
+    return {"w": w, "y": y, "dx": dx, "dw": dw}
+
+
+def test_train_fprop_full(train_full):
+    """Training FProp, every output against the oracle (full size)."""
+    w = train_full["w"]
+    banner("train fprop: oracle on the full output")
+    oxq, oxs = oracle.quant_1x128(w["X"])
+    owq, ows, _ = oracle.quant_128x128(w["W"], with_transpose=False)
+    check(train_full["y"], oracle.fprop(oxq, oxs, owq, ows, 12288), TOL, "train fprop (full)")
+
+
+def test_train_dgrad_full(train_full):
+    """Training DGrad, every output against the oracle (full size)."""
+    w = train_full["w"]
+    banner("train dgrad: oracle on the full output")
+    ogq, ogs = oracle.quant_1x128(w["dY"])
+    owq, ows, _ = oracle.quant_128x128(w["W"], with_transpose=False)
+    check(train_full["dx"], oracle.dgrad(ogq, ogs, owq, ows, 4096, 12288), TOL, "train dgrad (full)")
+
+
+def test_train_wgrad_full(train_full):
+    """Training WGrad, every output against the oracle (full size)."""
+    w = train_full["w"]
+    banner("train wgrad: oracle on the full output")
+    ogqT, ogsT = oracle.quant_colwise(w["dY"])
+    oxqT, oxsT = oracle.quant_colwise(w["X"])
+    check(train_full["dw"], oracle.wgrad(ogqT, ogsT, oxqT, oxsT, 8192), TOL, "train wgrad (full)")
 
 
 def test_unified_forward_is_batch_invariant():
@@ -305,25 +353,37 @@ def moe_gpu(w):
     return {k: host(v) for k, v in out.items()}
 
 
-def test_moe_grouped_full_launch_sampled_experts():
+@pytest.fixture(scope="module")
+def moe_full():
     w = wl.moe(0)
     banner("moe: grouped GEMMs at full size")
-    got = moe_gpu(w)
+    return w, moe_gpu(w)
+
+
+@pytest.mark.parametrize("proj", ["gu", "d"])
+def test_moe_grouped_full_every_expert(moe_full, proj):
+    """All six grouped GEMMs of the MoE layer at full size (4096 tokens,
+    top-8 of 128 experts): every expert's rows and weight gradient against
+    the oracle run on that expert alone."""
+    w, got = moe_full
     offs = w["offsets"]
-    counts = np.diff(offs)
-    experts = sorted({int(np.argmin(counts)), int(np.argmax(counts)), 0, 63, 127})
     I = w["inter"]
-    banner(f"moe: oracle on experts {experts}")
-    for e in experts:
+    banner(f"moe {proj}: oracle on all {w['experts']} experts")
+    worst = {"fprop": 0.0, "dgrad": 0.0, "wgrad": 0.0}
+    for e in range(w["experts"]):
         a, b = int(offs[e]), int(offs[e + 1])
-        n = b - a
-        Wgu, Wd = w["W_gu"][e], w["W_d"][e]
-        for (Xn, Wn, dYn, pre, Dn, Cn) in ((w["X_perm"][a:b], Wgu, w["dH"][a:b], "gu", 2 * I, w["hidden"]),
-                                           (w["A"][a:b], Wd, w["dY_d"][a:b], "d", w["hidden"], I)):
-            y, dx, dw = oracle_layer(Xn, Wn, dYn)
-            check(got[f"{pre}_fprop"][a:b], y, TOL, f"moe e{e} ({n} rows) {pre} fprop")
-            check(got[f"{pre}_dgrad"][a:b], dx, TOL, f"moe e{e} {pre} dgrad")
-            check(got[f"{pre}_wgrad"][e], dw, TOL, f"moe e{e} {pre} wgrad")
+        if proj == "gu":
+            Xn, Wn, dYn = w["X_perm"][a:b], w["W_gu"][e], w["dH"][a:b]
+        else:
+            Xn, Wn, dYn = w["A"][a:b], w["W_d"][e], w["dY_d"][a:b]
+        y, dx, dw = oracle_layer(Xn, Wn, dYn)
+        for name, g, r in (("fprop", got[f"{proj}_fprop"][a:b], y), ("dgrad", got[f"{proj}_dgrad"][a:b], dx),
+                           ("wgrad", got[f"{proj}_wgrad"][e], dw)):
+            err = oracle.rel_row_error(g, r)
+            assert err <= TOL, f"moe e{e} ({b - a} rows) {proj} {name}: {err}"
+            worst[name] = max(worst[name], err)
+    banner(f"moe {proj}: worst rel row error over the experts " +
+           ", ".join(f"{k} {v:.3e}" for k, v in worst.items()))
 
 
 def test_moe_grouped_edge_segments():

@@ -9,7 +9,7 @@ import torch
 import block_scaled_fp8_02_amd as fb
 import oracle
 from block_scaled_fp8_02_amd import workloads as wl
-from gpu_util import TOL, assert_bytes_equal, banner, dev, dev_strided, host
+from gpu_util import TOL, assert_bytes_equal, assert_scales_equal, banner, dev, dev_strided, host
 
 pytestmark = pytest.mark.gpu
 
@@ -45,6 +45,11 @@ def test_mx_quant_classes():
 
 
 def test_mx_workload_full():
+    """The MXFP8 workload (decode shapes: X [64 x 4096], fused gate+up W
+    [24576 x 4096], dY [64 x 24576]): codes and E8M0 bytes of all three
+    tensors in both orientations bit for bit, and every output of FProp,
+    DGrad (split along K, as the benchmark runs it) and WGrad (K = 64)
+    against the oracle."""
     w = wl.mx(0)
     banner("mx workload: quantize X, W, dY in both orientations; FProp/DGrad/WGrad")
     X, W, dY = w["X"], w["W"], w["dY"]
@@ -54,32 +59,60 @@ def test_mx_workload_full():
     gq, ge, gqT, geT = fb.fp8_mx_quantize_1x32(dev(dY))
     y = host(fb.fp8_mx_gemm_fprop(xq, xe, wq, we, N, D, C))
     dx = host(fb.fp8_mx_gemm_dgrad(gq, ge, wqT, weT, N, D, C))
-    dw = fb.fp8_mx_gemm_wgrad(gqT, geT, xqT, xeT, N, D, C)
-    torch.cuda.synchronize()
+    dw = host(fb.fp8_mx_gemm_wgrad(gqT, geT, xqT, xeT, N, D, C))
     banner("mx workload: oracle")
-    oxq, oxe = oracle.mx_quant_rows(X)
-    owq, owe = oracle.mx_quant_rows(W)
-    assert_bytes_equal(host(wq), owq, "mx W row codes")
-    assert_bytes_equal(host(we), owe, "mx W row scales")
-    owqT, oweT = oracle.mx_quant_cols(W)
-    assert_bytes_equal(host(wqT), owqT, "mx W col codes")
-    assert_bytes_equal(host(weT), oweT, "mx W col scales")
-    ogq, oge = oracle.mx_quant_rows(dY)
-    y_ref = oracle.mx_gemm(oxq, oxe, owq, owe, C)
-    err = oracle.rel_row_error(y, y_ref)
-    banner(f"mx fprop err {err:.3e}")
-    assert err <= TOL
-    dx_ref = oracle.mx_gemm(ogq, oge, owqT, oweT, D)
-    err = oracle.rel_row_error(dx, dx_ref)
-    banner(f"mx dgrad err {err:.3e}")
-    assert err <= TOL
-    rows = np.sort(np.random.default_rng(3).choice(D, 256, replace=False))
-    ogqT, ogeT = oracle.mx_quant_cols(np.ascontiguousarray(dY[:, rows]))
-    oxqT, oxeT = oracle.mx_quant_cols(X)
-    dw_ref = oracle.mx_gemm(ogqT, ogeT, oxqT, oxeT, N)
-    err = oracle.rel_row_error(host(dw)[rows], dw_ref)
-    banner(f"mx wgrad err (sampled rows) {err:.3e}")
-    assert err <= TOL
+    ora = {}
+    for name, t, got in (("X", X, (xq, xe, xqT, xeT)), ("W", W, (wq, we, wqT, weT)),
+                         ("dY", dY, (gq, ge, gqT, geT))):
+        oq, oe = oracle.mx_quant_rows(t)
+        oqT, oeT = oracle.mx_quant_cols(t)
+        for g, o, what in zip(got, (oq, oe, oqT, oeT), ("row codes", "row scales", "col codes", "col scales")):
+            assert_bytes_equal(host(g), o, f"mx {name} {what}")
+        ora[name] = (oq, oe, oqT, oeT)
+    (oxq, oxe, oxqT, oxeT), (owq, owe, owqT, oweT), (ogq, oge, ogqT, ogeT) = ora["X"], ora["W"], ora["dY"]
+    for got, ref, name in ((y, oracle.mx_gemm(oxq, oxe, owq, owe, C), "fprop"),
+                           (dx, oracle.mx_gemm(ogq, oge, owqT, oweT, D), "dgrad"),
+                           (dw, oracle.mx_gemm(ogqT, ogeT, oxqT, oxeT, N), "wgrad")):
+        err = oracle.rel_row_error(got, ref)
+        banner(f"mx {name} err (full) {err:.3e}")
+        assert err <= TOL, (name, err)
+
+
+def test_blockscaled_path_on_mx_workload_full():
+    """The 1x128 / 128x128 path on the same tensors as the MXFP8 workload:
+    quantizer outputs bit for bit (X row-wise and token-axis, W with its
+    transposed codes, dY row-wise along D and token-axis) and every output
+    of FProp, DGrad (64 x 4096 with K = 24576, split along K) and WGrad
+    (24576 x 4096 with K = 64, one partial token group) against the oracle,
+    in the launch configurations the benchmark times."""
+    w = wl.mx(0)
+    X, W, dY = w["X"], w["W"], w["dY"]
+    N, C, D = 64, 4096, 24576
+    banner("1x128 path on the mx workload: quantize + FProp/DGrad/WGrad")
+    xqT, xsT, xq, xs = fb.fp8_quantize_transposed(dev(X), rowwise=True)
+    gqT, gsT, gq, gs = fb.fp8_quantize_transposed(dev(dY), rowwise=True)
+    wq, ws, wqT = fb.fp8_quantize_weight_128x128(dev(W))
+    y = host(fb.fp8_gemm_fprop(xq, xs, wq, ws, N, D, C))
+    dx = host(fb.fp8_gemm_dgrad(gq, gs, wqT, ws, N, D, C))
+    dw = host(fb.fp8_gemm_wgrad(gqT, gsT, xqT, xsT, N, D, C))
+    banner("1x128 path on the mx workload: oracle")
+    oxq, oxs = oracle.quant_1x128(X)
+    oxqT, oxsT = oracle.quant_colwise(X)
+    ogq, ogs = oracle.quant_1x128(dY)
+    ogqT, ogsT = oracle.quant_colwise(dY)
+    owq, ows, owqT = oracle.quant_128x128(W)
+    for g, o, what in ((xq, oxq, "X codes"), (xqT, oxqT, "X token-axis codes"), (gq, ogq, "dY codes"),
+                       (gqT, ogqT, "dY token-axis codes"), (wq, owq, "W codes"), (wqT, owqT, "W^T codes")):
+        assert_bytes_equal(host(g), o, what)
+    for g, o, what in ((xs, oxs, "X scales"), (xsT, oxsT, "X token-axis scales"), (gs, ogs, "dY scales"),
+                       (gsT, ogsT, "dY token-axis scales"), (ws, ows, "W scales")):
+        assert_scales_equal(host(g), o, what)
+    for got, ref, name in ((y, oracle.fprop(oxq, oxs, owq, ows, C), "fprop"),
+                           (dx, oracle.dgrad(ogq, ogs, owq, ows, D, C), "dgrad (K split)"),
+                           (dw, oracle.wgrad(ogqT, ogsT, oxqT, oxsT, N), "wgrad (K = 64)")):
+        err = oracle.rel_row_error(got, ref)
+        banner(f"1x128 {name} err (full) {err:.3e}")
+        assert err <= TOL, (name, err)
 
 
 @pytest.mark.parametrize("N,D,C", [(1, 16, 32), (3, 130, 300), (200, 300, 260), (257, 384, 1024)])
