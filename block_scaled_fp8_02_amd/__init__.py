@@ -66,6 +66,8 @@ _SIGS = {
     "fp8_gemm_dgrad_split_bytes": [_i64, _i64, _i64],
     "fp8_gemm_dgrad_split": [_p, _i64, _p, _i64, _p, _i64, _p, _i64, _p, _i32, _i64, _i64, _i64, _i64,
                              _p, _i64, _p],
+    "fp8_gemm_dgrad_split_noalloc": [_p, _i64, _p, _i64, _p, _i64, _p, _i64, _p, _i32, _i64, _i64, _i64, _i64,
+                                     _p],
     "fp8_gemm_wgrad": [_p, _i64, _p, _i64, _p, _i64, _p, _i64, _p, _i32, _i64, _i32, _i64, _i64, _i64, _p],
     "fp8_gemm_fprop_grouped": [_p, _i64, _p, _i64, _p, _i64, _i64, _p, _i64, _i64, _p, _i32, _i64,
                                _p, _i64, _i64, _i64, _i64, _p],
@@ -533,6 +535,19 @@ def fp8_gemm_dgrad(gq, gs, wqT, ws, N, D, C, dx=None, out_dtype=torch.bfloat16):
         _call("fp8_gemm_dgrad", *args, _stream(gq.device))
     else:
         _call("fp8_gemm_dgrad_split", *args, _ptr(work), work.numel(), _stream(gq.device))
+    return dx
+
+
+def fp8_gemm_dgrad_split_noalloc(gq, gs, wqT, ws, N, D, C, dx, out_dtype=None):
+    """DGrad (split along K for few rows) with the library's own scratch
+    array as the partial-sum workspace: neither this call nor the library
+    allocates device memory (dx must be given)."""
+    dev = gq.device
+    _need_gemm(dev, gq, gs, wqT, ws, N, C, D, "gq", "wqT", b_blocks=True)
+    _need(ws, "ws", _cdiv(D, 128), _cdiv(C, 128), _F32, dev)
+    _need(dx, "dx", N, C, _FLOAT_IO, dev)
+    _call("fp8_gemm_dgrad_split_noalloc", _ptr(gq), _ld(gq), _ptr(gs), _ld(gs), _ptr(wqT), _ld(wqT), _ptr(ws),
+          _ld(ws), _ptr(dx), _out_dtype_code(dx.dtype), _ld(dx), N, D, C, _stream(gq.device))
     return dx
 
 

@@ -4,6 +4,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <mutex>
+
 #include "../../include/fp8blk.h"
 #include "kernels.hpp"
 
@@ -485,6 +487,66 @@ int fp8_gemm_dgrad_split(const uint8_t* gq, int64_t ldgq, const float* gs, int64
                          void* work, int64_t work_bytes, void* stream) {
     return gemm_dgrad_split(1, gq, ldgq, gs, ldgs, wqT, ldwqT, ws, ldws, dx, dxt, lddx, N, D, C,
                             work, work_bytes, stream);
+}
+
+}  // extern "C"
+
+// Scratch of fp8_gemm_dgrad_split_noalloc: the largest fp32 partial-sum
+// workspace the split plan can ask for (256 blocks of 64 rows x 128 columns).
+// Each device holds its own copy from the library's load until the process
+// ends.  In host code `scratch` is only the host-side stand-in of the device
+// array: its device address is looked up per device (scratch_for_stream)
+// and only that address is passed to kernels.
+constexpr int64_t kNoAllocScratchBytes = 256 * 64 * 128 * 4;
+static __device__ __align__(256) uint8_t scratch[kNoAllocScratchBytes];
+
+namespace {
+
+constexpr int kMaxScratchDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_addr[kMaxScratchDevices];                   // per device, once looked up
+
+// Device address of `scratch` on the device that `stream` belongs to.  The
+// first call for a device makes that device current, asks the runtime for
+// the symbol's address there and restores the caller's device; later calls
+// reuse the address.  Allocates nothing.
+int scratch_for_stream(void* stream, void** out) {
+    int dev = 0;
+    hipError_t e = hipStreamGetDevice(static_cast<hipStream_t>(stream), &dev);
+    if (e != hipSuccess) return hip_status(e);
+    if (dev < 0 || dev >= kMaxScratchDevices) return FP8B_EUNSUPPORTED;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (g_scratch_addr[dev] == nullptr) {
+        int cur = 0;
+        e = hipGetDevice(&cur);
+        if (e != hipSuccess) return hip_status(e);
+        if (cur != dev && (e = hipSetDevice(dev)) != hipSuccess) return hip_status(e);
+        void* p = nullptr;
+        const hipError_t eg = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (cur != dev && (e = hipSetDevice(cur)) != hipSuccess) return hip_status(e);
+        if (eg != hipSuccess) return hip_status(eg);
+        if (p == nullptr) return hip_status(hipErrorInvalidSymbol);
+        g_scratch_addr[dev] = p;
+    }
+    *out = g_scratch_addr[dev];
+    return FP8B_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int fp8_gemm_dgrad_split_noalloc(const uint8_t* gq, int64_t ldgq, const float* gs, int64_t ldgs,
+                                 const uint8_t* wqT, int64_t ldwqT, const float* ws, int64_t ldws,
+                                 void* dx, int dxt, int64_t lddx, int64_t N, int64_t D, int64_t C,
+                                 void* stream) {
+    FP8B_TRY(validate_gemm(1, gq, ldgq, gs, ldgs, wqT, ldwqT, ws, ldws, dx, dxt, lddx, 0, N, D, C));
+    const int64_t need = dgrad_split_bytes(N, D, C);
+    if (need > kNoAllocScratchBytes) return FP8B_EUNSUPPORTED;
+    void* work = nullptr;
+    if (need > 0) FP8B_TRY(scratch_for_stream(stream, &work));
+    return gemm_dgrad_split(1, gq, ldgq, gs, ldgs, wqT, ldwqT, ws, ldws, dx, dxt, lddx, N, D, C,
+                            work, kNoAllocScratchBytes, stream);
 }
 
 int fp8_gemm_wgrad(const uint8_t* gqT, int64_t ldgqT, const float* gsT, int64_t ldgsT,

@@ -21,9 +21,11 @@
  * - All pointers are DEVICE pointers (except where stated) owned by the
  *   caller.  The library's own kernels allocate and free no device memory,
  *   and it keeps no state between calls apart from lazily loaded code
- *   objects and, for the two dequantized-backward GEMMs, one hipBLASLt
- *   handle per device (created on first use; hipBLASLt may allocate inside
- *   it) and a cache of the algorithms it chose per problem shape.
+ *   objects, for the two dequantized-backward GEMMs one hipBLASLt handle
+ *   per device (created on first use; hipBLASLt may allocate inside it) and
+ *   a cache of the algorithms it chose per problem shape, and for
+ *   fp8_gemm_dgrad_split_noalloc the device address of its scratch array on
+ *   each device.
  * - Every call is asynchronous on `stream` (a hipStream_t passed as void*;
  *   NULL is the default stream).  Buffers must stay valid until the stream
  *   reaches the operation.
@@ -329,6 +331,27 @@ FP8B_API int fp8_gemm_dgrad_split(const uint8_t* gq, int64_t ldgq, const float* 
                          const uint8_t* wqT, int64_t ldwqT, const float* ws, int64_t ldws,
                          void* dx, int dxt, int64_t lddx, int64_t N, int64_t D, int64_t C,
                          void* work, int64_t work_bytes, void* stream);
+
+/* fp8_gemm_dgrad_split without a workspace argument, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation).  The fp32 partial sums go to a scratch
+ * array of 8 MiB (the largest workspace fp8_gemm_dgrad_split_bytes can
+ * return) that the library holds in each device's memory from its load
+ * until the process ends; the call allocates and frees nothing.  Output
+ * bit for bit equal to fp8_gemm_dgrad_split's (same kernels, same
+ * partition).  The scratch array is shared by every call on one device and
+ * keeps the last call's partial sums (nothing in it needs clearing: each
+ * call writes every partial sum it reads): calls on one device must not
+ * overlap in time (same stream, or streams ordered by events), or they race
+ * on it.  The device is the one `stream` belongs to; its first call there
+ * looks the array's address up once (the current device is restored).
+ * Errors as fp8_gemm_dgrad, FP8B_EUNSUPPORTED if a split would need more
+ * than 8 MiB (no shape does) or the device index is 64 or more, FP8B_EHIP if
+ * the runtime cannot locate the array. */
+FP8B_API int fp8_gemm_dgrad_split_noalloc(const uint8_t* gq, int64_t ldgq, const float* gs, int64_t ldgs,
+                                 const uint8_t* wqT, int64_t ldwqT, const float* ws, int64_t ldws,
+                                 void* dx, int dxt, int64_t lddx, int64_t N, int64_t D, int64_t C,
+                                 void* stream);
 
 /* WGrad dW[D x C] = dY^T X (Jet-RL notes, section 2.2 WGrad; 4.2: both
  * operands grouped along the token axis).
