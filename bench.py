@@ -11,8 +11,8 @@ bf16, seeded synthetic data) on the GPU:
     DGrad  dX = dY W
     WGrad  dW = dY^T X
 value = 3 * 2*N*D*C FLOP / step time (TFLOP/s), inputs resident in HBM.
-Two copies of every input alternate between steps so nothing is reused
-from the 256 MB Infinity Cache across steps.
+Three copies of every input (1.1 GB) rotate between steps so nothing is
+reused from the 256 MB Infinity Cache across steps.
 
 Printed JSON line: the contract fields, a per-kernel breakdown (HIP-event
 time per launch on the launch stream, TFLOP/s or GB/s, fraction of the
@@ -40,6 +40,8 @@ PEAK_HBM_GBS = 8000.0         # MI355X HBM3E
 
 METRIC = "block-scaled FP8 GEMM TFLOPS (FProp/DGrad/WGrad) + quantize GB/s, % of peak"
 N, C, D = 8192, 12288, 4096
+NCOPIES = 3                   # input copies rotated between timed steps (1.1 GB)
+REPS = 50                     # timed launches per kernel in the side sections
 
 
 def parse():
@@ -166,8 +168,11 @@ def main():
     def to_dev(bits):
         return torch.from_numpy(bits).view(torch.bfloat16).to(dev)
 
+    # three copies of every input (3 x 368 MB = 1.1 GB) rotate between steps:
+    # more than the 256 MB Infinity Cache and the L2s can hold, so every step
+    # reads its bf16 inputs from HBM
     copies = []
-    for k in range(2):
+    for k in range(NCOPIES):
         Xd, Wd, Gd = to_dev(w["X"]), to_dev(w["W"]), to_dev(w["dY"])
         copies.append((Xd, Wd, Gd))
     # preallocated outputs (allocation is outside the timed region)
@@ -191,7 +196,7 @@ def main():
     events = {n: [] for n in names}
 
     def step(i, record):
-        Xd, Wd, Gd = copies[i % 2]
+        Xd, Wd, Gd = copies[i % NCOPIES]
         ev = []
 
         def mark():
@@ -295,11 +300,11 @@ def main():
     torch.cuda.synchronize()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     e0.record()
-    for _ in range(10):
+    for _ in range(REPS):
         dst.copy_(src)
     e1.record()
     torch.cuda.synchronize()
-    copy_gbs = 2 * src.numel() * 4 / (e0.elapsed_time(e1) * 1e-3 / 10) / 1e9
+    copy_gbs = 2 * src.numel() * 4 / (e0.elapsed_time(e1) * 1e-3 / REPS) / 1e9
     ceil["hbm_copy_gbs"] = round(copy_gbs, 1)
     del src, dst
     for n in ("quant_weight", "quant_dual_X", "quant_dual_dY"):
@@ -315,21 +320,35 @@ def main():
                 fn()
             torch.cuda.synchronize()
             e0.record()
-            for _ in range(10):
+            for _ in range(REPS):
                 fn()
             e1.record()
             torch.cuda.synchronize()
-            t = e0.elapsed_time(e1) * 1e-3 / 10
+            t = e0.elapsed_time(e1) * 1e-3 / REPS
             tw[name] = {"us": round(t * 1e6, 1), "tflops": round(flops_gemm / t / 1e12, 1)}
         except Exception as ex:                                     # no fp8 GEMM in this torch build
             tw[name] = {"error": str(ex)[:120]}
     ceil["fp8_tensorwise_hipblaslt"] = tw
+    # matrix-core throughput on random register operands, all compute units
+    ceil["mfma_random_operands"] = mfma_peaks(torch, fb, dev)
+    pk8 = ceil["mfma_random_operands"]["fp8_16x16x128"]["tflops"]
+    pk16 = ceil["mfma_random_operands"]["bf16_16x16x32"]["tflops"]
+    for n in ("fprop", "dgrad", "wgrad"):
+        kernels[n]["frac_measured_fp8_mfma"] = round(kernels[n]["tflops"] / pk8, 4)
+    roofline["frac_measured_peak"] = round(roofline["achieved"] / pk8, 4)
+    roofline["measured_peak"] = pk8
+    for n, e in bf.items():
+        e["frac_measured_bf16_mfma"] = round(e["tflops"] / pk16, 4)
 
     pow2 = requant = deqbwd = None
     if not args.no_other:
         pow2 = pow2_layer(torch, fb, copies, flops_gemm)
         requant = requant_layer(torch, fb, copies)
         deqbwd = dequant_backward(torch, fb, copies, flops_gemm)
+        pk16 = ceil["mfma_random_operands"]["bf16_16x16x32"]["tflops"]
+        for n in ("dgrad", "wgrad"):
+            deqbwd[n]["frac_measured_bf16_mfma"] = round(deqbwd[n]["tflops"] / pk16, 4)
+            deqbwd[n]["speedup_vs_torch_bf16"] = round(bf[n]["us"] / deqbwd[n]["us"], 3)
 
     other = fused = None
     if not args.no_other:
@@ -338,9 +357,20 @@ def main():
         other = other_workloads(torch, fb, wl, dev, args.seed)
         fused = fused_producers(torch, fb, wl, dev, args.seed)
 
-    cpu = None
+    tiny = None
+    if not args.no_other:
+        tiny = tiny_layer(torch, fb, wl, dev, args.seed)
+
+    cpu = cpu_cfg = qerr = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(w, args.cpu_seconds)
+        del w
+        cpu_cfg = cpu_oracle_configs(args.seed, cpu)
+        qerr = quant_error_mx_vs_blockscaled(args.seed)
+        if other is not None:
+            for op in ("fprop", "dgrad", "wgrad"):
+                qerr[op]["tflops_blockscaled"] = other["decode_1x128"][op].get("tflops")
+                qerr[op]["tflops_mxfp8"] = other["decode_mxfp8"][op].get("tflops")
 
     out = {
         "metric": METRIC, "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1,
@@ -352,6 +382,9 @@ def main():
                                "1x128 act/grad + 128x128 weight FP8 path, FProp+DGrad+WGrad",
                    "N": N, "C": C, "D": D, "seed": args.seed, "inputs_resident_in_hbm": True},
         "kernels": kernels, "roofline": roofline, "bf16_baseline": bf, "cpu_baseline": cpu,
+        "cpu_oracle_by_config": cpu_cfg,
+        "quant_error_mx_vs_blockscaled": qerr,
+        "tiny_layer": tiny,
         "measured_ceilings": ceil,
         "pow2_scales_layer": pow2,
         "requant_from_fp8_X": requant,
@@ -362,7 +395,7 @@ def main():
     print(json.dumps(out), flush=True)
 
 
-def time_cold(torch, fn, flush, reps=10, warmup=2):
+def time_cold(torch, fn, flush, reps=REPS, warmup=2):
     """Median seconds of fn() on the current stream, each launch preceded
     (outside the events) by a 1 GiB read so that L2 and the Infinity Cache
     hold none of its operands."""
@@ -422,11 +455,11 @@ def pow2_layer(torch, fb, copies, flops_gemm):
         torch.cuda.synchronize()
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e0.record()
-        for _ in range(10):
+        for _ in range(REPS):
             fn()
         e1.record()
         torch.cuda.synchronize()
-        t = e0.elapsed_time(e1) * 1e-3 / 10
+        t = e0.elapsed_time(e1) * 1e-3 / REPS
         ent = {"us": round(t * 1e6, 2)}
         if name in ("fprop", "dgrad", "wgrad"):
             ent["tflops"] = round(flops_gemm / t / 1e12, 1)
@@ -466,10 +499,12 @@ def requant_layer(torch, fb, copies):
 
 def dequant_backward(torch, fb, copies, flops_gemm):
     """The training layer's backward in the dequantized mode: DGrad and
-    WGrad as bf16 GEMMs (hipBLASLt) on the forward's FP8 W and X codes
-    dequantized to bf16 (each entry point times its dequantization and its
-    GEMM), the dequantization kernels alone, and the bytes each mode keeps
-    between the forward and the backward pass.  Warm operands, 10 launches."""
+    WGrad as bf16 GEMMs (the library's bf16 MFMA kernel) on the forward's
+    FP8 W and X codes dequantized to bf16; each entry point's time includes
+    the transposing copies that give the GEMM its K-contiguous operands (W^T
+    dequantized for DGrad; X^T dequantized and dY^T for WGrad).  Also the
+    plain dequantization kernels alone, and the bytes each mode keeps between
+    the forward and the backward pass.  Warm operands, REPS launches."""
     Xd, Wd, Gd = copies[0]
     N, C = Xd.shape
     D = Wd.shape[0]
@@ -477,12 +512,13 @@ def dequant_backward(torch, fb, copies, flops_gemm):
     xq, xs = fb.fp8_quantize_act_1x128(Xd)
     wq, ws, _ = fb.fp8_quantize_weight_128x128(Wd, transpose=False)
     bf = dict(dtype=torch.bfloat16, device=Xd.device)
-    workW, workX = torch.empty((D, C), **bf), torch.empty((N, C), **bf)
+    workW, workX = torch.empty((C, D), **bf), torch.empty((C + D, N), **bf)
+    plainW, plainX = torch.empty((D, C), **bf), torch.empty((N, C), **bf)
     dx, dw = torch.empty((N, C), **bf), torch.empty((D, C), **bf)
     runs = {
-        "dequant_W": (lambda: fb.fp8_dequantize_bf16(wq, ws, fb.FP8B_SCALE_BLOCKS_128X128, C, out=workW),
+        "dequant_W": (lambda: fb.fp8_dequantize_bf16(wq, ws, fb.FP8B_SCALE_BLOCKS_128X128, C, out=plainW),
                       D * C + cd(D, 128) * cd(C, 128) * 4 + 2 * D * C, None),
-        "dequant_X": (lambda: fb.fp8_dequantize_bf16(xq, xs, fb.FP8B_SCALE_ROWS_1X128, C, out=workX),
+        "dequant_X": (lambda: fb.fp8_dequantize_bf16(xq, xs, fb.FP8B_SCALE_ROWS_1X128, C, out=plainX),
                       N * C + N * cd(C, 128) * 4 + 2 * N * C, None),
         "dgrad": (lambda: fb.fp8_dequant_gemm_dgrad(Gd, wq, ws, fb.FP8B_SCALE_BLOCKS_128X128, N, D, C,
                                                     dx=dx, work=workW), None, flops_gemm),
@@ -496,11 +532,11 @@ def dequant_backward(torch, fb, copies, flops_gemm):
         torch.cuda.synchronize()
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e0.record()
-        for _ in range(10):
+        for _ in range(REPS):
             fn()
         e1.record()
         torch.cuda.synchronize()
-        t = e0.elapsed_time(e1) * 1e-3 / 10
+        t = e0.elapsed_time(e1) * 1e-3 / REPS
         ent = {"us": round(t * 1e6, 2)}
         if nbytes:
             ent["gbs"] = round(nbytes / t / 1e9, 1)
@@ -511,8 +547,8 @@ def dequant_backward(torch, fb, copies, flops_gemm):
         out[name] = ent
     fp8_x = N * C + N * cd(C, 128) * 4
     out["kept_bytes"] = {"fp8_backward": 2 * fp8_x, "dequantized_backward": fp8_x,
-                         "dequantized_transient_workspace": 2 * N * C}
-    del workW, workX, dx, dw
+                         "dequantized_transient_workspace": 2 * (C + D) * N}
+    del workW, workX, plainW, plainX, dx, dw
     return out
 
 
@@ -717,6 +753,270 @@ def cpu_baseline(w, budget_s: float):
             "sample": f"W quantized 128x128 in full; {rows} token rows of X and dY through 1x128 "
                       f"quantization and FProp/DGrad; X and {rows} columns of dY through token-axis "
                       f"quantization and {rows} rows of WGrad (fp64 GEMMs)"}
+
+
+def mfma_peaks(torch, fb, dev):
+    """Matrix-core throughput on random operands held in registers (the
+    library's measurement kernel fp8b_mfma_peak): fp8 16x16x128 and bf16
+    16x16x32 MFMAs on every compute unit with 2 and 4 waves per SIMD; the
+    faster setting is the measured ceiling.  Median of REPS launches."""
+    cus = torch.cuda.get_device_properties(dev).multi_processor_count
+    out = {}
+    for kind, name, iters, spec in ((0, "fp8_16x16x128", 2000, PEAK_FP8_TFLOPS),
+                                    (1, "bf16_16x16x32", 4000, PEAK_BF16_TFLOPS)):
+        runs = {}
+        for wps in (2, 4):
+            blocks = cus * wps                      # a block is one wave per SIMD of a CU
+            buf, flops = fb.fp8b_mfma_peak(kind, blocks, iters, seed=1)
+            for _ in range(2):
+                fb.fp8b_mfma_peak(kind, blocks, iters, seed=1, out=buf)
+            torch.cuda.synchronize()
+            ts = []
+            for _ in range(REPS):
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record()
+                fb.fp8b_mfma_peak(kind, blocks, iters, seed=1, out=buf)
+                e1.record()
+                torch.cuda.synchronize()
+                ts.append(e0.elapsed_time(e1) * 1e-3)
+            t = float(np.median(ts))
+            runs[f"{wps}_waves_per_simd"] = {"us": round(t * 1e6, 1), "tflops": round(flops / t / 1e12, 1)}
+        best = max(r["tflops"] for r in runs.values())
+        out[name] = {"tflops": best, "frac_spec": round(best / spec, 4), "spec_tflops": spec, "runs": runs}
+    return out
+
+
+def tiny_layer(torch, fb, wl, dev, seed):
+    """The tiny plumbing layer (X fp32 [256 x 512], W [384 x 512], dY [256 x
+    384]): every kernel of the path, warm, the mean of REPS back-to-back
+    launches (launch-latency bound: time only)."""
+    w = wl.tiny(seed)
+    X, W, dY = (torch.from_numpy(w[k]).to(dev) for k in ("X", "W", "dY"))
+    Nt, Ct, Dt = w["N"], w["C"], w["D"]
+    xq, xs = fb.fp8_quantize_act_1x128(X)
+    gq, gs = fb.fp8_quantize_act_1x128(dY)
+    wq, ws, wqT = fb.fp8_quantize_weight_128x128(W)
+    xd = fb.fp8_quantize_transposed(X, rowwise=True)
+    gd = fb.fp8_quantize_transposed(dY, rowwise=True)
+    y = torch.empty((Nt, Dt), dtype=torch.bfloat16, device=dev)
+    dx = torch.empty((Nt, Ct), dtype=torch.bfloat16, device=dev)
+    dw = torch.empty((Dt, Ct), dtype=torch.bfloat16, device=dev)
+    runs = {
+        "quant_act_X": lambda: fb.fp8_quantize_act_1x128(X, xq, xs),
+        "quant_act_dY": lambda: fb.fp8_quantize_act_1x128(dY, gq, gs),
+        "quant_weight": lambda: fb.fp8_quantize_weight_128x128(W, q=wq, s=ws, qT=wqT),
+        "quant_dual_X": lambda: fb.fp8_quantize_transposed(X, rowwise=True, qT=xd[0], sT=xd[1], q=xd[2], s=xd[3]),
+        "quant_dual_dY": lambda: fb.fp8_quantize_transposed(dY, rowwise=True, qT=gd[0], sT=gd[1], q=gd[2], s=gd[3]),
+        "fprop": lambda: fb.fp8_gemm_fprop(xq, xs, wq, ws, Nt, Dt, Ct, y=y),
+        "dgrad": lambda: fb.fp8_gemm_dgrad(gq, gs, wqT, ws, Nt, Dt, Ct, dx=dx),
+        "wgrad": lambda: fb.fp8_gemm_wgrad(gd[0], gd[1], xd[0], xd[1], Nt, Dt, Ct, dw=dw),
+    }
+    out = {}
+    for name, fn in runs.items():
+        for _ in range(3):
+            fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(REPS):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        out[name] = {"us": round(e0.elapsed_time(e1) * 1e3 / REPS, 2)}
+    return out
+
+
+def cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def quant_error_mx_vs_blockscaled(seed):
+    """Quantization error of the two recipes on the MXFP8 workload's tensors
+    (X [64 x 4096], W [24576 x 4096], dY [64 x 24576], bf16): for each
+    GEMM, max |y_recipe - y_exact| / ||y_exact row||, with y_recipe the
+    oracle's GEMM on the recipe's dequantized operands (1x128 / 128x128 FP32
+    scales, or MXFP8 1x32 E8M0) and y_exact the fp64 GEMM of the unquantized
+    bf16 inputs."""
+    import oracle
+    from block_scaled_fp8_02_amd import workloads as wl
+    w = wl.mx(seed)
+    X, W, dY = w["X"], w["W"], w["dY"]
+    Nm, Cm, Dm = w["N"], w["C"], w["D"]
+    Xf, Wf, Gf = (oracle.as_f32(t).astype(np.float64) for t in (X, W, dY))
+    xq, xs = oracle.quant_1x128(X)
+    wq, ws, _ = oracle.quant_128x128(W, with_transpose=False)
+    gq, gs = oracle.quant_1x128(dY)
+    gqT, gsT = oracle.quant_colwise(dY)
+    xqT, xsT = oracle.quant_colwise(X)
+    mxq, mxe = oracle.mx_quant_rows(X)
+    mxqT, mxeT = oracle.mx_quant_cols(X)
+    mwq, mwe = oracle.mx_quant_rows(W)
+    mwqT, mweT = oracle.mx_quant_cols(W)
+    mgq, mge = oracle.mx_quant_rows(dY)
+    mgqT, mgeT = oracle.mx_quant_cols(dY)
+    ops = {
+        "fprop": (lambda: oracle.matmul_f64(Xf, Wf.T), lambda: oracle.fprop(xq, xs, wq, ws, Cm),
+                  lambda: oracle.mx_gemm(mxq, mxe, mwq, mwe, Cm)),
+        "dgrad": (lambda: oracle.matmul_f64(Gf, Wf), lambda: oracle.dgrad(gq, gs, wq, ws, Dm, Cm),
+                  lambda: oracle.mx_gemm(mgq, mge, mwqT, mweT, Dm)),
+        "wgrad": (lambda: oracle.matmul_f64(Gf.T, Xf), lambda: oracle.wgrad(gqT, gsT, xqT, xsT, Nm),
+                  lambda: oracle.mx_gemm(mgqT, mgeT, mxqT, mxeT, Nm)),
+    }
+    out = {}
+    for op, (exact, blk, mx) in ops.items():
+        ye = exact()
+        out[op] = {"blockscaled_1x128_128x128": float(f"{oracle.rel_row_error(blk(), ye):.4e}"),
+                   "mxfp8_1x32": float(f"{oracle.rel_row_error(mx(), ye):.4e}")}
+    out["metric"] = ("max |y_q - y_exact| / ||y_exact row||_2, y_q the oracle GEMM on one recipe's "
+                     "dequantized operands, y_exact the fp64 GEMM of the unquantized bf16 inputs")
+    return out
+
+
+def cpu_oracle_configs(seed, c3_sample):
+    """The oracle as it stands, on the host's cores, on every workload:
+    quantizers at full size everywhere, GEMMs at full size on the tiny,
+    decode, MXFP8 and MoE workloads; the training GEMMs are extrapolated
+    from the timed row sample of cpu_baseline (flagged).  Bytes are the
+    algorithmic bytes of the same operation on the GPU."""
+    import oracle
+    from block_scaled_fp8_02_amd import workloads as wl
+    cd = lambda a, b: (a + b - 1) // b
+    rup = lambda a: cd(a, 128) * 128
+
+    def timed(fn):
+        t0 = time.perf_counter()
+        r = fn()
+        return time.perf_counter() - t0, r
+
+    def qent(fn, nbytes):
+        t, r = timed(fn)
+        return {"s": round(t, 4), "gbs": round(nbytes / t / 1e9, 3)}, r
+
+    def gent(fn, flops):
+        t, r = timed(fn)
+        return {"s": round(t, 4), "gflops": round(flops / t / 1e9, 3)}, r
+
+    def b_act(rows, cols, esz):                         # 1x128 quantizer: in + codes + scales
+        return rows * cols * esz + rows * rup(cols) + rows * cd(cols, 128) * 4
+
+    def b_dual(rows, cols, esz):                        # row-wise + token-axis copies
+        return rows * cols * esz + rows * rup(cols) + cols * rup(rows) + (rows * cd(cols, 128) + cols * cd(rows, 128)) * 4
+
+    def b_w(Dw, Cw, esz, qT=True):
+        return Dw * Cw * esz + Dw * rup(Cw) * (2 if qT else 1) + cd(Dw, 128) * cd(Cw, 128) * 4
+
+    res = {"threads": int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1)), "cpu_model": cpu_model()}
+
+    # tiny (fp32 inputs)
+    w = wl.tiny(seed)
+    X, W, dY = w["X"], w["W"], w["dY"]
+    n, c, d = w["N"], w["C"], w["D"]
+    e = {}
+    e["quant_weight"], (wq, ws, _) = qent(lambda: oracle.quant_128x128(W), b_w(d, c, 4))
+    e["quant_dual_X"], (xq, xs, xqT, xsT) = qent(lambda: oracle.quant_1x128(X) + oracle.quant_colwise(X),
+                                                 b_dual(n, c, 4))
+    e["quant_dual_dY"], (gq, gs, gqT, gsT) = qent(lambda: oracle.quant_1x128(dY) + oracle.quant_colwise(dY),
+                                                  b_dual(n, d, 4))
+    e["fprop"], _ = gent(lambda: oracle.fprop(xq, xs, wq, ws, c), 2.0 * n * d * c)
+    e["dgrad"], _ = gent(lambda: oracle.dgrad(gq, gs, wq, ws, d, c), 2.0 * n * d * c)
+    e["wgrad"], _ = gent(lambda: oracle.wgrad(gqT, gsT, xqT, xsT, n), 2.0 * n * d * c)
+    res["tiny"] = e
+
+    # decode (bf16)
+    w = wl.decode(seed)
+    X, W = w["X"], w["W"]
+    n, c, d = w["N"], w["C"], w["D"]
+    e = {}
+    e["quant_act_X"], (xq, xs) = qent(lambda: oracle.quant_1x128(X), b_act(n, c, 2))
+    e["quant_weight"], (wq, ws, _) = qent(lambda: oracle.quant_128x128(W, with_transpose=False), b_w(d, c, 2, False))
+    e["fprop"], _ = gent(lambda: oracle.fprop(xq, xs, wq, ws, c), 2.0 * n * d * c)
+    res["decode"] = e
+    del w, X, W, wq
+
+    # training layer: quantizers at full size, GEMMs from the row sample
+    w = wl.train(seed)
+    X, W, dY = w["X"], w["W"], w["dY"]
+    n, c, d = w["N"], w["C"], w["D"]
+    e = {}
+    e["quant_weight"], _ = qent(lambda: oracle.quant_128x128(W), b_w(d, c, 2))
+    e["quant_dual_X"], _ = qent(lambda: oracle.quant_1x128(X) + oracle.quant_colwise(X), b_dual(n, c, 2))
+    e["quant_dual_dY"], _ = qent(lambda: oracle.quant_1x128(dY) + oracle.quant_colwise(dY), b_dual(n, d, 2))
+    if c3_sample:
+        rate = c3_sample["value"] * 1e12
+        for op in ("fprop", "dgrad", "wgrad"):
+            e[op] = {"s_extrapolated": round(2.0 * n * d * c / rate, 2), "gflops": round(rate / 1e9, 3),
+                     "flag": "extrapolated linearly from the timed row sample (cpu_baseline)"}
+    res["train"] = e
+    del w, X, W, dY
+
+    # MXFP8 workload: MX quantizers (both orientations) and GEMMs, and the
+    # 1x128 / 128x128 path on the same tensors, all at full size
+    w = wl.mx(seed)
+    X, W, dY = w["X"], w["W"], w["dY"]
+    n, c, d = w["N"], w["C"], w["D"]
+    mxb = lambda r, k: r * k * 2 + 2 * (r * rup(k) + r * rup(k) // 32)
+    e = {}
+    e["mx_quant_X"], (mxq, mxe, mxqT, mxeT) = qent(lambda: oracle.mx_quant_rows(X) + oracle.mx_quant_cols(X), mxb(n, c))
+    e["mx_quant_W"], (mwq, mwe, mwqT, mweT) = qent(lambda: oracle.mx_quant_rows(W) + oracle.mx_quant_cols(W), mxb(d, c))
+    e["mx_quant_dY"], (mgq, mge, mgqT, mgeT) = qent(lambda: oracle.mx_quant_rows(dY) + oracle.mx_quant_cols(dY),
+                                                    mxb(n, d))
+    e["mx_fprop"], _ = gent(lambda: oracle.mx_gemm(mxq, mxe, mwq, mwe, c), 2.0 * n * d * c)
+    e["mx_dgrad"], _ = gent(lambda: oracle.mx_gemm(mgq, mge, mwqT, mweT, d), 2.0 * n * d * c)
+    e["mx_wgrad"], _ = gent(lambda: oracle.mx_gemm(mgqT, mgeT, mxqT, mxeT, n), 2.0 * n * d * c)
+    del mwq, mwqT
+    e["quant_weight"], (wq, ws, _) = qent(lambda: oracle.quant_128x128(W), b_w(d, c, 2))
+    e["quant_dual_X"], (xq, xs, xqT, xsT) = qent(lambda: oracle.quant_1x128(X) + oracle.quant_colwise(X),
+                                                 b_dual(n, c, 2))
+    e["quant_dual_dY"], (gq, gs, gqT, gsT) = qent(lambda: oracle.quant_1x128(dY) + oracle.quant_colwise(dY),
+                                                  b_dual(n, d, 2))
+    e["fprop"], _ = gent(lambda: oracle.fprop(xq, xs, wq, ws, c), 2.0 * n * d * c)
+    e["dgrad"], _ = gent(lambda: oracle.dgrad(gq, gs, wq, ws, d, c), 2.0 * n * d * c)
+    e["wgrad"], _ = gent(lambda: oracle.wgrad(gqT, gsT, xqT, xsT, n), 2.0 * n * d * c)
+    res["mx"] = e
+    del w, X, W, dY, wq
+
+    # MoE layer: stacked expert weights, grouped token-axis quantizers, and
+    # all six GEMMs expert by expert
+    m = wl.moe(seed)
+    offs = m["offsets"]
+    E, I2, H = m["W_gu"].shape
+    I = m["inter"]
+    R = int(offs[-1])
+    P = oracle.padded_offsets(offs)
+    e = {}
+    e["quant_W_gu"], (guq, gus, _) = qent(lambda: oracle.quant_128x128(m["W_gu"].reshape(E * I2, H)),
+                                          b_w(E * I2, H, 2))
+    e["quant_W_d"], (dnq, dns, _) = qent(lambda: oracle.quant_128x128(m["W_d"].reshape(E * H, I)), b_w(E * H, I, 2))
+    q = {}
+    for name, t, k in (("X", m["X_perm"], H), ("A", m["A"], I), ("dH", m["dH"], I2), ("dY", m["dY_d"], H)):
+        e[f"quant_dual_{name}"], q[name] = qent(lambda: oracle.quant_1x128(t) + oracle.quant_colwise(t, offs),
+                                                b_dual(R, k, 2) + 128 * E * k)
+    tg = {k: 0.0 for k in ("gu_fprop", "gu_dgrad", "gu_wgrad", "d_fprop", "d_dgrad", "d_wgrad")}
+    for x in range(E):
+        a, b = int(offs[x]), int(offs[x + 1])
+        p0, p1 = int(P[x]), int(P[x + 1])
+        for pre, wq_, ws_, Dn, Cn, xin, gin in (("gu", guq, gus, I2, H, q["X"], q["dH"]),
+                                                 ("d", dnq, dns, H, I, q["A"], q["dY"])):
+            wq_e = wq_[x * Dn:(x + 1) * Dn]
+            ws_e = ws_[x * Dn // 128:(x + 1) * Dn // 128]
+            t, _ = timed(lambda: oracle.fprop(xin[0][a:b], xin[1][a:b], wq_e, ws_e, Cn))
+            tg[f"{pre}_fprop"] += t
+            t, _ = timed(lambda: oracle.dgrad(gin[0][a:b], gin[1][a:b], wq_e, ws_e, Dn, Cn))
+            tg[f"{pre}_dgrad"] += t
+            t, _ = timed(lambda: oracle.wgrad(gin[2][:, p0:p1], gin[3][:, p0 // 128:p1 // 128],
+                                              xin[2][:, p0:p1], xin[3][:, p0 // 128:p1 // 128], p1 - p0))
+            tg[f"{pre}_wgrad"] += t
+    for k, t in tg.items():
+        fl = 2.0 * R * I2 * H if k.startswith("gu") else 2.0 * R * H * I
+        e[k] = {"s": round(t, 4), "gflops": round(fl / t / 1e9, 3)}
+    res["moe"] = e
+    return res
 
 
 if __name__ == "__main__":

@@ -82,6 +82,7 @@ _SIGS = {
                                 _p, _i64, _p],
     "fp8_mx_gemm_wgrad": [_p, _i64, _p, _i64, _p, _i64, _p, _i64, _p, _i32, _i64, _i32, _i64, _i64, _i64, _p],
     "fp8b_e4m3_encode": [_p, _p, _i64, _p, _p],
+    "fp8b_mfma_peak": [_i32, _i64, _i64, ctypes.c_uint32, _p, _p, _p],
     "fp8b_validate_gemm": [_i32, _p, _i64, _p, _i64, _p, _i64, _p, _i64, _p, _i32, _i64, _i32,
                            _i64, _i64, _i64],
     "fp8b_abi_version": [],
@@ -376,16 +377,16 @@ def fp8_dequantize_bf16(q, s, kind: int, cols: int, out=None):
 
 
 def fp8_dequant_gemm_dgrad(dy, wq, ws, wkind: int, N: int, D: int, C: int, dx=None, work=None):
-    """dX = dY W^ in bf16 (hipBLASLt) with W^ the dequantized weight codes;
-    work (D x C bf16) receives W^."""
+    """dX = dY W^ in bf16 (the library's bf16 MFMA GEMM) with W^ the
+    dequantized weight codes; work (C x D bf16) receives W^ transposed."""
     dev = dy.device
     _need(dy, "dy", N, D, _BF16, dev)
     _need(wq, "wq", D, _rup(C), _U8, dev)
     _need_scales(ws, "ws", wkind, D, C, dev)
     dx = _new_out(N, C, torch.bfloat16, dev) if dx is None else dx
-    work = _new_out(D, C, torch.bfloat16, dev) if work is None else work
+    work = _new_out(C, D, torch.bfloat16, dev) if work is None else work
     _need(dx, "dx", N, C, _BF16, dev)
-    _need(work, "work", D, C, _BF16, dev)
+    _need(work, "work", C, D, _BF16, dev)
     _call("fp8_dequant_gemm_dgrad", _ptr(dy), _ld(dy), _ptr(wq), _ld(wq), _ptr(ws), _ld(ws), int(wkind),
           N, D, C, _ptr(dx), _ld(dx), _ptr(work), _ld(work), _stream(dy.device))
     return dx
@@ -393,16 +394,17 @@ def fp8_dequant_gemm_dgrad(dy, wq, ws, wkind: int, N: int, D: int, C: int, dx=No
 
 def fp8_dequant_gemm_wgrad(dy, xq, xs, xkind: int, N: int, D: int, C: int, dw=None,
                            out_dtype=torch.bfloat16, beta: int = 0, work=None):
-    """dW (+)= dY^T X^ in bf16 (hipBLASLt) with X^ the dequantized activation
-    codes; work (N x C bf16) receives X^."""
+    """dW (+)= dY^T X^ in bf16 (the library's bf16 MFMA GEMM) with X^ the
+    dequantized activation codes; work ((C + D) x N bf16) receives X^
+    transposed, then dY transposed."""
     dev = dy.device
     _need(dy, "dy", N, D, _BF16, dev)
     _need(xq, "xq", N, _rup(C), _U8, dev)
     _need_scales(xs, "xs", xkind, N, C, dev)
     dw = _new_out(D, C, out_dtype, dev) if dw is None else dw
-    work = _new_out(N, C, torch.bfloat16, dev) if work is None else work
+    work = _new_out(C + D, N, torch.bfloat16, dev) if work is None else work
     _need(dw, "dw", D, C, _FLOAT_IO, dev)
-    _need(work, "work", N, C, _BF16, dev)
+    _need(work, "work", C + D, N, _BF16, dev)
     _call("fp8_dequant_gemm_wgrad", _ptr(dy), _ld(dy), _ptr(xq), _ld(xq), _ptr(xs), _ld(xs), int(xkind),
           N, D, C, _ptr(dw), _out_dtype_code(dw.dtype), _ld(dw), int(beta), _ptr(work), _ld(work),
           _stream(dy.device))
@@ -705,6 +707,18 @@ def fp8b_e4m3_encode(x, s=None, out=None):
         raise ValueError("out must be a contiguous uint8 tensor with one byte per element of x")
     _call("fp8b_e4m3_encode", _ptr(x), _ptr(s), x.numel(), _ptr(out), _stream(x.device))
     return out
+
+
+def fp8b_mfma_peak(kind: int, blocks: int, iters: int, seed: int = 0, out=None, device=None):
+    """Launch the matrix-core throughput kernel (kind 0 fp8, 1 bf16) on the
+    current stream; returns (out tensor, FLOPs launched)."""
+    dev = torch.device("cuda", torch.cuda.current_device()) if device is None else device
+    out = _new((4 * blocks,), torch.float32, dev) if out is None else out
+    if out.device != dev or out.dtype != torch.float32 or not out.is_contiguous() or out.numel() < 4 * blocks:
+        raise ValueError("out must be a contiguous float32 tensor with 4 * blocks elements on the device")
+    flops = ctypes.c_double(0.0)
+    _call("fp8b_mfma_peak", kind, blocks, iters, seed, _ptr(out), ctypes.byref(flops), _stream(dev))
+    return out, flops.value
 
 
 def fp8b_validate_gemm(op, a, lda, sa, ldsa, b, ldb, sb, ldsb, out, out_dtype, ldo, beta, N, D, C) -> int:

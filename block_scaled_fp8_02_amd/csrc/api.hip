@@ -149,7 +149,7 @@ int check_offsets(const int32_t* offsets, int64_t E) {
 
 extern "C" {
 
-int fp8b_abi_version(void) { return 1; }
+int fp8b_abi_version(void) { return 2; }
 
 const char* fp8b_status_string(int status) {
     switch (status) {
@@ -329,24 +329,12 @@ static int check_fp8_operand(const uint8_t* q, int64_t ldq, const void* sc, int6
     return check_scales(sc, rows, rup128(cols) / 32, lds, 1);
 }
 
-// A bf16 or fp32 matrix only hipBLASLt touches: element alignment, any
-// leading dimension >= cols.
-static int check_blas_matrix(const void* p, int dt, int64_t rows, int64_t cols, int64_t ld) {
-    if (!dtype_ok(dt)) return FP8B_EINVAL;
-    if (rows < 0 || cols < 0 || ld < cols) return FP8B_ESHAPE;
-    if (rows == 0 || cols == 0) return FP8B_OK;
-    if (p == nullptr) return FP8B_EINVAL;
-    if (!aligned(p, (uintptr_t)esize(dt))) return FP8B_EALIGN;
-    return FP8B_OK;
-}
+// Largest row stride (elements) of a bf16 GEMM operand: a tile's 256 rows
+// are addressed with 32-bit byte offsets, as in the FP8 GEMMs.
+constexpr int64_t kMaxBf16Ld = (int64_t)1 << 23;
 
-static int lt_status_code(hipError_t e, int lt) {
-    if (lt != 0) {
-        g_last_hip_error = -lt;                 // hipBLASLt status, negated
-        return FP8B_EHIP;
-    }
-    return hip_status(e);
-}
+// Source kind of launch_transpose_bf16 for an FP8 operand of scale kind `kind`.
+static inline int transpose_src(int kind) { return kind + 1; }
 
 int fp8_dequantize_bf16(const uint8_t* q, int64_t ldq, const void* sc, int64_t lds, int kind,
                         int64_t rows, int64_t cols, uint16_t* out, int64_t ldo, void* stream) {
@@ -360,17 +348,21 @@ int fp8_dequant_gemm_dgrad(const uint16_t* dy, int64_t lddy, const uint8_t* wq, 
                            const void* ws, int64_t ldws, int wkind, int64_t N, int64_t D, int64_t C,
                            uint16_t* dx, int64_t lddx, uint16_t* work, int64_t ldwork, void* stream) {
     if (wkind != FP8B_SCALE_BLOCKS_128X128 && wkind != FP8B_SCALE_MX_1X32) return FP8B_EINVAL;
-    FP8B_TRY(check_blas_matrix(dy, FP8B_BF16, N, D, lddy));
+    FP8B_TRY(check_input(dy, FP8B_BF16, N, D, lddy));
     FP8B_TRY(check_fp8_operand(wq, ldwq, ws, ldws, wkind, D, C));
-    FP8B_TRY(check_input(work, FP8B_BF16, D, C, ldwork));
-    FP8B_TRY(check_blas_matrix(dx, FP8B_BF16, N, C, lddx));
+    FP8B_TRY(check_input(work, FP8B_BF16, C, D, ldwork));          // receives W^T [C x D]
+    FP8B_TRY(check_output(dx, FP8B_BF16, N, C, lddx, 0));
+    if (lddy > kMaxBf16Ld || ldwork > kMaxBf16Ld) return FP8B_EUNSUPPORTED;
     const hipStream_t st = static_cast<hipStream_t>(stream);
     if (N == 0 || C == 0) return FP8B_OK;
     if (D == 0) return hip_status(launch_zero_2d(dx, lddx * 2, C * 2, N, st));
-    FP8B_TRY(hip_status(launch_dequant_bf16(wq, ldwq, ws, ldws, wkind, D, C, work, ldwork, st)));
-    int lt = 0;
-    const hipError_t e = lt_gemm(false, false, C, N, D, work, ldwork, dy, lddy, dx, lddx, false, 0.0f, st, &lt);
-    return lt_status_code(e, lt);
+    FP8B_TRY(hip_status(launch_transpose_bf16(transpose_src(wkind), wq, ldwq, ws, ldws, D, C, work, ldwork, st)));
+    Bf16GemmArgs g{};
+    g.P = dy; g.ldp = lddy;
+    g.Q = work; g.ldq = ldwork;
+    g.O = dx; g.ldo = lddx; g.out_f32 = false; g.beta = 0;
+    g.M = N; g.Nn = C; g.K = D;
+    return hip_status(launch_gemm_bf16(g, st));
 }
 
 int fp8_dequant_gemm_wgrad(const uint16_t* dy, int64_t lddy, const uint8_t* xq, int64_t ldxq,
@@ -378,23 +370,27 @@ int fp8_dequant_gemm_wgrad(const uint16_t* dy, int64_t lddy, const uint8_t* xq, 
                            void* dw, int dwt, int64_t lddw, int beta,
                            uint16_t* work, int64_t ldwork, void* stream) {
     if (xkind != FP8B_SCALE_ROWS_1X128 && xkind != FP8B_SCALE_MX_1X32) return FP8B_EINVAL;
-    FP8B_TRY(check_blas_matrix(dy, FP8B_BF16, N, D, lddy));
+    FP8B_TRY(check_input(dy, FP8B_BF16, N, D, lddy));
     FP8B_TRY(check_fp8_operand(xq, ldxq, xs, ldxs, xkind, N, C));
-    FP8B_TRY(check_input(work, FP8B_BF16, N, C, ldwork));
-    if (beta != 0 && beta != 1) return FP8B_EINVAL;
-    if (beta == 1 && dwt != FP8B_F32) return FP8B_EUNSUPPORTED;
-    FP8B_TRY(check_blas_matrix(dw, dwt, D, C, lddw));
+    FP8B_TRY(check_input(work, FP8B_BF16, C + D, N, ldwork));      // X^T [C x N], then dY^T [D x N]
+    FP8B_TRY(check_output(dw, dwt, D, C, lddw, beta));
+    if (lddy > kMaxBf16Ld || ldwork > kMaxBf16Ld) return FP8B_EUNSUPPORTED;
     const hipStream_t st = static_cast<hipStream_t>(stream);
     if (D == 0 || C == 0) return FP8B_OK;
     if (N == 0) {
         if (beta) return FP8B_OK;
-        return hip_status(launch_zero_2d(dw, lddw * (dwt == FP8B_F32 ? 4 : 2), C * (dwt == FP8B_F32 ? 4 : 2), D, st));
+        return hip_status(launch_zero_2d(dw, lddw * esize(dwt), C * esize(dwt), D, st));
     }
-    FP8B_TRY(hip_status(launch_dequant_bf16(xq, ldxq, xs, ldxs, xkind, N, C, work, ldwork, st)));
-    int lt = 0;
-    const hipError_t e = lt_gemm(false, true, C, D, N, work, ldwork, dy, lddy, dw, lddw, dwt == FP8B_F32,
-                                 beta ? 1.0f : 0.0f, st, &lt);
-    return lt_status_code(e, lt);
+    uint16_t* xT = work;
+    uint16_t* gT = work + C * ldwork;
+    FP8B_TRY(hip_status(launch_transpose_bf16(transpose_src(xkind), xq, ldxq, xs, ldxs, N, C, xT, ldwork, st)));
+    FP8B_TRY(hip_status(launch_transpose_bf16(0, dy, lddy, nullptr, 0, N, D, gT, ldwork, st)));
+    Bf16GemmArgs g{};
+    g.P = gT; g.ldp = ldwork;
+    g.Q = xT; g.ldq = ldwork;
+    g.O = dw; g.ldo = lddw; g.out_f32 = dwt == FP8B_F32; g.beta = beta;
+    g.M = D; g.Nn = C; g.K = N;
+    return hip_status(launch_gemm_bf16(g, st));
 }
 
 int fp8b_validate_gemm(int op, const void* a, int64_t lda, const void* sa, int64_t ldsa,
@@ -655,6 +651,15 @@ int fp8_mx_gemm_wgrad(const uint8_t* gqT, int64_t ldgqT, const uint8_t* geT, int
                       void* dw, int dwt, int64_t lddw, int beta,
                       int64_t N, int64_t D, int64_t C, void* stream) {
     return gemm_dense(5, gqT, ldgqT, geT, ldgeT, xqT, ldxqT, xeT, ldxeT, dw, dwt, lddw, beta, N, D, C, stream);
+}
+
+int fp8b_mfma_peak(int kind, int64_t blocks, int64_t iters, uint32_t seed, float* out, double* flops,
+                   void* stream) {
+    if (kind != 0 && kind != 1) return FP8B_EINVAL;
+    if (blocks < 0 || iters < 0 || blocks > 0x7FFFFFFF) return FP8B_ESHAPE;
+    if (blocks > 0 && iters > 0 && out == nullptr) return FP8B_EINVAL;
+    if (flops != nullptr) *flops = (double)blocks * 4.0 * 16.0 * (double)iters * (kind == 0 ? 65536.0 : 16384.0);
+    return hip_status(launch_mfma_peak(kind, blocks, iters, seed, out, static_cast<hipStream_t>(stream)));
 }
 
 int fp8b_e4m3_encode(const float* x, const float* s, int64_t n, uint8_t* out, void* stream) {

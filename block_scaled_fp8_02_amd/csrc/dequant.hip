@@ -1,22 +1,16 @@
-// dequant.hip -- the dequantized-backward mode: bf16 GEMMs on bf16
-// dequantizations of the exact FP8 operands the forward pass produced.
-//
-// The Miles MXFP8/NVFP4 blog offers it as a selectable backward mode: the
-// backward GEMMs run in bf16, their FP8-side operands are the forward's
-// codes dequantized to bf16 (W for DGrad, X for WGrad), dY stays bf16, and
-// no column-wise FP8 copy is needed.  Here:
+// dequant.hip -- bf16 dequantization of FP8 operands, for the
+// dequantized-backward mode (the Miles MXFP8/NVFP4 blog's backward-mode
+// section: the backward GEMMs run in bf16 on bf16 dequantizations of the
+// exact FP8 operands the forward pass produced, W for DGrad and X for WGrad,
+// with dY in bf16 and no column-wise FP8 copy).
 //
 //   k_dequant_bf16   codes + scales -> bf16(fl32(E4M3(q) * s)); the scale
 //                    layouts are the 1x128 row groups, the 128x128 weight
 //                    blocks and the MX 1x32 E8M0 groups
-//   lt_gemm          the plain bf16 GEMM (fp32 accumulation) through
-//                    hipBLASLt, the library GEMM for bf16 operands
+//   k_zero_2d        the output of an empty contraction
+// The GEMMs themselves and the transposing dequantization that feeds them
+// are in bf16gemm.hip.
 #include <hip/hip_runtime.h>
-#include <hipblaslt/hipblaslt.h>
-
-#include <map>
-#include <mutex>
-#include <tuple>
 
 #include "device_common.hpp"
 #include "kernels.hpp"
@@ -102,95 +96,6 @@ hipError_t launch_zero_2d(void* p, int64_t ld_bytes, int64_t row_bytes, int64_t 
     const int64_t cap = 8 * (int64_t)device_cu_count();
     if (blocks > cap) blocks = cap;
     k_zero_2d<<<dim3((unsigned)blocks), 256, 0, st>>>(static_cast<uint8_t*>(p), ld_bytes, row_bytes, rows);
-    return hipGetLastError();
-}
-
-// ---------------------------------------------------------------------
-// hipBLASLt bf16 GEMM, column-major: D[m x n] = op(A)[m x k] op(B)[k x n]
-// (+ beta D).  One handle per device, created on first use; the chosen
-// algorithm is cached per problem (no workspace: only algorithms that need
-// none are considered, so no memory is allocated per call).
-// ---------------------------------------------------------------------
-namespace {
-
-struct LtKey {
-    int dev, ta, tb, out_f32, beta;
-    int64_t m, n, k, lda, ldb, ldd;
-    bool operator<(const LtKey& o) const {
-        return std::tie(dev, ta, tb, out_f32, beta, m, n, k, lda, ldb, ldd) <
-               std::tie(o.dev, o.ta, o.tb, o.out_f32, o.beta, o.m, o.n, o.k, o.lda, o.ldb, o.ldd);
-    }
-};
-
-std::mutex g_lt_mutex;
-hipblasLtHandle_t g_lt_handle[64] = {};
-std::map<LtKey, hipblasLtMatmulAlgo_t> g_lt_algos;
-
-}  // namespace
-
-hipError_t lt_gemm(bool ta, bool tb, int64_t m, int64_t n, int64_t k,
-                   const uint16_t* A, int64_t lda, const uint16_t* B, int64_t ldb,
-                   void* D, int64_t ldd, bool out_f32, float beta, hipStream_t st, int* lt_status) {
-    *lt_status = 0;
-    if (m == 0 || n == 0) return hipSuccess;
-    int dev = 0;
-    hipError_t he = hipGetDevice(&dev);
-    if (he != hipSuccess) return he;
-    if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
-
-    hipblasLtMatmulDesc_t desc = nullptr;
-    hipblasLtMatrixLayout_t la = nullptr, lb = nullptr, ld = nullptr;
-    hipblasStatus_t s = HIPBLAS_STATUS_SUCCESS;
-    const hipblasOperation_t opa = ta ? HIPBLAS_OP_T : HIPBLAS_OP_N, opb = tb ? HIPBLAS_OP_T : HIPBLAS_OP_N;
-    const hipDataType dt = out_f32 ? HIP_R_32F : HIP_R_16BF;
-    hipblasLtMatmulAlgo_t algo;
-    std::lock_guard<std::mutex> lock(g_lt_mutex);
-    if (g_lt_handle[dev] == nullptr) {
-        s = hipblasLtCreate(&g_lt_handle[dev]);
-        if (s != HIPBLAS_STATUS_SUCCESS) { *lt_status = (int)s; g_lt_handle[dev] = nullptr; return hipErrorUnknown; }
-    }
-    hipblasLtHandle_t h = g_lt_handle[dev];
-#define FP8B_LT(call)                                  \
-    do {                                               \
-        s = (call);                                    \
-        if (s != HIPBLAS_STATUS_SUCCESS) goto done;    \
-    } while (0)
-    {
-        FP8B_LT(hipblasLtMatmulDescCreate(&desc, HIPBLAS_COMPUTE_32F, HIP_R_32F));
-        FP8B_LT(hipblasLtMatmulDescSetAttribute(desc, HIPBLASLT_MATMUL_DESC_TRANSA, &opa, sizeof(opa)));
-        FP8B_LT(hipblasLtMatmulDescSetAttribute(desc, HIPBLASLT_MATMUL_DESC_TRANSB, &opb, sizeof(opb)));
-        FP8B_LT(hipblasLtMatrixLayoutCreate(&la, HIP_R_16BF, ta ? k : m, ta ? m : k, lda));
-        FP8B_LT(hipblasLtMatrixLayoutCreate(&lb, HIP_R_16BF, tb ? n : k, tb ? k : n, ldb));
-        FP8B_LT(hipblasLtMatrixLayoutCreate(&ld, dt, m, n, ldd));
-        const LtKey key{dev, (int)ta, (int)tb, (int)out_f32, beta != 0.0f, m, n, k, lda, ldb, ldd};
-        auto it = g_lt_algos.find(key);
-        if (it != g_lt_algos.end()) {
-            algo = it->second;
-        } else {
-            hipblasLtMatmulPreference_t pref = nullptr;
-            FP8B_LT(hipblasLtMatmulPreferenceCreate(&pref));
-            uint64_t wsz = 0;
-            s = hipblasLtMatmulPreferenceSetAttribute(pref, HIPBLASLT_MATMUL_PREF_MAX_WORKSPACE_BYTES, &wsz, sizeof(wsz));
-            hipblasLtMatmulHeuristicResult_t res[1];
-            int found = 0;
-            if (s == HIPBLAS_STATUS_SUCCESS)
-                s = hipblasLtMatmulAlgoGetHeuristic(h, desc, la, lb, ld, ld, pref, 1, res, &found);
-            hipblasLtMatmulPreferenceDestroy(pref);
-            if (s != HIPBLAS_STATUS_SUCCESS) goto done;
-            if (found < 1) { s = HIPBLAS_STATUS_NOT_SUPPORTED; goto done; }
-            algo = res[0].algo;
-            g_lt_algos.emplace(key, algo);
-        }
-        const float alpha = 1.0f;
-        FP8B_LT(hipblasLtMatmul(h, desc, &alpha, A, la, B, lb, &beta, D, ld, D, ld, &algo, nullptr, 0, st));
-    }
-done:
-#undef FP8B_LT
-    if (ld) hipblasLtMatrixLayoutDestroy(ld);
-    if (lb) hipblasLtMatrixLayoutDestroy(lb);
-    if (la) hipblasLtMatrixLayoutDestroy(la);
-    if (desc) hipblasLtMatmulDescDestroy(desc);
-    if (s != HIPBLAS_STATUS_SUCCESS) { *lt_status = (int)s; return hipErrorUnknown; }
     return hipGetLastError();
 }
 

@@ -47,19 +47,39 @@ hipError_t launch_silu_mul_quant(const uint16_t* gate, int64_t ldg, const uint16
                                  int64_t rows, int64_t cols, uint8_t* q, int64_t ldq, float* s, int64_t lds,
                                  uint16_t* a, int64_t lda, hipStream_t st);
 
-// Dequantized-backward mode (dequant.hip): bf16 dequantization of FP8 codes
-// (kind 0: 1x128 row groups, 1: 128x128 blocks, 2: MX 1x32 E8M0) and the
-// plain bf16 GEMM through hipBLASLt (column-major, fp32 accumulation).
+// Dequantized-backward mode.  dequant.hip: bf16 dequantization of FP8 codes
+// (kind 0: 1x128 row groups, 1: 128x128 blocks, 2: MX 1x32 E8M0).
 // Zero a rows x row_bytes region with row stride ld_bytes (a kernel, not a memset).
 hipError_t launch_zero_2d(void* p, int64_t ld_bytes, int64_t row_bytes, int64_t rows, hipStream_t st);
 hipError_t launch_dequant_bf16(const uint8_t* q, int64_t ldq, const void* s, int64_t lds, int kind,
                                int64_t rows, int64_t cols, uint16_t* out, int64_t ldo, hipStream_t st);
-hipError_t lt_gemm(bool ta, bool tb, int64_t m, int64_t n, int64_t k,
-                   const uint16_t* A, int64_t lda, const uint16_t* B, int64_t ldb,
-                   void* D, int64_t ldd, bool out_f32, float beta, hipStream_t st, int* lt_status);
+
+// bf16gemm.hip: O[i][j] (+)= sum_k P[i][k] Q[j][k], P (M x K) and Q (Nn x K)
+// bf16 contiguous along K (row strides ldp, ldq in elements, multiples of 8;
+// elements up to round_up(K, 8) of a row are read, those past K ignored),
+// fp32 accumulation, bf16 (nearest-even) or fp32 output (beta = 1: added to
+// the fp32 output).
+struct Bf16GemmArgs {
+    const uint16_t* P; int64_t ldp;
+    const uint16_t* Q; int64_t ldq;
+    void* O; int64_t ldo; bool out_f32; int beta;
+    int64_t M, Nn, K;
+};
+hipError_t launch_gemm_bf16(const Bf16GemmArgs& a, hipStream_t st);
+// out[c][r] = in[r][c] as bf16 (out row stride ldo, a multiple of 8 >= rows):
+// src 0 bf16 input (row stride ldi, a multiple of 8); 1, 2, 3 FP8 codes
+// (rows padded to 128) dequantized with the scale layouts of kind 0, 1, 2
+// above, bf16(fl32(E4M3(q) * scale)).
+hipError_t launch_transpose_bf16(int src, const void* in, int64_t ldi, const void* s, int64_t lds,
+                                 int64_t rows, int64_t cols, uint16_t* out, int64_t ldo, hipStream_t st);
 
 // Elementwise codec access.
 hipError_t launch_encode(const float* x, const float* s, int64_t n, uint8_t* out, hipStream_t st);
+
+// Matrix-core throughput on random register operands (peak.hip): kind 0 the
+// fp8 16x16x128 MFMA, kind 1 the bf16 16x16x32 MFMA; blocks of 256 threads,
+// 16 * iters MFMAs per wave, one fp32 per wave into out.
+hipError_t launch_mfma_peak(int kind, int64_t blocks, int64_t iters, uint32_t seed, float* out, hipStream_t st);
 
 // Compute units of the current device (cached per device).
 int device_cu_count();

@@ -19,13 +19,10 @@
  * Conventions shared by every entry point
  * ---------------------------------------
  * - All pointers are DEVICE pointers (except where stated) owned by the
- *   caller.  The library's own kernels allocate and free no device memory,
- *   and it keeps no state between calls apart from lazily loaded code
- *   objects, for the two dequantized-backward GEMMs one hipBLASLt handle
- *   per device (created on first use; hipBLASLt may allocate inside it) and
- *   a cache of the algorithms it chose per problem shape, and for
- *   fp8_gemm_dgrad_split_noalloc the device address of its scratch array on
- *   each device.
+ *   caller.  The library allocates and frees no device memory and calls no
+ *   other GPU library; it keeps no state between calls apart from lazily
+ *   loaded code objects and, for fp8_gemm_dgrad_split_noalloc, the device
+ *   address of its scratch array on each device.
  * - Every call is asynchronous on `stream` (a hipStream_t passed as void*;
  *   NULL is the default stream).  Buffers must stay valid until the stream
  *   reaches the operation.
@@ -88,9 +85,7 @@ FP8B_API int fp8b_abi_version(void);
 /* Static, human-readable text for a status code. */
 FP8B_API const char* fp8b_status_string(int status);
 
-/* HIP error code of the last FP8B_EHIP returned on the calling thread (for
- * the dequantized-backward GEMMs, a failing hipBLASLt status is returned
- * negated). */
+/* HIP error code of the last FP8B_EHIP returned on the calling thread. */
 FP8B_API int fp8b_last_hip_error(void);
 
 /* ------------------------------------------------------------------ */
@@ -220,22 +215,32 @@ FP8B_API int fp8_requantize_transposed_grouped(const uint8_t* q, int64_t ldq, co
 FP8B_API int fp8_dequantize_bf16(const uint8_t* q, int64_t ldq, const void* s, int64_t lds, int kind,
                         int64_t rows, int64_t cols, uint16_t* out, int64_t ldo, void* stream);
 
+/* Both GEMMs below run on the library's bf16 MFMA kernel (gfx950
+ * v_mfma_f32_16x16x32_bf16, fp32 accumulation, bf16 output rounded to
+ * nearest-even), which reads both operands contiguous along the contraction
+ * axis.  The caller-owned bf16 workspace `work` receives those operand
+ * copies (each row a contiguous run of the contraction axis, ldwork a
+ * multiple of 8 elements, 16-byte aligned), written by the call before its
+ * GEMM: the dequantized FP8 operand transposed, and for WGrad dY transposed.
+ * bf16 inputs and outputs follow the 16-byte rules of the FP8 kernels
+ * (pointer and ld * element size multiples of 16); rows are read in whole
+ * 16-byte chunks up to round_up(K, 8) elements (K the contraction length),
+ * and the elements past K are ignored.  Row strides of dy and work are at
+ * most 2^23 elements (FP8B_EUNSUPPORTED beyond). */
+
 /* dX [N x C] bf16 = dY [N x D] bf16 * W^ [D x C], W^ the dequantized forward
- * weight codes (kind FP8B_SCALE_BLOCKS_128X128 or FP8B_SCALE_MX_1X32, K = C).
- * work: caller-owned D x ldwork bf16 buffer that receives W^.  The GEMM is
- * hipBLASLt's bf16 GEMM with fp32 accumulation (no workspace); dy and dx
- * need only element alignment and any leading dimension (hipBLASLt reads and
- * writes them), work the 16-byte rules of the kernels; the first call
- * on a device creates a hipBLASLt handle there, and the algorithm is chosen
- * once per problem shape and cached. */
+ * weight codes (kind FP8B_SCALE_BLOCKS_128X128 or FP8B_SCALE_MX_1X32, codes
+ * D x ldwq, K = C).  work: C x ldwork bf16, ldwork >= D; receives W^T. */
 FP8B_API int fp8_dequant_gemm_dgrad(const uint16_t* dy, int64_t lddy, const uint8_t* wq, int64_t ldwq,
                            const void* ws, int64_t ldws, int wkind, int64_t N, int64_t D, int64_t C,
                            uint16_t* dx, int64_t lddx, uint16_t* work, int64_t ldwork, void* stream);
 
 /* dW [D x C] = dY^T X^ (+ dW when beta = 1; dwt FP8B_F32 required then), X^
  * the dequantized forward activation codes (kind FP8B_SCALE_ROWS_1X128 or
- * FP8B_SCALE_MX_1X32, rows N, K = C).  work: caller-owned N x ldwork bf16
- * buffer that receives X^.  GEMM as above. */
+ * FP8B_SCALE_MX_1X32, rows N, K = C).  work: (C + D) x ldwork bf16, ldwork
+ * >= N; rows [0, C) receive X^T and rows [C, C + D) receive dY^T (columns
+ * [N, round_up(N, 8)) are written zero).  An empty contraction (N = 0) writes
+ * zeros (beta = 0) or leaves dW unchanged (beta = 1). */
 FP8B_API int fp8_dequant_gemm_wgrad(const uint16_t* dy, int64_t lddy, const uint8_t* xq, int64_t ldxq,
                            const void* xs, int64_t ldxs, int xkind, int64_t N, int64_t D, int64_t C,
                            void* dw, int dwt, int64_t lddw, int beta,
@@ -438,6 +443,26 @@ FP8B_API int fp8_mx_gemm_wgrad(const uint8_t* gqT, int64_t ldgqT, const uint8_t*
  * fp32 quotient, nearest-even E4M3, saturating; s[i] == 0 gives the signed
  * zero of x[i].  If s is NULL the divisor is 1 (plain encode of x). */
 FP8B_API int fp8b_e4m3_encode(const float* x, const float* s, int64_t n, uint8_t* out, void* stream);
+
+/* ------------------------------------------------------------------ */
+/* Measurement aid (not part of the FP8 path)                          */
+/* ------------------------------------------------------------------ */
+
+/* Matrix-core throughput on random operands: the ceiling the GEMMs are
+ * compared with beside the published peak (the chip is power limited, and
+ * its clock under load depends on the data the matrix cores multiply).
+ * kind 0: v_mfma_f32_16x16x128_f8f6f4 on E4M3 codes (NaN codes excluded);
+ * kind 1: v_mfma_f32_16x16x32_bf16 on bf16 values of magnitude in [2^-8, 2^8).
+ * Launches `blocks` blocks of 4 waves; each wave keeps four random A and
+ * four random B fragments and four accumulators in registers (bytes from a
+ * SplitMix64 hash of seed, wave, lane and register) and issues 16 MFMAs per
+ * iteration, `iters` iterations, with no memory traffic in the loop.
+ * out: DEVICE fp32[4 * blocks], one value per wave (keeps the work live).
+ * flops (host, nullable): receives the floating-point operations launched,
+ * blocks * 4 * 16 * iters * (65536 for kind 0, 16384 for kind 1).
+ * Errors: FP8B_EINVAL (bad kind, NULL out), FP8B_ESHAPE, FP8B_EHIP. */
+FP8B_API int fp8b_mfma_peak(int kind, int64_t blocks, int64_t iters, uint32_t seed, float* out, double* flops,
+                   void* stream);
 
 /* Host-only argument check of the GEMM entry points: runs exactly the
  * validation the launch would run and returns its status, launching

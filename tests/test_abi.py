@@ -34,7 +34,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_abi_version_and_status_strings():
-    assert fb.fp8b_abi_version() == 1
+    assert fb.fp8b_abi_version() == 2
     assert fb.fp8b_status_string(0) == "ok"
     assert "shape" in fb.fp8b_status_string(2)
 
@@ -168,6 +168,13 @@ def test_dequantized_backward_rejects_bad_arguments_on_host():
     assert L.fp8_dequant_gemm_wgrad(Y, 128, Q, 256, S, 2, 1, 8, 128, 256, O, 1, 256, 0, W, 256, None) == 1
     assert L.fp8_dequant_gemm_wgrad(Y, 128, Q, 256, S, 2, 0, 8, 128, 256, O, 1, 256, 1, W, 256, None) == 4
     assert L.fp8_dequant_gemm_dgrad(Y, 128, Q, 256, S, 2, 1, 8, 128, 256, O, 256, W, 100, None) == 2
+    # the bf16 GEMM reads 16-byte chunks: dy and dx follow the 16-byte rules
+    assert L.fp8_dequant_gemm_dgrad(Y + 2, 128, Q, 256, S, 2, 1, 8, 128, 256, O, 256, W, 128, None) == 3
+    assert L.fp8_dequant_gemm_dgrad(Y, 132, Q, 256, S, 2, 1, 8, 128, 256, O, 256, W, 128, None) == 3
+    assert L.fp8_dequant_gemm_dgrad(Y, 128, Q, 256, S, 2, 1, 8, 128, 256, O + 8, 256, W, 128, None) == 3
+    # WGrad's workspace rows hold the token axis (ldwork >= N); row strides up to 2^23
+    assert L.fp8_dequant_gemm_wgrad(Y, 128, Q, 256, S, 2, 0, 16, 128, 256, O, 1, 256, 0, W, 8, None) == 2
+    assert L.fp8_dequant_gemm_dgrad(Y, (1 << 23) + 8, Q, 256, S, 2, 1, 8, 128, 256, O, 256, W, 128, None) == 4
 
 
 def test_dgrad_split_workspace_and_host_checks():

@@ -1,8 +1,9 @@
 """GPU parity of the dequantized-backward mode: the bf16 dequantization of
 FP8 operands bit for bit against the oracle (1x128 row groups, 128x128
-blocks, MX 1x32), and the bf16 DGrad/WGrad GEMMs on those operands
-against the oracle's binary64 product of the same bf16 values (2e-3 of the
-row norm: bf16 output rounding plus fp32 accumulation)."""
+blocks, MX 1x32), the transposed operand copies the bf16 GEMM reads (bit
+for bit), and the bf16 DGrad/WGrad GEMMs on those operands against the
+oracle's binary64 product of the same bf16 values (2e-3 of the row norm:
+bf16 output rounding plus fp32 accumulation)."""
 import numpy as np
 import pytest
 import torch
@@ -61,7 +62,7 @@ def test_dequant_backward_gemms(N, D, C):
     dY = oracle.bf16_rne((rng.standard_normal((N, D)) * 1e-3).astype(np.float32))
     xq, xs = oracle.quant_1x128(X)
     wq, ws, _ = oracle.quant_128x128(W, with_transpose=False)
-    dYd = dev(dY)
+    dYd = dev_strided(dY)
     dx = host(fb.fp8_dequant_gemm_dgrad(dYd, dev(wq), dev(ws), fb.FP8B_SCALE_BLOCKS_128X128, N, D, C))
     want_dx = oracle.bf16_matmul(dY, oracle.dequant_bf16_128x128(wq, ws, D, C))
     e = oracle.rel_row_error(dx, want_dx)
@@ -90,10 +91,79 @@ def test_dequant_backward_gemms(N, D, C):
     assert e <= TOL
 
 
-def test_dequant_backward_training_shape_sampled_rows():
+def tile_rows(n: int, seed: int, tile: int = 256) -> np.ndarray:
+    """One seeded row from every 256-row output tile, plus the first and last
+    row: every 256 x 256 tile of the output has a checked row."""
+    rng = np.random.default_rng(seed)
+    r = [t + int(rng.integers(0, min(tile, n - t))) for t in range(0, n, tile)] + [0, n - 1]
+    return np.unique(np.array(r, dtype=np.int64))
+
+
+@pytest.mark.parametrize("N,D,C", [(200, 300, 260), (3, 130, 300), (256, 384, 512)])
+def test_transposed_operand_copies(N, D, C):
+    """The workspaces the bf16 GEMMs read, bit for bit: W^ transposed (DGrad),
+    X^ transposed then dY transposed (WGrad), with columns [K, round_up(K,
+    8)) of each workspace row written zero."""
+    banner(f"transposed operand copies N={N} D={D} C={C}")
+    rng = np.random.default_rng(N + 3 * D + C)
+    X = oracle.bf16_rne(rand_x(rng, (N, C), 4.0))
+    W = oracle.bf16_rne((rng.standard_normal((D, C)) * 0.02).astype(np.float32))
+    dY = oracle.bf16_rne((rng.standard_normal((N, D)) * 1e-3).astype(np.float32))
+    dYd = dev_strided(dY)
+    bq, bs, _ = oracle.quant_128x128(W, with_transpose=False)
+    mq, me = oracle.mx_quant_rows(W)
+    for wq, ws, kind, deq in ((bq, bs, fb.FP8B_SCALE_BLOCKS_128X128, oracle.dequant_bf16_128x128(bq, bs, D, C)),
+                              (mq, me, fb.FP8B_SCALE_MX_1X32, oracle.dequant_bf16_mx(mq, me, C))):
+        work = fb._new_out(C, D, torch.bfloat16, dYd.device).fill_(float("nan"))
+        fb.fp8_dequant_gemm_dgrad(dYd, dev(wq), dev(ws), kind, N, D, C, work=work)
+        assert_bytes_equal(bits_of(work), np.ascontiguousarray(deq.T), f"W^T kind {kind}")
+    aq, as_ = oracle.quant_1x128(X)
+    nq, ne = oracle.mx_quant_rows(X)
+    for xq, xs, kind, deq in ((aq, as_, fb.FP8B_SCALE_ROWS_1X128, oracle.dequant_bf16_rows(aq, as_, C)),
+                              (nq, ne, fb.FP8B_SCALE_MX_1X32, oracle.dequant_bf16_mx(nq, ne, C))):
+        work = fb._new_out(C + D, N, torch.bfloat16, dYd.device).fill_(float("nan"))
+        fb.fp8_dequant_gemm_wgrad(dYd, dev(xq), dev(xs), kind, N, D, C, work=work)
+        full = work.as_strided((C + D, (N + 7) // 8 * 8), work.stride())
+        got = bits_of(full)
+        assert_bytes_equal(got[:C, :N], np.ascontiguousarray(deq.T), f"X^T kind {kind}")
+        assert_bytes_equal(got[C:, :N], np.ascontiguousarray(dY.T), "dY^T")
+        assert np.all(got[:, N:] == 0), "pad columns of the workspace rows"
+
+
+@pytest.mark.parametrize("N,D,C", [(37, 130, 200), (64, 1000, 136), (300, 77, 520)])
+def test_dequant_backward_ignores_row_padding(N, D, C):
+    """Contractions that end inside a 16-byte chunk and inside a 64-wide K
+    block, with NaN in every padding element of dY's rows: the padding is
+    read with the last chunk and must contribute nothing."""
+    banner(f"dequantized backward, NaN row padding, N={N} D={D} C={C}")
+    rng = np.random.default_rng(N * 11 + D + C)
+    X = oracle.bf16_rne(rng.standard_normal((N, C)).astype(np.float32))
+    W = oracle.bf16_rne((rng.standard_normal((D, C)) * 0.02).astype(np.float32))
+    dY = oracle.bf16_rne((rng.standard_normal((N, D)) * 1e-3).astype(np.float32))
+    ld = (D + 7) // 8 * 8 + 8
+    buf = torch.full((N, ld), float("nan"), dtype=torch.bfloat16, device="cuda")
+    buf[:, :D] = dev(dY)
+    dYd = buf[:, :D]
+    xq, xs = oracle.quant_1x128(X)
+    wq, ws, _ = oracle.quant_128x128(W, with_transpose=False)
+    dx = host(fb.fp8_dequant_gemm_dgrad(dYd, dev(wq), dev(ws), fb.FP8B_SCALE_BLOCKS_128X128, N, D, C))
+    assert np.all(np.isfinite(dx))
+    e = oracle.rel_row_error(dx, oracle.bf16_matmul(dY, oracle.dequant_bf16_128x128(wq, ws, D, C)))
+    banner(f"  dgrad {e:.3e}")
+    assert e <= TOL
+    dw = host(fb.fp8_dequant_gemm_wgrad(dYd, dev(xq), dev(xs), fb.FP8B_SCALE_ROWS_1X128, N, D, C,
+                                        out_dtype=torch.float32))
+    assert np.all(np.isfinite(dw))
+    e = oracle.rel_row_error(dw, oracle.bf16_matmul(np.ascontiguousarray(dY.T), oracle.dequant_bf16_rows(xq, xs, C)))
+    banner(f"  wgrad {e:.3e}")
+    assert e <= 1e-5
+
+
+def test_dequant_backward_training_shape_every_tile():
     """The training layer's backward in the dequantized mode, at full size:
     DGrad on the forward's 128x128 W codes, WGrad on the forward's 1x128 X
-    codes (from the GPU quantizers, as a layer runs them), sampled rows."""
+    codes (from the GPU quantizers, as a layer runs them), checked on one
+    row of every 256-row output tile (every output tile has a checked row)."""
     w = wl.train(0)
     N, C, D = w["N"], w["C"], w["D"]
     banner("dequantized backward at the training shape")
@@ -102,9 +172,8 @@ def test_dequant_backward_training_shape_sampled_rows():
     dYd = dev(w["dY"])
     dx = host(fb.fp8_dequant_gemm_dgrad(dYd, wq, ws, fb.FP8B_SCALE_BLOCKS_128X128, N, D, C))
     dw = host(fb.fp8_dequant_gemm_wgrad(dYd, xq, xs, fb.FP8B_SCALE_ROWS_1X128, N, D, C))
-    rng = np.random.default_rng(72)
-    rows = np.sort(rng.choice(N, 16, replace=False))
-    drows = np.sort(rng.choice(D, 16, replace=False))
+    rows = tile_rows(N, 72)
+    drows = tile_rows(D, 74)
     owq, ows, _ = oracle.quant_128x128(w["W"], with_transpose=False)
     e = oracle.rel_row_error(dx[rows], oracle.bf16_matmul(w["dY"][rows], oracle.dequant_bf16_128x128(owq, ows, D, C)))
     banner(f"  dgrad sampled rows {e:.3e}")
@@ -155,7 +224,7 @@ def test_dequant_backward_empty_contraction_writes_zeros():
     (with a fill kernel, not a memset) and leaves dW as it is with beta = 1."""
     N, D, C = 130, 200, 300
     banner("dequantized backward with an empty contraction")
-    dx = torch.full((N, C), 7.0, dtype=torch.bfloat16, device="cuda")
+    dx = fb._new_out(N, C, torch.bfloat16, torch.device("cuda")).fill_(7.0)
     fb.fp8_dequant_gemm_dgrad(torch.empty((N, 0), dtype=torch.bfloat16, device="cuda"),
                               torch.empty((0, 384), dtype=torch.uint8, device="cuda"),
                               torch.empty((0, 3), dtype=torch.float32, device="cuda"),
@@ -164,9 +233,9 @@ def test_dequant_backward_empty_contraction_writes_zeros():
     dy0 = torch.empty((0, D), dtype=torch.bfloat16, device="cuda")
     xq0 = torch.empty((0, 384), dtype=torch.uint8, device="cuda")
     xs0 = torch.empty((0, 3), dtype=torch.float32, device="cuda")
-    dw = torch.full((D, C), 7.0, dtype=torch.bfloat16, device="cuda")
+    dw = fb._new_out(D, C, torch.bfloat16, torch.device("cuda")).fill_(7.0)
     fb.fp8_dequant_gemm_wgrad(dy0, xq0, xs0, fb.FP8B_SCALE_ROWS_1X128, 0, D, C, dw=dw)
     assert torch.all(dw == 0)
-    dw32 = torch.full((D, C), 7.0, dtype=torch.float32, device="cuda")
+    dw32 = fb._new_out(D, C, torch.float32, torch.device("cuda")).fill_(7.0)
     fb.fp8_dequant_gemm_wgrad(dy0, xq0, xs0, fb.FP8B_SCALE_ROWS_1X128, 0, D, C, dw=dw32, beta=1)
     assert torch.all(dw32 == 7.0)
