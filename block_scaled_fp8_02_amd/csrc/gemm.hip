@@ -347,7 +347,9 @@ __global__ __launch_bounds__(64 * NW, 1) void k_gemm(GemmArgs g) {
         }
         __syncthreads();
         const bool full_cols = jhi - j0 == BJ && (g.ldo % 8) == 0;
-        for (int q = tid; q < rh * PPR; q += NT) {
+        int t0 = tid;                                                // opaque, as ln above
+        asm volatile("" : "+v"(t0));
+        for (int q = t0; q < rh * PPR; q += NT) {
             const int il = q / PPR, pp = q % PPR;
             const int64_t i = i0 + r0 + il;
             if (i < ihi) {
@@ -531,6 +533,8 @@ __global__ __launch_bounds__(64 * NW, 1) void k_gemm(GemmArgs g) {
         } else {
             // Software pipeline: step a issues the MFMAs of Q sub-tile a and
             // the promotion FMAs of sub-tile a-1, whose results are ready.
+            // Per-row Q scales (WGrad): step a reads sub-tile a's four scale
+            // words, used at step a + 1, so two such vectors are live at once.
             v4f prev[TI];
             uint4 sqa_prev = sqa;
 #pragma unroll
@@ -540,10 +544,9 @@ __global__ __launch_bounds__(64 * NW, 1) void k_gemm(GemmArgs g) {
                                   (a + 1) * DMA_PER_STEP < NCH ? (a + 1) * DMA_PER_STEP : NCH);
                 v8i af_n = af;
                 uint4 sqa_n = sqa;
-                if (a + 1 < TJ) {
-                    const int qr = qrow_l + (a + 1) * 16;
-                    af_n = lds_frag(base, qfo, (a + 1) * 16 * 128);
-                    if constexpr (SM == SCALE_Q_ROW) sqa_n = *reinterpret_cast<const uint4*>(&sc[qr + 4 * (lane >> 4)]);
+                if (a + 1 < TJ) af_n = lds_frag(base, qfo, (a + 1) * 16 * 128);
+                if constexpr (SM == SCALE_Q_ROW) {
+                    if (a < TJ) sqa_n = *reinterpret_cast<const uint4*>(&sc[qrow_l + a * 16 + 4 * (lane >> 4)]);
                 }
                 v4f cur[TI];
                 if (a < TJ) {
@@ -571,9 +574,8 @@ __global__ __launch_bounds__(64 * NW, 1) void k_gemm(GemmArgs g) {
 #pragma unroll
                     for (int b = 0; b < TI; ++b) prev[b] = cur[b];
                 }
-                sqa_prev = sqa;
+                if constexpr (SM == SCALE_Q_ROW) sqa_prev = sqa_n;  // sub-tile a's scales, used at step a + 1
                 af = af_n;
-                sqa = sqa_n;
                 __builtin_amdgcn_sched_barrier(0);
             }
         }
@@ -666,12 +668,17 @@ static hipError_t launch_sm(const GemmArgs& a, hipStream_t st) {
         if ((a.Nn + 31) / 32 >= 512) return launch_cfg<64, 32, 4, 1, 2, SM, 4, GROUP_NONE>(a, st);
         return launch_cfg<64, 16, 2, 1, 2, SM, 8, GROUP_NONE>(a, st);
     }
-    switch (a.group_mode) {                                   // 8 waves of 64 x 128
-        case GROUP_NONE: return launch_cfg<256, 256, 4, 8, 8, SM, 2, GROUP_NONE>(a, st);
-        case GROUP_ROWS: return launch_cfg<256, 256, 4, 8, 8, SM, 2, GROUP_ROWS>(a, st);
-        case GROUP_K: return launch_cfg<256, 256, 4, 8, 8, SM, 2, GROUP_K>(a, st);
-        default: return hipErrorInvalidValue;
+    // 8 waves of 64 x 128.  Only the pairings the entry points use are
+    // instantiated: row-grouped (MoE FProp, DGrad) with 128x128 weight
+    // scales, K-grouped (MoE WGrad) with per-row scales on both sides.
+    if (a.group_mode == GROUP_NONE) return launch_cfg<256, 256, 4, 8, 8, SM, 2, GROUP_NONE>(a, st);
+    if constexpr (SM == SCALE_Q_BLOCK) {
+        if (a.group_mode == GROUP_ROWS) return launch_cfg<256, 256, 4, 8, 8, SM, 2, GROUP_ROWS>(a, st);
     }
+    if constexpr (SM == SCALE_Q_ROW) {
+        if (a.group_mode == GROUP_K) return launch_cfg<256, 256, 4, 8, 8, SM, 2, GROUP_K>(a, st);
+    }
+    return hipErrorInvalidValue;
 }
 
 // Sum of the K ranges' fp32 partial outputs, ascending in the range index:
