@@ -59,6 +59,9 @@ def parse():
     ap.add_argument("--traffic", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="no GPU work: turn two rocprofv3 --pmc counter_collection.csv files "
                          "(FETCH_SIZE, WRITE_SIZE) of this benchmark into profiles/traffic_gemm_train.json")
+    ap.add_argument("--counters", nargs=2, metavar=("SQ1_CSV", "SQ2_CSV"),
+                    help="no GPU work: turn the two rocprofv3 --pmc SQ counter passes of this benchmark "
+                         "(SQ_PASS1, SQ_PASS2) into profiles/counters_train_layer.md")
     return ap.parse_args()
 
 
@@ -116,7 +119,8 @@ def traffic_summary(fetch_csv, write_csv):
             e[1] += float(r["Counter_Value"]) * 1024.0
         return [per[d] for d in sorted(per)]
 
-    out = {"src_sha": src_sha("gemm.hip", "device_common.hpp"), "src_sha_quant": src_sha("quant.hip", "device_common.hpp"),
+    out = {"src_sha": src_sha("gemm.hip", "gemm_common.hpp", "device_common.hpp"),
+           "src_sha_quant": src_sha("quant.hip", "device_common.hpp"),
            "copy_bytes": CALIB_BYTES, "kernels": {}}
     for counter, path, key in (("FETCH_SIZE", fetch_csv, "fetch"), ("WRITE_SIZE", write_csv, "write")):
         rows = load(path, counter)
@@ -141,10 +145,96 @@ def traffic_summary(fetch_csv, write_csv):
     print(json.dumps(out, indent=1))
 
 
+# The two SQ counter passes summarised by --counters (at most 8 SQ and 2
+# GRBM counters per pass).
+SQ_PASS1 = ["SQ_WAVES", "SQ_BUSY_CYCLES", "SQ_WAVE_CYCLES", "SQ_WAIT_ANY", "SQ_VALU_MFMA_BUSY_CYCLES",
+            "SQ_INSTS_MFMA", "SQ_ACTIVE_INST_VALU", "SQ_INSTS_LDS", "GRBM_GUI_ACTIVE"]
+SQ_PASS2 = ["SQ_WAIT_INST_ANY", "SQ_ACTIVE_INST_LDS", "SQ_ACTIVE_INST_ANY", "SQ_LDS_BANK_CONFLICT",
+            "SQ_INSTS_VALU", "SQ_ACTIVE_INST_MISC", "SQ_INST_LEVEL_LDS", "SQ_CYCLES"]
+
+
+def counters_summary(sq1_csv, sq2_csv):
+    """Per-kernel SQ counter figures of the training-layer step from two
+    --pmc passes (values summed over a dispatch's instances; medians over the
+    step's launches), written to profiles/counters_train_layer.md with the
+    hashes of the kernel sources they were taken on."""
+    import csv
+
+    def load(path):
+        per = {}
+        for r in csv.DictReader(open(path)):
+            d = int(r["Dispatch_Id"])
+            e = per.setdefault(d, {"name": r["Kernel_Name"], "t": (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) * 1e-9})
+            e[r["Counter_Name"]] = e.get(r["Counter_Name"], 0.0) + float(r["Counter_Value"])
+        return [per[d] for d in sorted(per) if "k_quant" in per[d]["name"] or "k_gemm" in per[d]["name"]]
+
+    a, b = load(sq1_csv), load(sq2_csv)
+    if len(a) != len(b) or len(a) % len(KERNEL_ORDER):
+        raise SystemExit(f"counter passes disagree: {len(a)} and {len(b)} library dispatches")
+    rows = []
+    for k, step in enumerate(KERNEL_ORDER):
+        ds = [{**a[i], **{c: v for c, v in b[i].items() if c not in ("name", "t")}}
+              for i in range(k, len(a), len(KERNEL_ORDER))]
+        med = lambda f: float(np.median([f(d) for d in ds]))
+        t = med(lambda d: d["t"])
+        clock = med(lambda d: d["GRBM_GUI_ACTIVE"] / 8 / d["t"])
+        ent = {"step": step, "kernel": ds[0]["name"].split("(")[0].replace("void ", ""), "us": t * 1e6,
+               "ghz": clock / 1e9}
+        if med(lambda d: d["SQ_INSTS_MFMA"]) > 0:
+            ent["mfma_busy"] = med(lambda d: d["SQ_VALU_MFMA_BUSY_CYCLES"] / (1024 * d["t"] * d["GRBM_GUI_ACTIVE"] / 8 / d["t"]))
+            ent["busy_per_mfma"] = med(lambda d: d["SQ_VALU_MFMA_BUSY_CYCLES"] / d["SQ_INSTS_MFMA"])
+            ent["valu_per_mfma"] = med(lambda d: d["SQ_INSTS_VALU"] / d["SQ_INSTS_MFMA"])
+        for key, c in (("wait", "SQ_WAIT_ANY"), ("issue_wait", "SQ_WAIT_INST_ANY"), ("active", "SQ_ACTIVE_INST_ANY"),
+                       ("lds_active", "SQ_ACTIVE_INST_LDS")):
+            ent[key] = med(lambda d: d[c] / d["SQ_WAVE_CYCLES"])
+        ent["lds_bank_conflict_per_lds"] = med(lambda d: d["SQ_LDS_BANK_CONFLICT"] / max(d["SQ_INSTS_LDS"], 1.0))
+        rows.append(ent)
+    pct = lambda v: f"{100 * v:.0f}%"
+    lines = [
+        "# SQ counters: training-step linear layer GEMMs and tile quantizers (X 8192x12288, W 4096x12288, dY 8192x4096)",
+        "",
+        "Commands (from the repository root, on one MI355X; two counter passes over the same launches):",
+        "",
+        "```",
+        "timeout -s KILL 120 rocprofv3 --pmc " + " ".join(SQ_PASS1) + " --output-format csv -d $PWD/gpurun_out/gsq1 -o b "
+        "-- python3 bench.py --steps 2 --warmup 1 --no-cpu-baseline --no-other",
+        "timeout -s KILL 120 rocprofv3 --pmc " + " ".join(SQ_PASS2) + " --output-format csv -d $PWD/gpurun_out/gsq2 -o b "
+        "-- python3 bench.py --steps 2 --warmup 1 --no-cpu-baseline --no-other",
+        "python3 bench.py --counters gpurun_out/gsq1/b_counter_collection.csv gpurun_out/gsq2/b_counter_collection.csv",
+        "```",
+        "",
+        f"Kernel sources hashed as gemm {src_sha('gemm.hip', 'gemm_common.hpp', 'device_common.hpp')}, "
+        f"quant {src_sha('quant.hip', 'device_common.hpp')}.",
+        "",
+        "Derived per kernel (median over the step's launches; the counter runs serialize launches, so durations are",
+        "those of the profiled runs): clock = GRBM_GUI_ACTIVE / 8 XCDs / duration; MFMA busy = SQ_VALU_MFMA_BUSY_CYCLES /",
+        "(1024 SIMDs x cycles); VALU per MFMA = SQ_INSTS_VALU / SQ_INSTS_MFMA (the MFMAs included); wait, issue-wait,",
+        "active and LDS-active = SQ_WAIT_ANY, SQ_WAIT_INST_ANY, SQ_ACTIVE_INST_ANY, SQ_ACTIVE_INST_LDS over SQ_WAVE_CYCLES.",
+        "",
+        "| Step | Kernel | Duration (us) | Clock (GHz) | MFMA busy | Busy cycles per MFMA | VALU per MFMA | Wait | Issue-wait | Active | LDS active | Bank conflicts per LDS instr. |",
+        "|---|---|---|---|---|---|---|---|---|---|---|---|",
+    ]
+    for e in rows:
+        if "mfma_busy" in e:
+            mf = f"{pct(e['mfma_busy'])} | {e['busy_per_mfma']:.1f} | {e['valu_per_mfma']:.2f}"
+        else:
+            mf = "- | - | -"
+        lines.append(f"| {e['step']} | `{e['kernel']}` | {e['us']:.1f} | {e['ghz']:.2f} | {mf} | {pct(e['wait'])} | "
+                     f"{pct(e['issue_wait'])} | {pct(e['active'])} | {pct(e['lds_active'])} | "
+                     f"{e['lds_bank_conflict_per_lds']:.2f} |")
+    path = os.path.join(ROOT, "profiles", "counters_train_layer.md")
+    with open(path, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
 def main():
     args = parse()
     if args.traffic:
         traffic_summary(*args.traffic)
+        return
+    if args.counters:
+        counters_summary(*args.counters)
         return
     if args.gpus != 1:
         print(f"bench.py times one GPU's share of the work; --gpus {args.gpus} is not supported "
@@ -258,7 +348,7 @@ def main():
     tfile = os.path.join(ROOT, "profiles", "traffic_gemm_train.json")
     if os.path.exists(tfile):
         tj = json.load(open(tfile))
-        fresh = {"gemm": tj.get("src_sha") == src_sha("gemm.hip", "device_common.hpp"),
+        fresh = {"gemm": tj.get("src_sha") == src_sha("gemm.hip", "gemm_common.hpp", "device_common.hpp"),
                  "quant": tj.get("src_sha_quant") == src_sha("quant.hip", "device_common.hpp")}
         for n, e in tj.get("kernels", {}).items():
             if n in kernels and fresh["quant" if n.startswith("quant") else "gemm"]:
@@ -333,8 +423,12 @@ def main():
     ceil["mfma_random_operands"] = mfma_peaks(torch, fb, dev)
     pk8 = ceil["mfma_random_operands"]["fp8_16x16x128"]["tflops"]
     pk16 = ceil["mfma_random_operands"]["bf16_16x16x32"]["tflops"]
+    fmt = {"fprop": "fp8_with_block_scale_promotion", "dgrad": "fp8_with_block_scale_promotion",
+           "wgrad": "fp8_with_row_scale_promotion"}
     for n in ("fprop", "dgrad", "wgrad"):
         kernels[n]["frac_measured_fp8_mfma"] = round(kernels[n]["tflops"] / pk8, 4)
+        kernels[n]["frac_measured_format_ceiling"] = round(
+            kernels[n]["tflops"] / ceil["mfma_random_operands"][fmt[n]]["tflops"], 4)
     roofline["frac_measured_peak"] = round(roofline["achieved"] / pk8, 4)
     roofline["measured_peak"] = pk8
     for n, e in bf.items():
@@ -758,12 +852,18 @@ def cpu_baseline(w, budget_s: float):
 def mfma_peaks(torch, fb, dev):
     """Matrix-core throughput on random operands held in registers (the
     library's measurement kernel fp8b_mfma_peak): fp8 16x16x128 and bf16
-    16x16x32 MFMAs on every compute unit with 2 and 4 waves per SIMD; the
-    faster setting is the measured ceiling.  Median of REPS launches."""
+    16x16x32 MFMAs on every compute unit with 2 and 4 waves per SIMD, and the
+    fp8 loop with the FP32-scale recipe's per-block promotion (one FMA per
+    result for the 1x128 x 128x128 GEMMs; a multiply and an FMA per result
+    for the token-axis WGrad): the ceiling the format itself leaves on this
+    chip.  The faster setting is the measured ceiling.  Median of REPS
+    launches."""
     cus = torch.cuda.get_device_properties(dev).multi_processor_count
     out = {}
     for kind, name, iters, spec in ((0, "fp8_16x16x128", 2000, PEAK_FP8_TFLOPS),
-                                    (1, "bf16_16x16x32", 4000, PEAK_BF16_TFLOPS)):
+                                    (1, "bf16_16x16x32", 4000, PEAK_BF16_TFLOPS),
+                                    (2, "fp8_with_block_scale_promotion", 2000, PEAK_FP8_TFLOPS),
+                                    (3, "fp8_with_row_scale_promotion", 2000, PEAK_FP8_TFLOPS)):
         runs = {}
         for wps in (2, 4):
             blocks = cus * wps                      # a block is one wave per SIMD of a CU

@@ -655,10 +655,10 @@ int fp8_mx_gemm_wgrad(const uint8_t* gqT, int64_t ldgqT, const uint8_t* geT, int
 
 int fp8b_mfma_peak(int kind, int64_t blocks, int64_t iters, uint32_t seed, float* out, double* flops,
                    void* stream) {
-    if (kind != 0 && kind != 1) return FP8B_EINVAL;
+    if (kind < 0 || kind > 3) return FP8B_EINVAL;
     if (blocks < 0 || iters < 0 || blocks > 0x7FFFFFFF) return FP8B_ESHAPE;
     if (blocks > 0 && iters > 0 && out == nullptr) return FP8B_EINVAL;
-    if (flops != nullptr) *flops = (double)blocks * 4.0 * 16.0 * (double)iters * (kind == 0 ? 65536.0 : 16384.0);
+    if (flops != nullptr) *flops = (double)blocks * 4.0 * 16.0 * (double)iters * (kind == 1 ? 16384.0 : 65536.0);
     return hip_status(launch_mfma_peak(kind, blocks, iters, seed, out, static_cast<hipStream_t>(stream)));
 }
 

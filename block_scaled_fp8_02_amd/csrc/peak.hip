@@ -44,6 +44,76 @@ __device__ __forceinline__ int bf16_word(uint64_t ctr) {
     return (int)(keep | ex);
 }
 
+// The fp8 loop with the per-block promotion of the FP32-scale recipe added,
+// pipelined as in the block-scaled GEMM: every MFMA starts from zero (one
+// 128-wide K block), and its four results are added into fp32 accumulators
+// one step later with one FMA each by a combined scale (ROWSCALE = false,
+// the 1x128 x 128x128 GEMMs) or, for per-row scales on both operands (the
+// token-axis WGrad), by a product formed per result first (one multiply and
+// one FMA each).  Scales are random and opaque to the compiler every step,
+// so nothing is hoisted out of the loop.
+template <bool ROWSCALE>
+__global__ __launch_bounds__(256) void k_mfma_promote_peak(int64_t iters, uint32_t seed, float* __restrict__ out) {
+    const int lane = threadIdx.x & 63;
+    const uint64_t wave = (uint64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+    const uint64_t base = ((uint64_t)seed << 40) ^ (wave << 12) ^ ((uint64_t)lane << 5);
+    v8i a[4], b[4];
+#pragma unroll
+    for (int f = 0; f < 4; ++f)
+#pragma unroll
+        for (int r = 0; r < 8; ++r) {
+            const uint64_t ca = base + (uint64_t)(f * 8 + r), cb = ca + (1ull << 39);
+            a[f][r] = fp8_word(ca);
+            b[f][r] = fp8_word(cb);
+        }
+    float sp[4], sq[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        sp[j] = 1.0f + (float)(mix64(base + 100 + j) >> 41) * 0x1p-23f;
+        sq[j] = 1.0f + (float)(mix64(base + 200 + j) >> 41) * 0x1p-23f;
+    }
+    v4f acc[4][4], prev[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        prev[j] = v4f{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int r = 0; r < 4; ++r) acc[j][r] = v4f{0.f, 0.f, 0.f, 0.f};
+    }
+    for (int64_t it = 0; it < iters; ++it) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+#pragma unroll
+            for (int j = 0; j < 4; ++j) asm volatile("" : "+v"(sp[j]), "+v"(sq[j]));
+            v4f cur[4];
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                cur[j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a[j], b[(j + r) & 3],
+                                                                          v4f{0.f, 0.f, 0.f, 0.f}, 0, 0, 0, 0, 0, 0);
+            const int pr = (r + 3) & 3;                                 // the previous step's sub-tile
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                if constexpr (ROWSCALE) {
+#pragma unroll
+                    for (int e = 0; e < 4; ++e)
+                        acc[pr][j][e] = __builtin_fmaf(prev[j][e], sp[j] * sq[e], acc[pr][j][e]);
+                } else {
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) acc[pr][j][e] = __builtin_fmaf(prev[j][e], sp[j], acc[pr][j][e]);
+                }
+                prev[j] = cur[j];
+            }
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    }
+    v4f s = v4f{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) s += acc[j][r];
+    const float v = s[0] + s[1] + s[2] + s[3];
+    if (lane == 0) out[wave] = v;
+}
+
 template <bool BF16>
 __global__ __launch_bounds__(256) void k_mfma_peak(int64_t iters, uint32_t seed, float* __restrict__ out) {
     const int lane = threadIdx.x & 63;
@@ -89,8 +159,14 @@ __global__ __launch_bounds__(256) void k_mfma_peak(int64_t iters, uint32_t seed,
 hipError_t launch_mfma_peak(int kind, int64_t blocks, int64_t iters, uint32_t seed, float* out, hipStream_t st) {
     if (blocks <= 0 || iters <= 0) return hipSuccess;
     if (blocks > 0x7FFFFFFF) return hipErrorInvalidValue;
-    if (kind == 0) k_mfma_peak<false><<<dim3((unsigned)blocks), 256, 0, st>>>(iters, seed, out);
-    else k_mfma_peak<true><<<dim3((unsigned)blocks), 256, 0, st>>>(iters, seed, out);
+    const dim3 grid((unsigned)blocks);
+    switch (kind) {
+        case 0: k_mfma_peak<false><<<grid, 256, 0, st>>>(iters, seed, out); break;
+        case 1: k_mfma_peak<true><<<grid, 256, 0, st>>>(iters, seed, out); break;
+        case 2: k_mfma_promote_peak<false><<<grid, 256, 0, st>>>(iters, seed, out); break;
+        case 3: k_mfma_promote_peak<true><<<grid, 256, 0, st>>>(iters, seed, out); break;
+        default: return hipErrorInvalidValue;
+    }
     return hipGetLastError();
 }
 

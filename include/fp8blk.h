@@ -452,14 +452,20 @@ FP8B_API int fp8b_e4m3_encode(const float* x, const float* s, int64_t n, uint8_t
  * compared with beside the published peak (the chip is power limited, and
  * its clock under load depends on the data the matrix cores multiply).
  * kind 0: v_mfma_f32_16x16x128_f8f6f4 on E4M3 codes (NaN codes excluded);
- * kind 1: v_mfma_f32_16x16x32_bf16 on bf16 values of magnitude in [2^-8, 2^8).
+ * kind 1: v_mfma_f32_16x16x32_bf16 on bf16 values of magnitude in [2^-8, 2^8);
+ * kind 2: kind 0 with the FP32-scale promotion of the 1x128 x 128x128 GEMMs
+ *         (each MFMA's four results added into fp32 accumulators one step
+ *         later with one FMA each by a combined scale);
+ * kind 3: kind 0 with the promotion of the token-axis WGrad (per-row scales
+ *         on both operands: one multiply and one FMA per result).
  * Launches `blocks` blocks of 4 waves; each wave keeps four random A and
  * four random B fragments and four accumulators in registers (bytes from a
  * SplitMix64 hash of seed, wave, lane and register) and issues 16 MFMAs per
  * iteration, `iters` iterations, with no memory traffic in the loop.
  * out: DEVICE fp32[4 * blocks], one value per wave (keeps the work live).
  * flops (host, nullable): receives the floating-point operations launched,
- * blocks * 4 * 16 * iters * (65536 for kind 0, 16384 for kind 1).
+ * blocks * 4 * 16 * iters * (16384 for kind 1, else 65536); the promotion
+ * work of kinds 2 and 3 is not counted, as in the GEMMs' own figures.
  * Errors: FP8B_EINVAL (bad kind, NULL out), FP8B_ESHAPE, FP8B_EHIP. */
 FP8B_API int fp8b_mfma_peak(int kind, int64_t blocks, int64_t iters, uint32_t seed, float* out, double* flops,
                    void* stream);
