@@ -707,11 +707,21 @@ def other_workloads(torch, fb, wl, dev, seed):
     dec["fprop"] = report(time_cold(torch, lambda: fb.fp8_gemm_fprop(xq, xs, wq, ws, N, D, C, y=y), flush),
                           N * C + D * C + N * cd(C, 128) * 4 + cd(D, 128) * cd(C, 128) * 4 + N * D * 2,
                           2.0 * N * D * C)
-    # the rollout step (quantize the activation, then FProp) as two eager
-    # launches and as one HIP graph replay of the same two kernels
+    # the decode layout of the weight (written once per weight update) and
+    # FProp on it: the rollout path, bit for bit the row-major FProp
+    wp, _ = fb.fp8_pack_decode_weight(wq, D, C)
+    dec["pack_decode_layout"] = report(time_cold(torch, lambda: fb.fp8_pack_decode_weight(wq, D, C, wp=wp), flush),
+                                       2 * D * C)
+    dec["fprop_packed"] = report(time_cold(torch, lambda: fb.fp8_gemm_fprop_decode(xq, xs, wp, ws, N, D, C, y=y),
+                                           flush),
+                                 N * C + D * C + N * cd(C, 128) * 4 + cd(D, 128) * cd(C, 128) * 4 + N * D * 2,
+                                 2.0 * N * D * C)
+    # the rollout step (quantize the activation, then FProp on the packed
+    # weight) as two eager launches and as one HIP graph replay of the same
+    # two kernels
     def step():
         fb.fp8_quantize_act_1x128(X, xq, xs)
-        fb.fp8_gemm_fprop(xq, xs, wq, ws, N, D, C, y=y)
+        fb.fp8_gemm_fprop_decode(xq, xs, wp, ws, N, D, C, y=y)
     step_bytes = (N * C * 2 + 2 * (N * C + N * cd(C, 128) * 4) + D * C + cd(D, 128) * cd(C, 128) * 4
                   + N * D * 2)
     dec["step_eager"] = report(time_cold(torch, step, flush), step_bytes, 2.0 * N * D * C)
@@ -740,7 +750,7 @@ def other_workloads(torch, fb, wl, dev, seed):
                           2.0 * N * D * C)
     dec["wgrad"] = report(time_cold(torch, lambda: fb.fp8_gemm_wgrad(gqT, gsT, xqT, xsT, N, D, C, dw=dw1), flush),
                           (D + C) * 128 + (D + C) * 4 + D * C * 2, 2.0 * N * D * C)
-    del gq, gqT, xqT, dx1, dw1, wqT
+    del gq, gqT, xqT, dx1, dw1, wqT, wp
     out["decode_1x128"] = dec
 
     # the same tensors through the MXFP8 path (plus dY [64 x 24576])
@@ -756,6 +766,13 @@ def other_workloads(torch, fb, wl, dev, seed):
     dw = torch.empty((D, C), dtype=torch.bfloat16, device=dev)
     mx["fprop"] = report(time_cold(torch, lambda: fb.fp8_mx_gemm_fprop(q_x[0], q_x[1], q_w[0], q_w[1], N, D, C, y=y),
                                    flush), N * C * 33 // 32 + D * C * 33 // 32 + N * D * 2, 2.0 * N * D * C)
+    mp = fb.fp8_pack_decode_weight(q_w[0], D, C, we=q_w[1])
+    mx["pack_decode_layout"] = report(time_cold(torch, lambda: fb.fp8_pack_decode_weight(
+        q_w[0], D, C, we=q_w[1], wp=mp[0], wep=mp[1]), flush), 2 * D * C * 33 // 32)
+    mx["fprop_packed"] = report(time_cold(torch, lambda: fb.fp8_mx_gemm_fprop_decode(
+        q_x[0], q_x[1], mp[0], mp[1], N, D, C, y=y), flush),
+        N * C * 33 // 32 + D * C * 33 // 32 + N * D * 2, 2.0 * N * D * C)
+    del mp
     mx["dgrad"] = report(time_cold(torch, lambda: fb.fp8_mx_gemm_dgrad(q_g[0], q_g[1], q_w[2], q_w[3], N, D, C, dx=dx),
                                    flush), N * D * 33 // 32 + D * C * 33 // 32 + N * C * 2, 2.0 * N * D * C)
     Kp = 128   # the token axis (64) padded to one 128-wide block

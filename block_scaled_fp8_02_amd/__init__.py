@@ -77,6 +77,10 @@ _SIGS = {
                                _p, _i64, _i64, _i64, _i64, _p],
     "fp8_mx_quantize_1x32": [_p, _i32, _i64, _i64, _i64, _p, _i64, _p, _i64, _p, _i64, _p, _i64, _p],
     "fp8_mx_gemm_fprop": [_p, _i64, _p, _i64, _p, _i64, _p, _i64, _p, _i32, _i64, _i64, _i64, _i64, _p],
+    "fp8_decode_pack_bytes": [_i64, _i64, _i32],
+    "fp8_pack_decode_weight": [_p, _i64, _p, _i64, _i64, _i64, _p, _p, _p],
+    "fp8_gemm_fprop_decode": [_p, _i64, _p, _i64, _p, _p, _i64, _p, _i32, _i64, _i64, _i64, _i64, _p],
+    "fp8_mx_gemm_fprop_decode": [_p, _i64, _p, _i64, _p, _p, _p, _i32, _i64, _i64, _i64, _i64, _p],
     "fp8_mx_gemm_dgrad": [_p, _i64, _p, _i64, _p, _i64, _p, _i64, _p, _i32, _i64, _i64, _i64, _i64, _p],
     "fp8_mx_gemm_dgrad_split": [_p, _i64, _p, _i64, _p, _i64, _p, _i64, _p, _i32, _i64, _i64, _i64, _i64,
                                 _p, _i64, _p],
@@ -104,7 +108,8 @@ def lib():
             fn = getattr(L, name)
             fn.argtypes = args
             fn.restype = {"fp8b_status_string": ctypes.c_char_p,
-                          "fp8_gemm_dgrad_split_bytes": ctypes.c_int64}.get(name, ctypes.c_int)
+                          "fp8_gemm_dgrad_split_bytes": ctypes.c_int64,
+                          "fp8_decode_pack_bytes": ctypes.c_int64}.get(name, ctypes.c_int)
         _lib = L
     return _lib
 
@@ -667,6 +672,70 @@ def fp8_mx_gemm_fprop(xq, xe, wq, we, N, D, C, y=None, out_dtype=torch.bfloat16)
     _need(y, "y", N, D, _FLOAT_IO, dev)
     _call("fp8_mx_gemm_fprop", _ptr(xq), _ld(xq), _ptr(xe), _ld(xe), _ptr(wq), _ld(wq), _ptr(we), _ld(we),
           _ptr(y), _out_dtype_code(y.dtype), _ld(y), N, D, C, _stream(xq.device))
+    return y
+
+
+# ------------------------------------------------------- rollout decode
+def _need_packed(t, name, rows, cols, dtype, dev):
+    """A decode-layout buffer: exactly rows x cols elements, contiguous."""
+    if (not isinstance(t, torch.Tensor) or not t.is_cuda or t.device != dev or t.dtype != dtype
+            or tuple(t.shape) != (rows, cols) or not t.is_contiguous()):
+        raise ValueError(f"{name} must be a contiguous {dtype} tensor [{rows}, {cols}] on {dev}")
+    return t
+
+
+def fp8_decode_pack_bytes(D: int, C: int, part: int = 0) -> int:
+    return int(lib().fp8_decode_pack_bytes(D, C, part))
+
+
+def fp8_pack_decode_weight(wq, D, C, we=None, wp=None, wep=None):
+    """Decode layout of quantized weight codes wq [D, >= rup(C)] and, for
+    MX, their E8M0 bytes we -> (wp uint8 [16 ceil(D/16), rup(C)],
+    wep int32 [16 ceil(D/16), ceil(C/128)] or None).  The 2-D shapes only
+    size the buffers: their contents are in the decode order."""
+    dev = wq.device
+    _need(wq, "wq", D, _rup(C), _U8, dev)
+    R = _rup(D, 16)
+    wp = _new((R, _rup(C)), torch.uint8, dev) if wp is None else wp
+    _need_packed(wp, "wp", R, _rup(C), torch.uint8, dev)
+    if we is not None:
+        _need(we, "we", D, _rup(C) // 32, _U8, dev)
+        wep = _new((R, _cdiv(C, 128)), torch.int32, dev) if wep is None else wep
+        _need_packed(wep, "wep", R, _cdiv(C, 128), torch.int32, dev)
+    else:
+        wep = None
+    _call("fp8_pack_decode_weight", _ptr(wq), _ld(wq), _ptr(we), _ld(we) if we is not None else 0, D, C,
+          _ptr(wp), _ptr(wep), _stream(dev))
+    return wp, wep
+
+
+def fp8_gemm_fprop_decode(xq, xs, wp, ws, N, D, C, y=None, out_dtype=torch.bfloat16):
+    """FProp of N <= 64 tokens on the decode layout wp of the weight codes
+    (ws: the weight's 128x128 scales); bit for bit fp8_gemm_fprop."""
+    dev = xq.device
+    _need(xq, "xq", N, _rup(C), _U8, dev)
+    _need(xs, "xs", N, _cdiv(C, 128), _F32, dev)
+    _need_packed(wp, "wp", _rup(D, 16), _rup(C), torch.uint8, dev)
+    _need(ws, "ws", _cdiv(D, 128), _cdiv(C, 128), _F32, dev)
+    y = _new_out(N, D, out_dtype, dev) if y is None else y
+    _need(y, "y", N, D, _FLOAT_IO, dev)
+    _call("fp8_gemm_fprop_decode", _ptr(xq), _ld(xq), _ptr(xs), _ld(xs), _ptr(wp), _ptr(ws), _ld(ws),
+          _ptr(y), _out_dtype_code(y.dtype), _ld(y), N, D, C, _stream(dev))
+    return y
+
+
+def fp8_mx_gemm_fprop_decode(xq, xe, wp, wep, N, D, C, y=None, out_dtype=torch.bfloat16):
+    """MXFP8 FProp of N <= 64 tokens on the decode layout (wp, wep); bit for
+    bit fp8_mx_gemm_fprop."""
+    dev = xq.device
+    _need(xq, "xq", N, _rup(C), _U8, dev)
+    _need(xe, "xe", N, _rup(C) // 32, _U8, dev)
+    _need_packed(wp, "wp", _rup(D, 16), _rup(C), torch.uint8, dev)
+    _need_packed(wep, "wep", _rup(D, 16), _cdiv(C, 128), torch.int32, dev)
+    y = _new_out(N, D, out_dtype, dev) if y is None else y
+    _need(y, "y", N, D, _FLOAT_IO, dev)
+    _call("fp8_mx_gemm_fprop_decode", _ptr(xq), _ld(xq), _ptr(xe), _ld(xe), _ptr(wp), _ptr(wep),
+          _ptr(y), _out_dtype_code(y.dtype), _ld(y), N, D, C, _stream(dev))
     return y
 
 

@@ -100,7 +100,7 @@ int validate_gemm(int op, const void* a, int64_t lda, const void* sa, int64_t ld
     FP8B_TRY(check_codes(a, M, K, lda));
     FP8B_TRY(check_codes(b, Nn, K, ldb));
     const int64_t kb = mx ? rup128(K) / 32 : cdiv(K, 128);
-    const uintptr_t sal = mx ? 1 : 4;
+    const uintptr_t sal = 4;                             // fp32 words, or E8M0 bytes read as words
     FP8B_TRY(check_scales(sa, M, kb, ldsa, sal));
     if (!mx && base != 2) {
         // 128x128 weight scale grid [ceil(D/128) x ceil(C/128)], row stride ldsb
@@ -108,6 +108,8 @@ int validate_gemm(int op, const void* a, int64_t lda, const void* sa, int64_t ld
     } else {
         FP8B_TRY(check_scales(sb, Nn, kb, ldsb, sal));
     }
+    // E8M0 rows are fetched four bytes (one K block) at a time
+    if (mx && K > 0 && ((M > 0 && ldsa % 4 != 0) || (Nn > 0 && ldsb % 4 != 0))) return FP8B_EALIGN;
     FP8B_TRY(check_output(out, odt, M, Nn, ldo, beta));
     return FP8B_OK;
 }
@@ -149,7 +151,7 @@ int check_offsets(const int32_t* offsets, int64_t E) {
 
 extern "C" {
 
-int fp8b_abi_version(void) { return 2; }
+int fp8b_abi_version(void) { return 3; }
 
 const char* fp8b_status_string(int status) {
     switch (status) {
@@ -651,6 +653,57 @@ int fp8_mx_gemm_wgrad(const uint8_t* gqT, int64_t ldgqT, const uint8_t* geT, int
                       void* dw, int dwt, int64_t lddw, int beta,
                       int64_t N, int64_t D, int64_t C, void* stream) {
     return gemm_dense(5, gqT, ldgqT, geT, ldgeT, xqT, ldxqT, xeT, ldxeT, dw, dwt, lddw, beta, N, D, C, stream);
+}
+
+int64_t fp8_decode_pack_bytes(int64_t D, int64_t C, int part) {
+    if (D < 0 || C < 0) return 0;
+    const int64_t rows = cdiv(D, 16) * 16;
+    if (part == 0) return rows * rup128(C);
+    if (part == 1) return rows * cdiv(C, 128) * 4;
+    return 0;
+}
+
+int fp8_pack_decode_weight(const uint8_t* wq, int64_t ldwq, const uint8_t* we, int64_t ldwe,
+                           int64_t D, int64_t C, uint8_t* wp, uint32_t* wep, void* stream) {
+    if (D < 0 || C < 0) return FP8B_ESHAPE;
+    FP8B_TRY(check_codes(wq, D, C, ldwq));
+    if (we != nullptr) {
+        FP8B_TRY(check_scales(we, D, rup128(C) / 32, ldwe, 4));
+        if (ldwe % 4 != 0) return FP8B_EALIGN;
+    }
+    if (D == 0 || C == 0) return FP8B_OK;
+    if (wp == nullptr || (we != nullptr && wep == nullptr)) return FP8B_EINVAL;
+    if (!aligned(wp, 16) || (we != nullptr && !aligned(wep, 4))) return FP8B_EALIGN;
+    return hip_status(launch_pack_decode(wq, ldwq, we, ldwe, D, cdiv(C, 128), wp, we != nullptr ? wep : nullptr,
+                                         static_cast<hipStream_t>(stream)));
+}
+
+// Decode FProp on a packed weight (op 0 block-scaled, op 3 MX).  The packed
+// codes are validated as a code operand with rows of round_up(C,128) bytes,
+// the packed MX words as scale rows of round_up(C,128)/32 bytes.
+static int gemm_decode(int op, const uint8_t* xq, int64_t ldxq, const void* xs, int64_t ldxs,
+                       const uint8_t* wp, const void* ws, int64_t ldws,
+                       void* y, int yt, int64_t ldy, int64_t N, int64_t D, int64_t C, void* stream) {
+    if (N > 64) return FP8B_EUNSUPPORTED;
+    const int64_t ldp = rup128(C), ldsw = op == 3 ? rup128(C) / 32 : ldws;
+    FP8B_TRY(validate_gemm(op, xq, ldxq, xs, ldxs, wp, ldp, ws, ldsw, y, yt, ldy, 0, N, D, C));
+    const hipStream_t st = static_cast<hipStream_t>(stream);
+    if (N == 0 || D == 0) return FP8B_OK;
+    if (C == 0) return hip_status(launch_zero_2d(y, ldy * esize(yt), D * esize(yt), N, st));
+    const GemmArgs g = dense_args(op, xq, ldxq, xs, ldxs, wp, ldp, ws, ldsw, y, yt, ldy, 0, N, D, C);
+    return hip_status(launch_gemm_decode_packed(g, st));
+}
+
+int fp8_gemm_fprop_decode(const uint8_t* xq, int64_t ldxq, const float* xs, int64_t ldxs,
+                          const uint8_t* wp, const float* ws, int64_t ldws,
+                          void* y, int yt, int64_t ldy, int64_t N, int64_t D, int64_t C, void* stream) {
+    return gemm_decode(0, xq, ldxq, xs, ldxs, wp, ws, ldws, y, yt, ldy, N, D, C, stream);
+}
+
+int fp8_mx_gemm_fprop_decode(const uint8_t* xq, int64_t ldxq, const uint8_t* xe, int64_t ldxe,
+                             const uint8_t* wp, const uint32_t* wep,
+                             void* y, int yt, int64_t ldy, int64_t N, int64_t D, int64_t C, void* stream) {
+    return gemm_decode(3, xq, ldxq, xe, ldxe, wp, wep, 0, y, yt, ldy, N, D, C, stream);
 }
 
 int fp8b_mfma_peak(int kind, int64_t blocks, int64_t iters, uint32_t seed, float* out, double* flops,

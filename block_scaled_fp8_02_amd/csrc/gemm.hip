@@ -661,6 +661,9 @@ static hipError_t launch_sm(const GemmArgs& a, hipStream_t st) {
     // least one block per compute unit, with 4 or 8 stages in flight.  The
     // per-element arithmetic is the same in every configuration.
     if (a.M <= 64 && a.group_mode == GROUP_NONE) {
+        // a weight of at least 128 x 96 rows: streamed through registers,
+        // 96 rows per block (decode.hip)
+        if (rows96_applies(a)) return launch_gemm_rows96(a, st);
         // K split into ranges (few-row DGrad, where the output has too few
         // tiles to occupy the chip): 128-row weight tiles as for a large weight
         if (a.ksplit > 1) return launch_cfg<64, 128, 4, 1, 8, SM, 4, GROUP_NONE>(a, st);

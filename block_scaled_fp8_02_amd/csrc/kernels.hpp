@@ -118,6 +118,22 @@ struct GemmArgs {
 
 hipError_t launch_gemm(const GemmArgs& a, hipStream_t st);
 
+// Few-token GEMM with the weight streamed through registers (decode.hip):
+// whether it takes a launch (at most 64 rows of P, a long Q, no K split, no
+// grouping, 128x128 or MX scales), and the launch.  Per-output arithmetic
+// identical to launch_gemm's.
+bool rows96_applies(const GemmArgs& a);
+hipError_t launch_gemm_rows96(const GemmArgs& a, hipStream_t st);
+// The same kernel on a weight in the decode layout (Q and, for MX, sQ as
+// written by launch_pack_decode; 128x128 scales as for launch_gemm): any
+// Nn, 1 <= M <= 64, beta 0.
+hipError_t launch_gemm_decode_packed(const GemmArgs& a, hipStream_t st);
+// Decode layout of row-major codes wq [D x ldwq] (KB K blocks per row) and,
+// when we != nullptr, of their E8M0 bytes we [D x ldwe]: wp gets
+// 16 ceil(D/16) KB 128 bytes, wep 16 ceil(D/16) KB words.
+hipError_t launch_pack_decode(const uint8_t* wq, int64_t ldwq, const uint8_t* we, int64_t ldwe,
+                              int64_t D, int64_t KB, uint8_t* wp, uint32_t* wep, hipStream_t st);
+
 // out[i][j] = sum over s = 0 .. S-1, in that order, of part[s * slice + i * ldp + j]
 // (fp32), stored as bf16 (nearest-even) or fp32 at row stride ldo.
 hipError_t launch_split_sum(const float* part, int64_t S, int64_t slice, int64_t ldp, int64_t M, int64_t Nn,

@@ -419,7 +419,9 @@ FP8B_API int fp8_mx_quantize_1x32(const void* x, int xt, int64_t rows, int64_t c
  * with both operands K-contiguous:
  *   FProp: a = X row-wise [N x C], b = W row-wise [D x C]          -> y [N x D]
  *   DGrad: a = dY row-wise [N x D], b = W column-wise [C x D]      -> dx [N x C]
- *   WGrad: a = dY column-wise [D x N], b = X column-wise [C x N]   -> dw [D x C] */
+ *   WGrad: a = dY column-wise [D x N], b = X column-wise [C x N]   -> dw [D x C]
+ * E8M0 operands: pointers and row strides multiples of 4 (FP8B_EALIGN
+ * otherwise; each K block's four bytes are fetched as one word). */
 FP8B_API int fp8_mx_gemm_fprop(const uint8_t* xq, int64_t ldxq, const uint8_t* xe, int64_t ldxe,
                       const uint8_t* wq, int64_t ldwq, const uint8_t* we, int64_t ldwe,
                       void* y, int yt, int64_t ldy, int64_t N, int64_t D, int64_t C, void* stream);
@@ -434,6 +436,56 @@ FP8B_API int fp8_mx_gemm_wgrad(const uint8_t* gqT, int64_t ldgqT, const uint8_t*
                       const uint8_t* xqT, int64_t ldxqT, const uint8_t* xeT, int64_t ldxeT,
                       void* dw, int dwt, int64_t lddw, int beta,
                       int64_t N, int64_t D, int64_t C, void* stream);
+
+/* ------------------------------------------------------------------ */
+/* Rollout decode: FProp of at most 64 tokens on a packed weight        */
+/* ------------------------------------------------------------------ */
+
+/* Rollout runs the training forward's FP8 FProp (Jet-RL notes, section 2.2
+ * FProp, and the unified precision flow of the Jet-RL summary: rollout uses
+ * the same quantized weights and GEMM as the training forward) on few
+ * tokens, where reading the weight is the whole cost.  The decode layout
+ * holds the same codes in the order the decode kernel's loads consume them,
+ * so each load reads 1 KB of consecutive bytes; it is written once per
+ * weight update and read by every decode step.  The results are bit for bit
+ * those of fp8_gemm_fprop / fp8_mx_gemm_fprop on the row-major weight (same
+ * products, same per-output reduction order).
+ *
+ * fp8_decode_pack_bytes: bytes of the decode-layout codes (part 0:
+ * 16 ceil(D/16) round_up(C,128)) or of the packed MX scale words (part 1:
+ * 16 ceil(D/16) ceil(C/128) 4); 0 for negative sizes or another part.
+ *
+ * fp8_pack_decode_weight: decode layout of wq [D x ldwq] codes (as written by
+ * fp8_quantize_weight_128x128 or fp8_mx_quantize_1x32; ldwq >= round_up(C,128),
+ * pointer and ldwq multiples of 16) into wp (DEVICE, part-0 bytes, 16-byte
+ * aligned; rows past D in the last group of 16 are zero codes); when we is
+ * not NULL, also the E8M0 bytes we [D x ldwe] (pointer and ldwe multiples of
+ * 4, ldwe >= round_up(C,128)/32) into the words wep (DEVICE, part-1 bytes,
+ * 4-byte aligned; required then).  The layout, for g < ceil(D/16), K block
+ * k < ceil(C/128), h in {0,1}, lane l < 64: wp bytes
+ * [((g ceil(C/128) + k) 2 + h) 1024 + 16 l, +16) hold row 16 g + l % 16,
+ * bytes [128 k + 16 (l/16 + 4 h), +16) of the row-major codes; word
+ * wep[(g ceil(C/128) + k) 16 + r] holds the four E8M0 bytes of row 16 g + r
+ * for K block k (0x7F7F7F7F past D).  wp and wep are owned by the caller;
+ * D == 0 or C == 0 writes nothing. */
+FP8B_API int64_t fp8_decode_pack_bytes(int64_t D, int64_t C, int part);
+FP8B_API int fp8_pack_decode_weight(const uint8_t* wq, int64_t ldwq, const uint8_t* we, int64_t ldwe,
+                                    int64_t D, int64_t C, uint8_t* wp, uint32_t* wep, void* stream);
+
+/* FProp y[N x D] = X W^T with N <= 64 (N > 64: FP8B_EUNSUPPORTED) on the
+ * decode layout wp of W's codes; xq/xs and ws as for fp8_gemm_fprop
+ * (1x128 tokens, 128x128 weight scales), y [N x ldy] of dtype yt.
+ * C == 0 writes zeros. */
+FP8B_API int fp8_gemm_fprop_decode(const uint8_t* xq, int64_t ldxq, const float* xs, int64_t ldxs,
+                                   const uint8_t* wp, const float* ws, int64_t ldws,
+                                   void* y, int yt, int64_t ldy, int64_t N, int64_t D, int64_t C, void* stream);
+
+/* The MXFP8 form: xq/xe as for fp8_mx_gemm_fprop, the weight as wp and wep
+ * from fp8_pack_decode_weight of its codes and E8M0 bytes. */
+FP8B_API int fp8_mx_gemm_fprop_decode(const uint8_t* xq, int64_t ldxq, const uint8_t* xe, int64_t ldxe,
+                                      const uint8_t* wp, const uint32_t* wep,
+                                      void* y, int yt, int64_t ldy, int64_t N, int64_t D, int64_t C,
+                                      void* stream);
 
 /* ------------------------------------------------------------------ */
 /* Codec access (for exhaustive checks of the device codec)            */

@@ -9,7 +9,7 @@
 #include "fp8blk.h"
 int main(void) {
   int bad = 0;
-  if (fp8b_abi_version() != 2) bad++;
+  if (fp8b_abi_version() != 3) bad++;
   for (int s = -1; s < 8; ++s) if (!fp8b_status_string(s)) bad++;
   int64_t shapes[][3] = {{64,24576,4096},{1,3000,4099},{37,2304,301},{0,0,0},{-1,5,5},{65,4096,512},{64,1 << 20,128}};
   for (int i = 0; i < 7; ++i) (void)fp8_gemm_dgrad_split_bytes(shapes[i][0], shapes[i][1], shapes[i][2]);
@@ -22,6 +22,12 @@ int main(void) {
   if (fp8_gemm_dgrad_split_noalloc(P, 4096, P, 32, P, 4096, P, 4, NULL, 0, 512, 64, 4096, 512, NULL) != 1) bad++;
   if (fp8_dequant_gemm_wgrad(P, 128, P, 256, P, 2, 0, 16, 128, 256, P, 1, 256, 0, P, 8, NULL) != 2) bad++;
   if (fp8b_mfma_peak(5, 1, 1, 0, P, NULL, NULL) != 1) bad++;
+  for (int64_t d = -1; d < 40; d += 13)
+    for (int part = -1; part < 3; ++part) (void)fp8_decode_pack_bytes(d, 300, part);
+  if (fp8_pack_decode_weight(P, 384, P, 13, 17, 300, P, P, NULL) != 3) bad++;
+  if (fp8_pack_decode_weight(P, 384, NULL, 0, 17, 300, NULL, NULL, NULL) != 1) bad++;
+  if (fp8_gemm_fprop_decode(P, 384, P, 3, P, P, 3, P, 1, 24, 65, 17, 300, NULL) != 4) bad++;
+  if (fp8_mx_gemm_fprop_decode(P, 384, P, 13, P, P, P, 1, 24, 64, 17, 300, NULL) != 3) bad++;
   int32_t offs[3] = {0, 1, 2};
   (void)offs;
   printf("host validation sanitizer run: %s\n", bad ? "FAILED" : "ok");

@@ -34,7 +34,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_abi_version_and_status_strings():
-    assert fb.fp8b_abi_version() == 2
+    assert fb.fp8b_abi_version() == 3
     assert fb.fp8b_status_string(0) == "ok"
     assert "shape" in fb.fp8b_status_string(2)
 
@@ -90,9 +90,16 @@ def test_validate_gemm_leading_dimension_limits():
 
 
 def test_validate_mx():
-    # MX: E8M0 scales per 32 along the padded K (alignment 1)
-    assert v(3, ldsa=16, ldsb=16, sa=SA + 1, sb=SB + 3) == 0
+    # MX: E8M0 scales per 32 along the padded K, fetched as one word per K
+    # block: pointers and row strides multiples of 4
+    assert v(3, ldsa=16, ldsb=16) == 0
+    assert v(3, ldsa=16, ldsb=20, sa=SA + 4, sb=SB + 12) == 0
+    assert v(3, ldsa=16, ldsb=16, sa=SA + 1) == 3
+    assert v(3, ldsa=16, ldsb=16, sb=SB + 2) == 3
+    assert v(3, ldsa=18, ldsb=16) == 3
+    assert v(5, lda=256, ldb=256, ldsa=8, ldsb=10, ldo=512) == 3
     assert v(3, ldsa=15, ldsb=16) == 2
+    assert v(3, ldsa=18, ldsb=16, N=0) == 0             # nothing read
 
 
 def test_binding_refuses_cpu_tensors():
@@ -208,3 +215,50 @@ def test_dgrad_split_workspace_and_host_checks():
         assert call(fn, None, need) == 1            # no workspace
         assert call(fn, WK + 8, need) == 3          # misaligned workspace
         assert call(fn, WK, need - 16) == 2         # too small
+
+
+def test_decode_entry_points_host_checks():
+    """Decode layout sizes and the host-side rejections of the pack and
+    decode FProp entry points (each failing call returns before any launch;
+    the calls that succeed have nothing to do)."""
+    L = fb.lib()
+    assert L.fp8_decode_pack_bytes(24576, 4096, 0) == 24576 * 4096
+    assert L.fp8_decode_pack_bytes(24576, 4096, 1) == 24576 * 32 * 4
+    assert L.fp8_decode_pack_bytes(17, 300, 0) == 32 * 384           # rows to 16, K to 128
+    assert L.fp8_decode_pack_bytes(17, 300, 1) == 32 * 3 * 4
+    assert L.fp8_decode_pack_bytes(-1, 5, 0) == 0
+    assert L.fp8_decode_pack_bytes(5, 5, 2) == 0
+    WQ, WE, WP, WEP, XQ, XS, WS, Y = (0x100000, 0x200000, 0x300000, 0x400000, 0x500000, 0x600000,
+                                      0x700000, 0x800000)
+    pack = L.fp8_pack_decode_weight
+    assert pack(WQ, 384, None, 0, 17, 300, None, None, None) == 1          # no output
+    assert pack(WQ + 8, 384, None, 0, 17, 300, WP, None, None) == 3        # misaligned codes
+    assert pack(WQ, 256, None, 0, 17, 300, WP, None, None) == 2            # row shorter than 384
+    assert pack(WQ, 384, None, 0, 17, 300, WP + 8, None, None) == 3        # misaligned output
+    assert pack(WQ, 384, WE, 12, 17, 300, WP, None, None) == 1             # scales without their output
+    assert pack(WQ, 384, WE, 13, 17, 300, WP, WEP, None) == 3              # E8M0 row stride not a multiple of 4
+    assert pack(WQ, 384, WE, 12, 17, 300, WP, WEP + 2, None) == 3
+    assert pack(WQ, 384, WE, 8, 17, 300, WP, WEP, None) == 2               # 12 E8M0 bytes per row needed
+    assert pack(WQ, 384, None, 0, 0, 300, None, None, None) == 0           # empty
+    assert pack(WQ, 384, None, 0, 17, -1, WP, None, None) == 2
+    fprop = L.fp8_gemm_fprop_decode
+    ok = dict(xq=XQ, ldxq=384, xs=XS, ldxs=3, wp=WP, ws=WS, ldws=3, y=Y, yt=1, ldy=24, N=64, D=17, C=300)
+
+    def f(**kw):
+        a = dict(ok, **kw)
+        return fprop(a["xq"], a["ldxq"], a["xs"], a["ldxs"], a["wp"], a["ws"], a["ldws"], a["y"], a["yt"],
+                     a["ldy"], a["N"], a["D"], a["C"], None)
+    assert f(N=65) == 4                                                    # more than 64 tokens
+    assert f(wp=WP + 8) == 3
+    assert f(wp=0) == 1
+    assert f(ldxq=256) == 2
+    assert f(ldws=2) == 2
+    assert f(y=Y + 8) == 3
+    assert f(ldy=20) == 3                                                  # 40-byte bf16 rows
+    assert f(N=0) == 0
+    mx = L.fp8_mx_gemm_fprop_decode
+    assert mx(XQ, 384, XS + 1, 12, WP, WEP, Y, 1, 24, 64, 17, 300, None) == 3   # misaligned E8M0 rows
+    assert mx(XQ, 384, XS, 13, WP, WEP, Y, 1, 24, 64, 17, 300, None) == 3
+    assert mx(XQ, 384, XS, 12, WP, WEP + 2, Y, 1, 24, 64, 17, 300, None) == 3
+    assert mx(XQ, 384, XS, 12, WP, WEP, Y, 1, 24, 65, 17, 300, None) == 4
+    assert mx(XQ, 384, XS, 12, WP, WEP, Y, 1, 24, 0, 17, 300, None) == 0

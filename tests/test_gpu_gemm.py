@@ -228,6 +228,9 @@ def test_decode_fprop_full():
     xq, xs = fb.fp8_quantize_act_1x128(dev(X))
     wq, ws, _ = fb.fp8_quantize_weight_128x128(dev(W), transpose=False)
     y = host(fb.fp8_gemm_fprop(xq, xs, wq, ws, 64, 24576, 4096))
+    wp, _ = fb.fp8_pack_decode_weight(wq, 24576, 4096)
+    y_dec = host(fb.fp8_gemm_fprop_decode(xq, xs, wp, ws, 64, 24576, 4096))
+    assert np.array_equal(y_dec.view(np.uint32), y.view(np.uint32))     # the packed weight, bit for bit
     oxq, oxs = oracle.quant_1x128(X)
     owq, ows, _ = oracle.quant_128x128(W, with_transpose=False)
     check(y, oracle.fprop(oxq, oxs, owq, ows, 4096), TOL, "decode fprop")
@@ -303,6 +306,106 @@ def test_unified_forward_is_batch_invariant():
             assert torch.equal(ym, y_big[:m]), (D, m)
     y_again = fb.fp8_gemm_fprop(xq, xs, wq[:D], ws, 8192, D, 4096)
     assert torch.equal(y_again, y_big)
+
+
+# Decode-shaped FProp (at most 64 token rows, a weight of at least 128 groups
+# of 96 rows) runs on the weight-streaming decode kernel; these shapes give it
+# a ragged last row group, contractions shorter than one staged chunk, a
+# partial chunk and a partial register-ring group.
+ROWS96_SHAPES = [(1, 12289, 1), (37, 12289, 300), (64, 12300, 1100), (17, 24576, 640),
+                 (64, 12193, 4099)]
+
+
+@pytest.mark.parametrize("M,D,C", ROWS96_SHAPES)
+def test_decode_rows_kernel_ragged(M, D, C):
+    banner(f"decode rows kernel M={M} D={D} C={C}")
+    rng = np.random.default_rng(M * 5 + D + C)
+    X = (rng.standard_normal((80, C)) * np.exp(rng.uniform(-3, 3, (80, 1)))).astype(np.float32)
+    W = (rng.standard_normal((D, C)) * 0.02).astype(np.float32)
+    wq, ws, _ = fb.fp8_quantize_weight_128x128(dev_strided(W), transpose=False)
+    xq, xs = fb.fp8_quantize_act_1x128(dev_strided(X))
+    y32 = host(fb.fp8_gemm_fprop(xq[:M], xs[:M], wq, ws, M, D, C, out_dtype=torch.float32))
+    oxq, oxs = oracle.quant_1x128(X[:M])
+    owq, ows, _ = oracle.quant_128x128(W, with_transpose=False)
+    mag = oracle.matmul_f64(np.abs(oracle.deq_rowgroups(oxq, oxs, C)),
+                            np.abs(oracle.deq_128x128(owq, ows, D, C)).T)
+    check_f32(y32, oracle.fprop(oxq, oxs, owq, ows, C), mag, "decode rows fprop f32")
+    # same rows as the 80-row call (training tiles), bit for bit, both outputs
+    for dt in (torch.float32, torch.bfloat16):
+        y_big = fb.fp8_gemm_fprop(xq, xs, wq, ws, 80, D, C, out_dtype=dt)
+        y_m = fb.fp8_gemm_fprop(xq[:M], xs[:M], wq, ws, M, D, C, out_dtype=dt)
+        assert torch.equal(y_m, y_big[:M]), dt
+
+
+def packed_codes_ref(wq_host, D, C):
+    """Decode layout of row-major codes, written out with numpy: per group
+    of 16 rows and K block, half h holds chunks q + 4h of rows r at lane
+    16q + r (rows past D zero)."""
+    KB, R = (C + 127) // 128, (D + 15) // 16 * 16
+    rows = np.zeros((R, KB * 128), np.uint8)
+    rows[:D] = wq_host[:D, :KB * 128]
+    t = rows.reshape(R // 16, 16, KB, 2, 4, 16)          # grp, r, k, h, q, byte
+    return np.ascontiguousarray(t.transpose(0, 2, 3, 4, 1, 5)).reshape(R, KB * 128)
+
+
+@pytest.mark.parametrize("D,C", [(1, 1), (17, 300), (100, 128), (37, 1100)])
+def test_pack_decode_layout(D, C):
+    rng = np.random.default_rng(D + C)
+    W = (rng.standard_normal((D, C)) * 0.02).astype(np.float32)
+    wq, ws, _ = fb.fp8_quantize_weight_128x128(dev_strided(W), transpose=False)
+    wp, wep = fb.fp8_pack_decode_weight(wq, D, C)
+    assert wep is None
+    np.testing.assert_array_equal(host(wp), packed_codes_ref(host(wq), D, C))
+
+
+# Decode FProp on the packed weight: bit for bit the row-major FProp (itself
+# checked against the oracle above), at ragged shapes, few-row weights and
+# the full decode weight, for both output types.
+DECODE_SHAPES = [(1, 1, 1), (5, 17, 130), (64, 100, 4096), (37, 12289, 300), (64, 12300, 1100),
+                 (17, 24576, 640), (64, 12193, 4099), (3, 2000, 8192)]
+
+
+@pytest.mark.parametrize("M,D,C", DECODE_SHAPES)
+def test_decode_packed_matches_fprop(M, D, C):
+    banner(f"decode packed M={M} D={D} C={C}")
+    rng = np.random.default_rng(M + 3 * D + C)
+    X = (rng.standard_normal((M, C)) * np.exp(rng.uniform(-3, 3, (M, 1)))).astype(np.float32)
+    W = (rng.standard_normal((D, C)) * 0.02).astype(np.float32)
+    wq, ws, _ = fb.fp8_quantize_weight_128x128(dev_strided(W), transpose=False)
+    xq, xs = fb.fp8_quantize_act_1x128(dev_strided(X))
+    wp, _ = fb.fp8_pack_decode_weight(wq, D, C)
+    for dt in (torch.float32, torch.bfloat16):
+        y_row = fb.fp8_gemm_fprop(xq, xs, wq, ws, M, D, C, out_dtype=dt)
+        y_dec = fb.fp8_gemm_fprop_decode(xq, xs, wp, ws, M, D, C, out_dtype=dt)
+        assert torch.equal(y_dec, y_row), dt
+
+
+def test_decode_packed_oracle_and_edges():
+    """The packed decode against the oracle directly (fp32 output), more than
+    64 tokens refused, an empty contraction written as zeros."""
+    M, D, C = 64, 2000, 1100
+    rng = np.random.default_rng(77)
+    X = (rng.standard_normal((M, C)) * np.exp(rng.uniform(-3, 3, (M, 1)))).astype(np.float32)
+    W = (rng.standard_normal((D, C)) * 0.02).astype(np.float32)
+    wq, ws, _ = fb.fp8_quantize_weight_128x128(dev_strided(W), transpose=False)
+    xq, xs = fb.fp8_quantize_act_1x128(dev_strided(X))
+    wp, _ = fb.fp8_pack_decode_weight(wq, D, C)
+    y = host(fb.fp8_gemm_fprop_decode(xq, xs, wp, ws, M, D, C, out_dtype=torch.float32))
+    oxq, oxs = oracle.quant_1x128(X)
+    owq, ows, _ = oracle.quant_128x128(W, with_transpose=False)
+    mag = oracle.matmul_f64(np.abs(oracle.deq_rowgroups(oxq, oxs, C)), np.abs(oracle.deq_128x128(owq, ows, D, C)).T)
+    check_f32(y, oracle.fprop(oxq, oxs, owq, ows, C), mag, "decode packed f32")
+    X65 = dev(np.ones((65, C), np.float32))
+    xq65, xs65 = fb.fp8_quantize_act_1x128(X65)
+    with pytest.raises(RuntimeError):
+        fb.fp8_gemm_fprop_decode(xq65, xs65, wp, ws, 65, D, C)
+    z = torch.full((5, 8), 3.0, dtype=torch.float32, device="cuda")[:, :7]
+    empty = torch.zeros((7, 16), dtype=torch.uint8, device="cuda")
+    fb.fp8_gemm_fprop_decode(empty[:5, :0], torch.zeros((5, 4), dtype=torch.float32, device="cuda")[:, :0],
+                             torch.zeros((16, 0), dtype=torch.uint8, device="cuda"),
+                             torch.zeros((1, 4), dtype=torch.float32, device="cuda")[:, :0], 5, 7, 0, y=z)
+    torch.cuda.synchronize()
+    assert torch.all(z == 0)
 
 
 def test_wgrad_accumulate_fp32():

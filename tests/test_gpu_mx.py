@@ -162,3 +162,59 @@ def test_mx_forward_is_batch_invariant():
             xqm, xem, _, _ = fb.fp8_mx_quantize_1x32(dev(X[:m]), colwise=False)
             ym = fb.fp8_mx_gemm_fprop(xqm, xem, wq[:D], we[:D], m, D, 4096)
             assert torch.equal(ym, y_big[:m]), (D, m)
+
+
+@pytest.mark.parametrize("M,D,C", [(1, 12289, 1), (37, 12289, 300), (64, 12300, 1100),
+                                   (64, 12193, 4099)])
+def test_mx_decode_rows_kernel_ragged(M, D, C):
+    """Decode-shaped MX FProp (weight-streaming decode kernel): oracle parity
+    at ragged shapes, and the 80-row call's rows bit for bit."""
+    banner(f"mx decode rows kernel M={M} D={D} C={C}")
+    rng = np.random.default_rng(M * 3 + D + C)
+    X = (rng.standard_normal((80, C)) * np.exp(rng.uniform(-3, 3, (80, C)))).astype(np.float32)
+    W = (rng.standard_normal((D, C)) * 0.02).astype(np.float32)
+    xq, xe, _, _ = fb.fp8_mx_quantize_1x32(dev_strided(X), colwise=False)
+    wq, we, _, _ = fb.fp8_mx_quantize_1x32(dev_strided(W), colwise=False)
+    y = host(fb.fp8_mx_gemm_fprop(xq[:M], xe[:M], wq, we, M, D, C, out_dtype=torch.float32))
+    oxq, oxe = oracle.mx_quant_rows(X[:M])
+    owq, owe = oracle.mx_quant_rows(W)
+    mag = oracle.matmul_f64(np.abs(oracle.deq_mx(oxq, oxe, C)), np.abs(oracle.deq_mx(owq, owe, C)).T)
+    ref = oracle.mx_gemm(oxq, oxe, owq, owe, C)
+    err = oracle.rel_row_error(y, ref)
+    ratio = float(np.max(np.abs(y - ref) / np.maximum(mag, 1e-300)))
+    banner(f"mx decode rows: {err:.3e}, |err|/sum|ab| {ratio:.3e}")
+    assert err <= TOL
+    assert ratio <= 2.0 ** -12
+    for dt in (torch.float32, torch.bfloat16):
+        y_big = fb.fp8_mx_gemm_fprop(xq, xe, wq, we, 80, D, C, out_dtype=dt)
+        y_m = fb.fp8_mx_gemm_fprop(xq[:M], xe[:M], wq, we, M, D, C, out_dtype=dt)
+        assert torch.equal(y_m, y_big[:M]), dt
+
+
+def packed_scale_words_ref(we_host, D, C):
+    """Packed MX scale words with numpy: word (group, K block, r) holds row
+    16 group + r's four E8M0 bytes of that K block (127s past D)."""
+    KB, R = (C + 127) // 128, (D + 15) // 16 * 16
+    b = np.full((R, KB * 4), 127, np.uint8)
+    b[:D] = we_host[:D, :KB * 4]
+    words = b.reshape(R, KB, 4).copy().view(np.int32).reshape(R, KB)     # little-endian words
+    return np.ascontiguousarray(words.reshape(R // 16, 16, KB).transpose(0, 2, 1)).reshape(R, KB)
+
+
+@pytest.mark.parametrize("M,D,C", [(1, 1, 1), (5, 17, 130), (37, 12289, 300), (64, 12300, 1100),
+                                   (64, 12193, 4099), (64, 24576, 4096)])
+def test_mx_decode_packed_matches_fprop(M, D, C):
+    """MX FProp on the packed weight and scale words: the packing checked
+    byte for byte, the output bit for bit the row-major MX FProp."""
+    banner(f"mx decode packed M={M} D={D} C={C}")
+    rng = np.random.default_rng(M + 5 * D + C)
+    X = (rng.standard_normal((M, C)) * np.exp(rng.uniform(-3, 3, (M, C)))).astype(np.float32)
+    W = (rng.standard_normal((D, C)) * 0.02).astype(np.float32)
+    xq, xe, _, _ = fb.fp8_mx_quantize_1x32(dev_strided(X), colwise=False)
+    wq, we, _, _ = fb.fp8_mx_quantize_1x32(dev_strided(W), colwise=False)
+    wp, wep = fb.fp8_pack_decode_weight(wq, D, C, we=we)
+    np.testing.assert_array_equal(host(wep), packed_scale_words_ref(host(we), D, C))
+    for dt in (torch.float32, torch.bfloat16):
+        y_row = fb.fp8_mx_gemm_fprop(xq, xe, wq, we, M, D, C, out_dtype=dt)
+        y_dec = fb.fp8_mx_gemm_fprop_decode(xq, xe, wp, wep, M, D, C, out_dtype=dt)
+        assert torch.equal(y_dec, y_row), dt
