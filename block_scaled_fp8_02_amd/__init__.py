@@ -529,7 +529,10 @@ def fp8_gemm_fprop(xq, xs, wq, ws, N, D, C, y=None, out_dtype=torch.bfloat16):
     return y
 
 
-def fp8_gemm_dgrad(gq, gs, wqT, ws, N, D, C, dx=None, out_dtype=torch.bfloat16):
+def fp8_gemm_dgrad(gq, gs, wqT, ws, N, D, C, dx=None, out_dtype=torch.bfloat16, work=None):
+    """DGrad; for few rows and a long contraction it runs split along K with
+    `work` (dgrad_split_workspace's size) as the partial sums, a new
+    workspace when work is None."""
     dev = gq.device
     _need_gemm(dev, gq, gs, wqT, ws, N, C, D, "gq", "wqT", b_blocks=True)
     _need(ws, "ws", _cdiv(D, 128), _cdiv(C, 128), _F32, dev)
@@ -537,11 +540,11 @@ def fp8_gemm_dgrad(gq, gs, wqT, ws, N, D, C, dx=None, out_dtype=torch.bfloat16):
     _need(dx, "dx", N, C, _FLOAT_IO, dev)
     args = (_ptr(gq), _ld(gq), _ptr(gs), _ld(gs), _ptr(wqT), _ld(wqT), _ptr(ws), _ld(ws),
             _ptr(dx), _out_dtype_code(dx.dtype), _ld(dx), N, D, C)
-    work = dgrad_split_workspace(N, D, C, dev)
+    work = _split_work(work, N, D, C, dev)
     if work is None:
         _call("fp8_gemm_dgrad", *args, _stream(gq.device))
     else:
-        _call("fp8_gemm_dgrad_split", *args, _ptr(work), work.numel(), _stream(gq.device))
+        _call("fp8_gemm_dgrad_split", *args, _ptr(work), work.numel() * work.element_size(), _stream(gq.device))
     return dx
 
 
@@ -565,6 +568,22 @@ def dgrad_split_workspace(N: int, D: int, C: int, dev):
     with torch.cuda.device(dev):
         nbytes = lib().fp8_gemm_dgrad_split_bytes(N, D, C)
     return None if nbytes <= 0 else torch.empty((nbytes,), dtype=torch.uint8, device=dev)
+
+
+def _split_work(work, N, D, C, dev):
+    """The workspace a DGrad call uses: the caller's (checked against the
+    split's size; nothing is allocated, e.g. under stream capture) or a new
+    one from dgrad_split_workspace.  None when no split applies."""
+    if work is None:
+        return dgrad_split_workspace(N, D, C, dev)
+    with torch.cuda.device(dev):
+        nbytes = lib().fp8_gemm_dgrad_split_bytes(N, D, C)
+    if nbytes <= 0:
+        return None
+    if (not isinstance(work, torch.Tensor) or work.device != dev or not work.is_contiguous()
+            or work.numel() * work.element_size() < nbytes):
+        raise ValueError(f"work must be a contiguous tensor on {dev} of at least {nbytes} bytes")
+    return work
 
 
 def fp8_gemm_wgrad(gqT, gsT, xqT, xsT, N, D, C, dw=None, out_dtype=torch.bfloat16, beta: int = 0):
@@ -739,18 +758,21 @@ def fp8_mx_gemm_fprop_decode(xq, xe, wp, wep, N, D, C, y=None, out_dtype=torch.b
     return y
 
 
-def fp8_mx_gemm_dgrad(gq, ge, wqT, weT, N, D, C, dx=None, out_dtype=torch.bfloat16):
+def fp8_mx_gemm_dgrad(gq, ge, wqT, weT, N, D, C, dx=None, out_dtype=torch.bfloat16, work=None):
+    """DGrad; for few rows and a long contraction it runs split along K with
+    `work` (dgrad_split_workspace's size) as the partial sums, a new
+    workspace when work is None."""
     dev = gq.device
     _need_gemm(dev, gq, ge, wqT, weT, N, C, D, "gq", "wqT", mx=True)
     dx = _new_out(N, C, out_dtype, dev) if dx is None else dx
     _need(dx, "dx", N, C, _FLOAT_IO, dev)
     args = (_ptr(gq), _ld(gq), _ptr(ge), _ld(ge), _ptr(wqT), _ld(wqT), _ptr(weT), _ld(weT),
             _ptr(dx), _out_dtype_code(dx.dtype), _ld(dx), N, D, C)
-    work = dgrad_split_workspace(N, D, C, dev)
+    work = _split_work(work, N, D, C, dev)
     if work is None:
         _call("fp8_mx_gemm_dgrad", *args, _stream(gq.device))
     else:
-        _call("fp8_mx_gemm_dgrad_split", *args, _ptr(work), work.numel(), _stream(gq.device))
+        _call("fp8_mx_gemm_dgrad_split", *args, _ptr(work), work.numel() * work.element_size(), _stream(gq.device))
     return dx
 
 

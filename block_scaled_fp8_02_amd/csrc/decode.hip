@@ -9,8 +9,8 @@
 // of a row's block), its four results added into the fp32 accumulators with
 // one FMA each by fl32(s_x * s_w), in ascending K blocks; for MXFP8 one
 // scaled MFMA per block accumulating in the matrix core.  So every output is
-// bit for bit what the training-size kernel gives (the rollout forward stays
-// a subgraph of the training forward).
+// bit for bit what the training-size kernel gives: rollout computes exactly
+// the training forward's rows.
 //
 // Layout on the chip:
 //   * 96 weight rows per block (6 waves of 16): 24576 rows are 256 blocks,

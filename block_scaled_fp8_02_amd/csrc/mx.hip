@@ -100,21 +100,19 @@ __global__ __launch_bounds__(256) void k_mx_quant(const T* __restrict__ x, int64
     for (int j = 0; j < 8; ++j)
         *reinterpret_cast<uint2*>(tileT + (cg * 8 + j) * 128 + ((rg ^ cg) << 3)) = make_uint2(tlo[j], thi[j]);
     __syncthreads();
-    const int crow = t >> 1, h = t & 1;
-    const int64_t c = cb + crow;
-    if (c < cols) {
-        uint32_t wv[16];
+    // 8 lanes per code row, so that every store instruction writes 8 whole
+    // 128-byte rows: lane chunk ch holds logical 8-byte chunks 2ch and 2ch+1,
+    // stored at physical (2ch)^s and (2ch+1)^s, s = crow/8 (one aligned
+    // 16-byte pair, its halves swapped when s is odd).
+    const int ch = t & 7;
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            const int phys = (8 * h + i) ^ (crow >> 3);
-            const uint2 u = *reinterpret_cast<const uint2*>(tileT + crow * 128 + (phys << 3));
-            wv[2 * i] = u.x;
-            wv[2 * i + 1] = u.y;
-        }
-        uint8_t* dst = qT + c * ldqT + rb + 64 * h;
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-            *reinterpret_cast<uint4*>(dst + 16 * i) = make_uint4(wv[4 * i], wv[4 * i + 1], wv[4 * i + 2], wv[4 * i + 3]);
+    for (int i = 0; i < 4; ++i) {
+        const int crow = (t >> 3) + 32 * i;
+        const int s8 = crow >> 3;
+        const uint4 u = *reinterpret_cast<const uint4*>(tileT + crow * 128 + ((((2 * ch) ^ s8) & ~1) << 3));
+        const uint4 w = (s8 & 1) ? make_uint4(u.z, u.w, u.x, u.y) : u;
+        const int64_t c = cb + crow;
+        if (c < cols) *reinterpret_cast<uint4*>(qT + c * ldqT + rb + 16 * ch) = w;
     }
 }
 

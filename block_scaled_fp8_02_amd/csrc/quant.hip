@@ -448,22 +448,19 @@ __global__ __launch_bounds__(256, 2) void k_quant_tiles(QuantTileArgs A) {
         }
         lds_barrier();                                               // (3)
         if (want_qT) {
-            const int crow = t >> 1, h = t & 1;
-            const int64_t c = at.cb + crow;
-            if (c < A.cols) {
-                uint32_t wv[16];
+            // 8 lanes per code row: every store instruction writes 8 whole
+            // 128-byte rows.  Lane chunk ch holds logical 8-byte chunks 2ch and
+            // 2ch+1, stored at physical (2ch)^s and (2ch+1)^s, s = crow/8: one
+            // aligned 16-byte pair, its halves swapped when s is odd.
+            const int ch = t & 7;
 #pragma unroll
-                for (int i = 0; i < 8; ++i) {
-                    const int phys = (8 * h + i) ^ (crow >> 3);
-                    const uint2 u = *reinterpret_cast<const uint2*>(tileT + crow * 128 + (phys << 3));
-                    wv[2 * i] = u.x;
-                    wv[2 * i + 1] = u.y;
-                }
-                uint8_t* dst = A.qT + c * A.ldqT + at.pos + 64 * h;
-#pragma unroll
-                for (int i = 0; i < 4; ++i)
-                    *reinterpret_cast<uint4*>(dst + 16 * i) =
-                        make_uint4(wv[4 * i], wv[4 * i + 1], wv[4 * i + 2], wv[4 * i + 3]);
+            for (int i = 0; i < 4; ++i) {
+                const int crow = (t >> 3) + 32 * i;
+                const int s8 = crow >> 3;
+                const uint4 u = *reinterpret_cast<const uint4*>(tileT + crow * 128 + ((((2 * ch) ^ s8) & ~1) << 3));
+                const uint4 w = (s8 & 1) ? make_uint4(u.z, u.w, u.x, u.y) : u;
+                const int64_t c = at.cb + crow;
+                if (c < A.cols) *reinterpret_cast<uint4*>(A.qT + c * A.ldqT + at.pos + 16 * ch) = w;
             }
         }
         if (MODE != QT_WEIGHT && t == 0) scaled_flag = 0;   // every wave has read it (before barrier 3)

@@ -155,6 +155,11 @@ def test_dgrad_k_split(N, D, C):
     check_f32(host(dx), want, mag, "split dgrad f32")
     again = fb.fp8_gemm_dgrad(gq, gs, wqT, ws, N, D, C, out_dtype=f32)
     assert torch.equal(dx, again), "split dgrad is not repeatable"
+    # the caller's workspace (nothing allocated in the call), a short one refused
+    work = fb.dgrad_split_workspace(N, D, C, gq.device)
+    assert torch.equal(fb.fp8_gemm_dgrad(gq, gs, wqT, ws, N, D, C, out_dtype=f32, work=work), dx)
+    with pytest.raises(ValueError):
+        fb.fp8_gemm_dgrad(gq, gs, wqT, ws, N, D, C, out_dtype=f32, work=work[:-16])
     check(host(fb.fp8_gemm_dgrad(gq, gs, wqT, ws, N, D, C)), want, TOL, "split dgrad bf16")
     plain = fb._new_out(N, C, f32, gq.device)
     fb._call("fp8_gemm_dgrad", fb._ptr(gq), fb._ld(gq), fb._ptr(gs), fb._ld(gs), fb._ptr(wqT), fb._ld(wqT),
@@ -181,6 +186,8 @@ def test_mx_dgrad_k_split(N, D, C):
     check_f32(host(dx), want, mag, "mx split dgrad f32")
     again = fb.fp8_mx_gemm_dgrad(gq, ge, wqT, weT, N, D, C, out_dtype=torch.float32)
     assert torch.equal(dx, again), "mx split dgrad is not repeatable"
+    work = fb.dgrad_split_workspace(N, D, C, gq.device)
+    assert torch.equal(fb.fp8_mx_gemm_dgrad(gq, ge, wqT, weT, N, D, C, out_dtype=torch.float32, work=work), dx)
     check(host(fb.fp8_mx_gemm_dgrad(gq, ge, wqT, weT, N, D, C)), want, TOL, "mx split dgrad bf16")
 
 
@@ -286,8 +293,8 @@ def test_train_wgrad_full(train_full):
 
 def test_unified_forward_is_batch_invariant():
     """Rollout FProp of 64 tokens equals rows 0..63 of the training-size
-    FProp bit for bit, with the decode weight (Jet-RL: the inference graph
-    is a subgraph of the training forward graph)."""
+    FProp bit for bit, with the decode weight (Jet-RL notes, section 4.1:
+    rollout runs the training forward's own FP8 computation)."""
     w = wl.decode(0)
     rng = wl.rng_for(7)
     X = wl.normal(rng, (8192, 4096), 1.0)
