@@ -358,7 +358,14 @@ __global__ __launch_bounds__(64 * NW, 1) void k_gemm(GemmArgs g) {
                 const int64_t j = j0 + 8 * pp;
                 uint16_t* o = reinterpret_cast<uint16_t*>(Ob) + i * g.ldo + j;
                 if (full_cols) {
-                    *reinterpret_cast<uint4*>(o) = v;
+                    // streaming store: the output leaves L2 with the epilogue
+                    // instead of as dirty lines that the next kernel's traffic
+                    // must write back (measured: the quantizers that follow a
+                    // GEMM in the training step run 3-4 us faster)
+                    __builtin_nontemporal_store(v.x, reinterpret_cast<uint32_t*>(o));
+                    __builtin_nontemporal_store(v.y, reinterpret_cast<uint32_t*>(o) + 1);
+                    __builtin_nontemporal_store(v.z, reinterpret_cast<uint32_t*>(o) + 2);
+                    __builtin_nontemporal_store(v.w, reinterpret_cast<uint32_t*>(o) + 3);
                 } else {
                     const uint32_t w[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
