@@ -344,6 +344,38 @@ def test_decode_rows_kernel_ragged(M, D, C):
         assert torch.equal(y_m, y_big[:M]), dt
 
 
+@pytest.mark.parametrize("N,D,C", [(37, 300, 12300), (64, 1100, 12193), (1, 128, 16500)])
+def test_dgrad_on_decode_kernel(N, D, C):
+    """Few-row DGrad with a wide output and a contraction too short to split
+    runs on the weight-streaming decode kernel, which then reads the 128x128
+    weight scales transposed (K block along the grid's rows): fp32 output
+    against the oracle, both recipes."""
+    banner(f"dgrad on the decode kernel N={N} D={D} C={C}")
+    assert fb.lib().fp8_gemm_dgrad_split_bytes(N, D, C) == 0
+    rng = np.random.default_rng(N + D + C)
+    W = (rng.standard_normal((D, C)) * 0.02).astype(np.float32)
+    dY = (rng.standard_normal((N, D)) * np.exp(rng.uniform(-2, 2, (N, 1)))).astype(np.float32)
+    gq, gs = fb.fp8_quantize_act_1x128(dev_strided(dY))
+    wq, ws, wqT = fb.fp8_quantize_weight_128x128(dev_strided(W))
+    dx = host(fb.fp8_gemm_dgrad(gq, gs, wqT, ws, N, D, C, out_dtype=torch.float32))
+    ogq, ogs = oracle.quant_1x128(dY)
+    owq, ows, _ = oracle.quant_128x128(W, with_transpose=False)
+    mag = oracle.matmul_f64(np.abs(oracle.deq_rowgroups(ogq, ogs, D)), np.abs(oracle.deq_128x128(owq, ows, D, C)))
+    check_f32(dx, oracle.dgrad(ogq, ogs, owq, ows, D, C), mag, "dgrad decode kernel f32")
+    # MX: the row-wise E8M0 of W^T
+    mgq, mge, _, _ = fb.fp8_mx_quantize_1x32(dev_strided(dY), colwise=False)
+    _, _, mwqT, mweT = fb.fp8_mx_quantize_1x32(dev_strided(W), rowwise=False)
+    mdx = host(fb.fp8_mx_gemm_dgrad(mgq, mge, mwqT, mweT, N, D, C, out_dtype=torch.float32))
+    oq, oe = oracle.mx_quant_rows(dY)
+    owqT, oweT = oracle.mx_quant_cols(W)
+    ref = oracle.mx_gemm(oq, oe, owqT, oweT, D)
+    mmag = oracle.matmul_f64(np.abs(oracle.deq_mx(oq, oe, D)), np.abs(oracle.deq_mx(owqT, oweT, D)).T)
+    err = oracle.rel_row_error(mdx, ref)
+    ratio = float(np.max(np.abs(mdx - ref) / np.maximum(mmag, 1e-300)))
+    banner(f"mx dgrad decode kernel: {err:.3e}, |err|/sum|ab| {ratio:.3e}")
+    assert err <= TOL and ratio <= ACC_BOUND
+
+
 def packed_codes_ref(wq_host, D, C):
     """Decode layout of row-major codes, written out with numpy: per group
     of 16 rows and K block, half h holds chunks q + 4h of rows r at lane
