@@ -736,6 +736,37 @@ def other_workloads(torch, fb, wl, dev, seed):
         step()
     dec["step_graph"] = report(time_cold(torch, graph.replay, flush), step_bytes, 2.0 * N * D * C)
     del graph
+    # a chain of 16 rollout steps over four copies of the packed weight (403 MB,
+    # more than the Infinity Cache holds, so each step reads its weight from
+    # HBM): eager launches, one HIP graph replay of all 32 kernels, and the
+    # packed FProp alone back-to-back; times per step
+    nch = 16
+    wps = [wp] + [wp.clone() for _ in range(3)]
+
+    def chain():
+        for i in range(nch):
+            fb.fp8_quantize_act_1x128(X, xq, xs)
+            fb.fp8_gemm_fprop_decode(xq, xs, wps[i % 4], ws, N, D, C, y=y)
+
+    def fprops():
+        for i in range(nch):
+            fb.fp8_gemm_fprop_decode(xq, xs, wps[i % 4], ws, N, D, C, y=y)
+    dec["step_chain16_eager"] = report(time_cold(torch, chain, flush, reps=20) / nch, step_bytes, 2.0 * N * D * C)
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        chain()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        chain()
+    dec["step_chain16_graph"] = report(time_cold(torch, graph.replay, flush, reps=20) / nch, step_bytes,
+                                       2.0 * N * D * C)
+    del graph
+    dec["fprop_packed_back_to_back"] = report(
+        time_cold(torch, fprops, flush, reps=20) / nch,
+        N * C + D * C + N * cd(C, 128) * 4 + cd(D, 128) * cd(C, 128) * 4 + N * D * 2, 2.0 * N * D * C)
+    del wps
     # the backward GEMMs of the same 64-token layer on the 1x128 / 128x128
     # path (the MXFP8 section below times the same three GEMMs): DGrad with
     # dY [64 x 24576] quantized along D (split along K, 64 rows), WGrad with
