@@ -191,7 +191,12 @@ struct TileAt {
 // tile, 76 us with 32).
 constexpr int64_t QT_BAND = 1;
 
-__device__ __forceinline__ TileAt locate_tile(const QuantTileArgs& A, int64_t k, SegPos& cur) {
+// Experts whose offsets a grouped tile quantizer keeps in LDS (more: read
+// from global memory).
+constexpr int QT_MAX_OFFS = 1025;
+
+// offs: the experts' offsets (A.offsets, or the block's LDS copy of them).
+__device__ __forceinline__ TileAt locate_tile(const QuantTileArgs& A, const int32_t* offs, int64_t k, SegPos& cur) {
     TileAt at;
     at.valid = k < A.tiles;
     const int64_t nr = A.tiles / A.col_tiles;                     // row tiles (grouped: an upper bound)
@@ -214,16 +219,16 @@ __device__ __forceinline__ TileAt locate_tile(const QuantTileArgs& A, int64_t k,
     }
     // a block's row-tile index normally only grows; search afresh if not
     if (at.rt < cur.first) cur = SegPos{0, 0, 0};
-    cur = wave_find_tile(A.offsets, A.E, at.rt, 128, cur);
+    cur = wave_find_tile(offs, A.E, at.rt, 128, cur);
     at.valid = cur.e < A.E;
     if (!at.valid) {                                               // past the experts' last tile
         cur = SegPos{0, 0, 0};
         at.a = at.b = at.pos = 0;
         return at;
     }
-    const int64_t hi = A.offsets[cur.e + 1];
+    const int64_t hi = offs[cur.e + 1];
     const int64_t g = at.rt - cur.first;
-    at.a = A.offsets[cur.e] + 128 * g;
+    at.a = offs[cur.e] + 128 * g;
     at.b = at.a + 128 < hi ? at.a + 128 : hi;
     at.pos = cur.P + 128 * g;
     return at;
@@ -321,20 +326,29 @@ __global__ __launch_bounds__(256, 2) void k_quant_tiles(QuantTileArgs A) {
     const bool want_qT = MODE != QT_WEIGHT || A.qT != nullptr;
     if (t == 0) scaled_flag = 0;
 
+    // grouped: the experts' offsets, read once into LDS (each tile's expert
+    // search then reads LDS instead of global memory)
+    __shared__ int32_t soffs[QT_MAX_OFFS];
+    const int32_t* offs = A.offsets;
+    if (A.offsets != nullptr && A.E < QT_MAX_OFFS) {
+        for (int64_t i = t; i <= A.E; i += 256) soffs[i] = A.offsets[i];
+        offs = soffs;
+        lds_barrier();
+    }
+
     SegPos cur{0, 0, 0};
     int64_t k = blockIdx.x;
-    TileAt at = locate_tile(A, k, cur);
+    TileAt at = locate_tile(A, offs, k, cur);
     RawTile<T> raw;
     if (at.valid) load_tile(A, at, rg, cg, raw);
     lds_barrier();
 
     for (; k < A.tiles; k += gridDim.x) {
-        const TileAt nx = locate_tile(A, k + gridDim.x, cur);
-        if (!at.valid) {                                           // (grouped) a tile past an expert's end
-            if (nx.valid) load_tile(A, nx, rg, cg, raw);
-            at = nx;
-            continue;
-        }
+        // grouped: the experts' row tiles are numbered without gaps, so the
+        // first tile past the last expert ends the block's work (the launch
+        // sizes the slots for the worst case)
+        if (!at.valid) break;                                      // uniform
+        const TileAt nx = locate_tile(A, offs, k + gridDim.x, cur);
         TileVals<T> v;
         v.set(raw);
         if (nx.valid) load_tile(A, nx, rg, cg, raw);            // next tile, while this one is quantized
