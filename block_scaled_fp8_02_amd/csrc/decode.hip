@@ -24,9 +24,9 @@
 //     q+4).  Row-major, one load covers 64 bytes of 16 rows 4 KB apart; in
 //     the decode layout it covers 1 KB of consecutive bytes and a wave reads
 //     its 16 rows as one linear 64 KB stream, which HBM serves markedly
-//     faster (measured on this workload: 16 x 64-byte pieces per load reach
-//     4.5 TB/s, 1 KB runs 5.4 TB/s).  MX scale words are packed the same
-//     way, 16 rows of a K block in one 64-byte run;
+//     faster (measured reading a 24576 x 4096 weight: 16 x 64-byte pieces
+//     per load reach 4.5 TB/s, 1 KB runs 5.4 TB/s).  MX scale words are
+//     packed the same way, 16 rows of a K block in one 64-byte run;
 //   * the tokens' codes and scales go through LDS in chunks of 4 K blocks
 //     (32 KB, three buffers), copied global->LDS two chunks ahead by a
 //     seventh, producer wave with a wait counter of its own; the six weight
