@@ -659,17 +659,18 @@ static hipError_t launch_cfg(const GemmArgs& args, hipStream_t st) {
 
 template <int SM>
 static hipError_t launch_sm(const GemmArgs& a, hipStream_t st) {
-    // Few rows (decode, M <= 64): the weight stream dominates.  A large
-    // weight takes 128-row tiles (8 waves of 64x16, 4 stages): each block
-    // re-reads the 64-row activation from L2 once per 128 weight rows, and
-    // the L2 traffic that saves outweighs the idle compute units (64x24576x4096:
-    // 34 us against 38 us with 32-row tiles, the MX form 36 against 42).
-    // Smaller weights keep narrow tiles (32 or 16 rows) to spread over at
-    // least one block per compute unit, with 4 or 8 stages in flight.  The
-    // per-element arithmetic is the same in every configuration.
+    // Few rows (decode, M <= 64): the weight stream dominates.  A weight of
+    // at least 128 groups of 96 rows (block or MX scales, no accumulation)
+    // streams through registers, 96 rows per block (decode.hip; 64x24576x4096
+    // in 28 us against 29 us on the 128-row tiles below).  Otherwise 128-row
+    // tiles (8 waves of 64x16, 4 stages) for the K-split DGrad and wide
+    // weights: each block re-reads the 64-row activation from L2 once per 128
+    // weight rows, and the L2 traffic that saves outweighs idle compute units
+    // (64x24576x4096: 34 us against 38 us with 32-row tiles).  Smaller weights
+    // keep narrow tiles (32 or 16 rows) to spread over at least one block per
+    // compute unit, with 4 or 8 stages in flight.  The per-element arithmetic
+    // is the same in every configuration.
     if (a.M <= 64 && a.group_mode == GROUP_NONE) {
-        // a weight of at least 128 x 96 rows: streamed through registers,
-        // 96 rows per block (decode.hip)
         if (rows96_applies(a)) return launch_gemm_rows96(a, st);
         // K split into ranges (few-row DGrad, where the output has too few
         // tiles to occupy the chip): 128-row weight tiles as for a large weight
