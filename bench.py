@@ -399,6 +399,28 @@ def main():
     del src, dst
     for n in ("quant_weight", "quant_dual_X", "quant_dual_dY"):
         kernels[n]["frac_measured_copy"] = round(kernels[n]["gbs"] / copy_gbs, 4)
+    # the same copy at each quantizer's own size (half its algorithmic bytes
+    # read, half written), rotating over six sources so that none is in the
+    # Infinity Cache: the ceiling a kernel of that size meets, ramp included
+    same = {}
+    for n in ("quant_weight", "quant_dual_X", "quant_dual_dY"):
+        nel = kernels[n]["alg_bytes"] // 8
+        srcs = [torch.empty(nel, dtype=torch.float32, device=dev).fill_(1.0) for _ in range(6)]
+        dst = torch.empty(nel, dtype=torch.float32, device=dev)
+        for i in range(6):
+            dst.copy_(srcs[i])
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for i in range(30):
+            dst.copy_(srcs[i % 6])
+        e1.record()
+        torch.cuda.synchronize()
+        gbs = 2 * nel * 4 / (e0.elapsed_time(e1) * 1e-3 / 30) / 1e9
+        same[n] = round(gbs, 1)
+        kernels[n]["frac_same_size_copy"] = round(kernels[n]["gbs"] / gbs, 4)
+        del srcs, dst
+    ceil["hbm_copy_gbs_same_size"] = same
     one = torch.ones((), device=dev)
     f8 = lambda t: t.view(torch.float8_e4m3fn)
     tw = {}
