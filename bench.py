@@ -353,8 +353,9 @@ def main():
         "dgrad": lambda: fb.fp8_gemm_dgrad(b["gq"], b["gs"], b["wqT"], b["ws"], N, D, C, dx=b["dx"]),
         "wgrad": lambda: fb.fp8_gemm_wgrad(b["gqT"], b["gsT"], b["xqT"], b["xsT"], N, D, C, dw=b["dw"]),
     }
-    for n, fn in warm_fns.items():
-        kernels[n]["us_warm"] = round(time_warm(torch, fn) * 1e6, 2)
+    if not args.no_other:                        # a side measurement, like the other sections
+        for n, fn in warm_fns.items():
+            kernels[n]["us_warm"] = round(time_warm(torch, fn) * 1e6, 2)
 
     dom = max(("fprop", "dgrad", "wgrad"), key=lambda n: kernels[n]["us"])
     t_dom = kernels[dom]["us"] * 1e-6
