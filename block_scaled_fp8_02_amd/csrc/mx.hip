@@ -27,7 +27,12 @@ __global__ __launch_bounds__(256) void k_mx_quant(const T* __restrict__ x, int64
                                                   uint8_t* __restrict__ qT, int64_t ldqT,
                                                   uint8_t* __restrict__ eT, int64_t ldeT) {
     __shared__ __attribute__((aligned(16))) uint8_t tileT[128 * 128];
+    __shared__ uint8_t ebT[4][128];                                   // column E8M0 bytes per 32-row block
     const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+    // E8M0 bytes leave four at a time (one 128-wide tile's four 32-blocks)
+    // where the buffers allow 4-byte stores
+    const bool e_words = e != nullptr && reinterpret_cast<uintptr_t>(e) % 4 == 0 && lde % 4 == 0;
+    const bool eT_words = eT != nullptr && reinterpret_cast<uintptr_t>(eT) % 4 == 0 && ldeT % 4 == 0;
     const int rg = t >> 4, cg = t & 15;
     // consecutive blocks walk along a row of tiles: the tiles in flight at
     // one time read whole input rows and write whole code rows
@@ -55,11 +60,17 @@ __global__ __launch_bounds__(256) void k_mx_quant(const T* __restrict__ x, int64
             m = fmaxf(m, __shfl_xor(m, 2));
             const int k = mx_exponent(m);
             const int64_t r = r0 + p;
+            // the row's four E8M0 bytes of this tile (lanes cg = 0, 4, 8, 12)
+            // go out as one word from lane cg = 0
+            const uint32_t b = (uint32_t)(c0 < cols ? k + 127 : 127);
+            const uint32_t b1 = __shfl_down(b, 4, 16), b2 = __shfl_down(b, 8, 16), b3 = __shfl_down(b, 12, 16);
             if (r < rows) {
                 *reinterpret_cast<uint2*>(q + r * ldq + c0) = make_uint2(mx_encode4(&v[p][0], k), mx_encode4(&v[p][4], k));
-                if ((cg & 3) == 0) {
-                    const int64_t blk = c0 / 32;
-                    e[r * lde + blk] = (uint8_t)(c0 < cols ? k + 127 : 127);
+                if (e_words) {
+                    if (cg == 0)
+                        *reinterpret_cast<uint32_t*>(e + r * lde + cb / 32) = b | (b1 << 8) | (b2 << 16) | (b3 << 24);
+                } else if ((cg & 3) == 0) {
+                    e[r * lde + c0 / 32] = (uint8_t)b;
                 }
             }
         }
@@ -82,8 +93,13 @@ __global__ __launch_bounds__(256) void k_mx_quant(const T* __restrict__ x, int64
         const bool padblk = rb + 32 * wave >= rows;
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
-            const int64_t c = c0 + j;
-            if (c < cols) eT[c * ldeT + rblk] = (uint8_t)(padblk ? 127 : kc[j] + 127);
+            const uint8_t bt = (uint8_t)(padblk ? 127 : kc[j] + 127);
+            if (eT_words) {
+                ebT[wave][cg * 8 + j] = bt;                           // the column's word leaves after the barrier
+            } else {
+                const int64_t c = c0 + j;
+                if (c < cols) eT[c * ldeT + rblk] = bt;
+            }
         }
     }
     uint32_t lo[8], hi[8];
@@ -100,6 +116,9 @@ __global__ __launch_bounds__(256) void k_mx_quant(const T* __restrict__ x, int64
     for (int j = 0; j < 8; ++j)
         *reinterpret_cast<uint2*>(tileT + (cg * 8 + j) * 128 + ((rg ^ cg) << 3)) = make_uint2(tlo[j], thi[j]);
     __syncthreads();
+    if (eT_words && t < 128 && cb + t < cols)
+        *reinterpret_cast<uint32_t*>(eT + (cb + t) * ldeT + rb / 32) =
+            (uint32_t)ebT[0][t] | ((uint32_t)ebT[1][t] << 8) | ((uint32_t)ebT[2][t] << 16) | ((uint32_t)ebT[3][t] << 24);
     // 8 lanes per code row, so that every store instruction writes 8 whole
     // 128-byte rows: lane chunk ch holds logical 8-byte chunks 2ch and 2ch+1,
     // stored at physical (2ch)^s and (2ch+1)^s, s = crow/8 (one aligned

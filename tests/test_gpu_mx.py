@@ -34,6 +34,29 @@ def test_mx_quant_ragged(shape):
     check_mx_quant(wl.f32_to_bf16_bits(x))
 
 
+@pytest.mark.parametrize("shape", [(129, 300), (64, 4096)])
+def test_mx_quant_odd_scale_strides(shape):
+    """E8M0 rows whose stride is not a multiple of 4 bytes: the quantizer
+    stores those scales byte by byte (4-byte rows take one word per tile);
+    both orientations bit-exact against the oracle."""
+    rows, cols = shape
+    banner(f"mx quant, odd E8M0 strides {shape}")
+    rng = np.random.default_rng(rows + cols)
+    x = (rng.standard_normal(shape) * np.exp(rng.uniform(-4, 4, shape))).astype(np.float32)
+    kb, kbT = -(-cols // 128) * 4, -(-rows // 128) * 4
+    q = torch.empty((rows, -(-cols // 128) * 128), dtype=torch.uint8, device="cuda")
+    qT = torch.empty((cols, -(-rows // 128) * 128), dtype=torch.uint8, device="cuda")
+    e = torch.empty((rows, kb + 1), dtype=torch.uint8, device="cuda")[:, :kb]
+    eT = torch.empty((cols, kbT + 3), dtype=torch.uint8, device="cuda")[:, :kbT]
+    fb.fp8_mx_quantize_1x32(dev_strided(x), q=q, e=e, qT=qT, eT=eT)
+    oq, oe = oracle.mx_quant_rows(x)
+    oqT, oeT = oracle.mx_quant_cols(x)
+    assert_bytes_equal(host(q), oq, "mx row codes")
+    assert_bytes_equal(host(e), oe, "mx row scales (odd stride)")
+    assert_bytes_equal(host(qT), oqT, "mx col codes")
+    assert_bytes_equal(host(eT), oeT, "mx col scales (odd stride)")
+
+
 def test_mx_quant_classes():
     x = np.zeros((64, 256), np.float32)
     x[1] = np.finfo(np.float32).max
