@@ -1,0 +1,109 @@
+"""A seeded sweep of random small shapes through every quantizer and the
+three GEMMs, against the oracle: codes and scales bit for bit (1x128 rows,
+128x128 weight blocks with the transposed codes, the token-axis dual
+quantizer, MXFP8 in both orientations), GEMM fp32 outputs within the row-norm
+tolerance and the fp8 accumulation bound.  The accumulation bound holds for
+every output; the row-norm tolerance is checked where a row has at least 16
+outputs: with fewer, the row norm can be a single sum that these inputs
+cancel to a fraction of a percent of its sum |a_k b_k|, and a relative
+error of that one sum measures the cancellation, not the GEMM (measured with
+element-wise magnitudes over three decades: D = 1, C = 292, worst row 0.23%
+of its sum |a_k b_k|, error 1.3e-5 of it).
+Shapes mix sizes below, at and
+just past the 32-, 128- and 256-element boundaries; activations and
+gradients are Gaussian rows whose magnitudes spread over three decades, with
+outlier channels, as in the workloads."""
+import numpy as np
+import pytest
+import torch
+
+import block_scaled_fp8_02_amd as fb
+import oracle
+from gpu_util import TOL, assert_bytes_equal, assert_scales_equal, banner, dev_strided, host
+
+pytestmark = pytest.mark.gpu
+
+# Element bound for fp32 outputs: 2^-11 * sum_k |a_k b_k|.  The fp8 MFMA sums
+# each 128-wide block with a narrower internal precision than fp32; with
+# outlier channels (x50) sharing a block with ordinary values its error on one
+# block was measured at up to 2.8e-4 of sum |a_k b_k| (DGrad, D = 33: a single
+# partial block), above the 2^-12 that inputs without outliers stay within.
+ACC_BOUND = 2.0 ** -11
+EDGES = [1, 2, 31, 32, 33, 127, 128, 129, 255, 256, 257]
+
+
+def _shapes(seed: int, n: int):
+    rng = np.random.default_rng(seed)
+    out = []
+    for _ in range(n):
+        dims = [int(rng.choice(EDGES)) if rng.random() < 0.5 else int(rng.integers(1, 300)) for _ in range(3)]
+        out.append(tuple(dims))
+    return out
+
+
+SHAPES = _shapes(2024, 16)
+
+
+def _data(rng, shape, spread=3.0):
+    """Gaussian rows with magnitudes spread over three decades, and 1% of
+    the columns (at least one) scaled x50, as the workloads' outlier
+    channels."""
+    rows, cols = shape
+    x = rng.standard_normal(shape) * np.exp(rng.uniform(-spread, spread, (rows, 1)))
+    hot = rng.choice(cols, max(1, round(0.01 * cols)), replace=False)
+    x[:, hot] *= 50.0
+    return x.astype(np.float32)
+
+
+@pytest.mark.parametrize("N,D,C", SHAPES)
+def test_random_shape_quantizers_and_gemms(N, D, C):
+    banner(f"random shape N={N} D={D} C={C}")
+    rng = np.random.default_rng(N * 1000003 + D * 1009 + C)
+    X = _data(rng, (N, C))
+    W = (rng.standard_normal((D, C)) * 0.02).astype(np.float32)
+    dY = (_data(rng, (N, D)) * 1e-3).astype(np.float32)
+    xd, wd, gd = dev_strided(X), dev_strided(W), dev_strided(dY)
+
+    # quantizers
+    xqT, xsT, xq, xs = fb.fp8_quantize_transposed(xd, rowwise=True)
+    wq, ws, wqT = fb.fp8_quantize_weight_128x128(wd)
+    gq, gs = fb.fp8_quantize_act_1x128(gd)
+    gqT, gsT, _, _ = fb.fp8_quantize_transposed(gd)
+    oxq, oxs = oracle.quant_1x128(X)
+    oxqT, oxsT = oracle.quant_colwise(X)
+    owq, ows, owqT = oracle.quant_128x128(W)
+    ogq, ogs = oracle.quant_1x128(dY)
+    ogqT, ogsT = oracle.quant_colwise(dY)
+    for got, want, what in ((xq, oxq, "X codes"), (xqT, oxqT, "X^T codes"), (wq, owq, "W codes"),
+                            (wqT, owqT, "W^T codes"), (gq, ogq, "dY codes"), (gqT, ogqT, "dY^T codes")):
+        assert_bytes_equal(host(got), want, what)
+    for got, want, what in ((xs, oxs, "X scales"), (xsT, oxsT, "X^T scales"), (ws, ows, "W scales"),
+                            (gs, ogs, "dY scales"), (gsT, ogsT, "dY^T scales")):
+        assert_scales_equal(host(got), want, what)
+    mq, me, mqT, meT = fb.fp8_mx_quantize_1x32(xd)
+    omq, ome = oracle.mx_quant_rows(X)
+    omqT, omeT = oracle.mx_quant_cols(X)
+    for got, want, what in ((mq, omq, "MX codes"), (me, ome, "MX E8M0"), (mqT, omqT, "MX^T codes"),
+                            (meT, omeT, "MX^T E8M0")):
+        assert_bytes_equal(host(got), want, what)
+
+    # GEMMs, fp32 outputs
+    f32 = torch.float32
+    y = host(fb.fp8_gemm_fprop(xq, xs, wq, ws, N, D, C, out_dtype=f32))
+    dx = host(fb.fp8_gemm_dgrad(gq, gs, wqT, ws, N, D, C, out_dtype=f32))
+    dw = host(fb.fp8_gemm_wgrad(gqT, gsT, xqT, xsT, N, D, C, out_dtype=f32))
+    Xa = np.abs(oracle.deq_rowgroups(oxq, oxs, C))
+    Wa = np.abs(oracle.deq_128x128(owq, ows, D, C))
+    Ga = np.abs(oracle.deq_rowgroups(ogq, ogs, D))
+    K = ogqT.shape[1]
+    GTa = np.abs(oracle.deq_rowgroups(ogqT, ogsT, K))
+    XTa = np.abs(oracle.deq_rowgroups(oxqT, oxsT, K))
+    for got, want, mag, what in (
+            (y, oracle.fprop(oxq, oxs, owq, ows, C), oracle.matmul_f64(Xa, Wa.T), "fprop"),
+            (dx, oracle.dgrad(ogq, ogs, owq, ows, D, C), oracle.matmul_f64(Ga, Wa), "dgrad"),
+            (dw, oracle.wgrad(ogqT, ogsT, oxqT, oxsT, K), oracle.matmul_f64(GTa, XTa.T), "wgrad")):
+        ratio = float(np.max(np.abs(got - want) / np.maximum(mag, 1e-300)))
+        assert ratio <= ACC_BOUND, (what, ratio)
+        if got.shape[1] >= 16:
+            err = oracle.rel_row_error(got, want)
+            assert err <= TOL, (what, err)
