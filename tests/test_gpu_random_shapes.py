@@ -107,3 +107,97 @@ def test_random_shape_quantizers_and_gemms(N, D, C):
         if got.shape[1] >= 16:
             err = oracle.rel_row_error(got, want)
             assert err <= TOL, (what, err)
+
+
+def _check_gemm(got, want, mag, what):
+    ratio = float(np.max(np.abs(got - want) / np.maximum(mag, 1e-300))) if got.size else 0.0
+    assert ratio <= ACC_BOUND, (what, ratio)
+    if got.ndim == 2 and got.shape[1] >= 16:
+        err = oracle.rel_row_error(got, want)
+        assert err <= TOL, (what, err)
+
+
+@pytest.mark.parametrize("N,D,C", SHAPES)
+def test_random_shape_mx_gemms(N, D, C):
+    """The MXFP8 GEMMs on the same shapes (E8M0 scales on the scaled MFMA)."""
+    banner(f"random shape MX N={N} D={D} C={C}")
+    rng = np.random.default_rng(N * 7919 + D * 31 + C)
+    X = _data(rng, (N, C))
+    W = (rng.standard_normal((D, C)) * 0.02).astype(np.float32)
+    dY = (_data(rng, (N, D)) * 1e-3).astype(np.float32)
+    xq, xe, xqT, xeT = fb.fp8_mx_quantize_1x32(dev_strided(X))
+    wq, we, wqT, weT = fb.fp8_mx_quantize_1x32(dev_strided(W))
+    gq, ge, gqT, geT = fb.fp8_mx_quantize_1x32(dev_strided(dY))
+    f32 = torch.float32
+    y = host(fb.fp8_mx_gemm_fprop(xq, xe, wq, we, N, D, C, out_dtype=f32))
+    dx = host(fb.fp8_mx_gemm_dgrad(gq, ge, wqT, weT, N, D, C, out_dtype=f32))
+    dw = host(fb.fp8_mx_gemm_wgrad(gqT, geT, xqT, xeT, N, D, C, out_dtype=f32))
+    o = {k: oracle.mx_quant_rows(v) for k, v in (("x", X), ("w", W), ("g", dY))}
+    oT = {k: oracle.mx_quant_cols(v) for k, v in (("x", X), ("w", W), ("g", dY))}
+    a = lambda q, e, k: np.abs(oracle.deq_mx(q, e, k))
+    _check_gemm(y, oracle.mx_gemm(*o["x"], *o["w"], C), oracle.matmul_f64(a(*o["x"], C), a(*o["w"], C).T), "mx fprop")
+    _check_gemm(dx, oracle.mx_gemm(*o["g"], *oT["w"], D),
+                oracle.matmul_f64(a(*o["g"], D), a(*oT["w"], D).T), "mx dgrad")
+    _check_gemm(dw, oracle.mx_gemm(*oT["g"], *oT["x"], N),
+                oracle.matmul_f64(a(*oT["g"], N), a(*oT["x"], N).T), "mx wgrad")
+
+
+def _routing(seed: int):
+    rng = np.random.default_rng(seed)
+    E = int(rng.integers(1, 13))
+    sizes = [int(rng.choice([0, 1, 127, 128, 129])) if rng.random() < 0.4 else int(rng.integers(0, 300))
+             for _ in range(E)]
+    offs = np.concatenate([[0], np.cumsum(sizes)]).astype(np.int32)
+    H = int(rng.choice(EDGES)) if rng.random() < 0.5 else int(rng.integers(1, 300))
+    Dn = int(rng.choice([128, 256]))
+    return offs, H, Dn
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_random_grouped_layer(seed):
+    """Grouped (MoE) quantization and GEMMs on random routings: 1 to 12
+    experts, empty, one-row and 128-boundary experts, ragged hidden sizes;
+    the token-axis codes and scales bit for bit, every expert's GEMMs
+    against the oracle on that expert's rows."""
+    offs, H, Dn = _routing(seed)
+    E, R = len(offs) - 1, int(offs[-1])
+    banner(f"random grouped layer seed={seed} E={E} rows={R} H={H} Dn={Dn}")
+    if R == 0:
+        pytest.skip("routing with no rows")
+    rng = np.random.default_rng(1000 + seed)
+    X = _data(rng, (R, H))
+    dY = (_data(rng, (R, Dn)) * 1e-3).astype(np.float32)
+    Ws = (rng.standard_normal((E, Dn, H)) * 0.02).astype(np.float32)
+    od = torch.from_numpy(offs).to("cuda")
+    xqT, xsT, xq, xs = fb.fp8_quantize_transposed_grouped(dev_strided(X), od, rowwise=True)
+    gqT, gsT, gq, gs = fb.fp8_quantize_transposed_grouped(dev_strided(dY), od, rowwise=True)
+    oqT, osT = oracle.quant_colwise(X, offs)
+    P = oqT.shape[1]
+    assert_bytes_equal(host(xqT)[:, :P], oqT, "grouped X^T codes")
+    assert_scales_equal(host(xsT)[:, :P // 128], osT, "grouped X^T scales")
+    wq, ws, wqT = fb.fp8_quantize_weight_128x128(dev_strided(Ws.reshape(E * Dn, H)))
+    f32 = torch.float32
+    nbs = Dn // 128
+    y = host(fb.fp8_gemm_fprop_grouped(xq, xs, wq, Dn * wq.stride(0), ws, nbs * ws.stride(0), od, R, Dn, H,
+                                       out_dtype=f32))
+    dx = host(fb.fp8_gemm_dgrad_grouped(gq, gs, wqT, Dn, ws, nbs * ws.stride(0), od, R, Dn, H, out_dtype=f32))
+    dw = host(fb.fp8_gemm_wgrad_grouped(gqT, gsT, xqT, xsT, od, R, Dn, H, out_dtype=f32))
+    for e in range(E):
+        a, b = int(offs[e]), int(offs[e + 1])
+        if a == b:
+            assert np.all(dw[e] == 0), f"empty expert {e}"
+            continue
+        oxq, oxs = oracle.quant_1x128(X[a:b])
+        owq, ows, _ = oracle.quant_128x128(Ws[e], with_transpose=False)
+        ogq, ogs = oracle.quant_1x128(dY[a:b])
+        ogqT, ogsT = oracle.quant_colwise(dY[a:b])
+        oxqT, oxsT = oracle.quant_colwise(X[a:b])
+        K = ogqT.shape[1]
+        Xa = np.abs(oracle.deq_rowgroups(oxq, oxs, H))
+        Wa = np.abs(oracle.deq_128x128(owq, ows, Dn, H))
+        Ga = np.abs(oracle.deq_rowgroups(ogq, ogs, Dn))
+        GTa = np.abs(oracle.deq_rowgroups(ogqT, ogsT, K))
+        XTa = np.abs(oracle.deq_rowgroups(oxqT, oxsT, K))
+        _check_gemm(y[a:b], oracle.fprop(oxq, oxs, owq, ows, H), oracle.matmul_f64(Xa, Wa.T), f"e{e} fprop")
+        _check_gemm(dx[a:b], oracle.dgrad(ogq, ogs, owq, ows, Dn, H), oracle.matmul_f64(Ga, Wa), f"e{e} dgrad")
+        _check_gemm(dw[e], oracle.wgrad(ogqT, ogsT, oxqT, oxsT, K), oracle.matmul_f64(GTa, XTa.T), f"e{e} wgrad")
