@@ -201,3 +201,45 @@ def test_random_grouped_layer(seed):
         _check_gemm(y[a:b], oracle.fprop(oxq, oxs, owq, ows, H), oracle.matmul_f64(Xa, Wa.T), f"e{e} fprop")
         _check_gemm(dx[a:b], oracle.dgrad(ogq, ogs, owq, ows, Dn, H), oracle.matmul_f64(Ga, Wa), f"e{e} dgrad")
         _check_gemm(dw[e], oracle.wgrad(ogqT, ogsT, oxqT, oxsT, K), oracle.matmul_f64(GTa, XTa.T), f"e{e} wgrad")
+
+
+@pytest.mark.parametrize("N,D,C", SHAPES)
+def test_random_shape_variants(N, D, C):
+    """The variants on the same shapes: power-of-two scales (codes, scales
+    and E8M0 bytes bit for bit), the token-axis requantization of the saved
+    1x128 copy (bit for bit), and, for at most 64 tokens, FProp on the packed
+    decode weight (bit for bit the row-major FProp, both recipes)."""
+    banner(f"random shape variants N={N} D={D} C={C}")
+    rng = np.random.default_rng(N * 104729 + D * 7 + C)
+    X = _data(rng, (N, C))
+    W = (rng.standard_normal((D, C)) * 0.02).astype(np.float32)
+    xd, wd = dev_strided(X), dev_strided(W)
+    # power-of-two scales
+    pq, ps, pe = fb.fp8_quantize_act_1x128_pow2(xd)
+    oq, os_ = oracle.quant_1x128(X, pow2=True)
+    assert_bytes_equal(host(pq), oq, "pow2 codes")
+    assert_scales_equal(host(ps), os_, "pow2 scales")
+    assert_bytes_equal(host(pe), np.repeat(oracle.e8m0_of_pow2(os_), 4, axis=1), "pow2 E8M0")
+    pqT, psT, _, _, _, _ = fb.fp8_quantize_transposed_pow2(xd, rowwise=False, e8=False)
+    oqT, osT = oracle.quant_colwise(X, pow2=True)
+    assert_bytes_equal(host(pqT), oqT, "pow2 token-axis codes")
+    assert_scales_equal(host(psT), osT, "pow2 token-axis scales")
+    # requantization of the saved row-wise copy
+    xq, xs = fb.fp8_quantize_act_1x128(xd)
+    rqT, rsT = fb.fp8_requantize_transposed(xq, xs, C)
+    ox, oxs = oracle.quant_1x128(X)
+    orqT, orsT = oracle.requant_colwise(ox, oxs, C)
+    assert_bytes_equal(host(rqT), orqT, "requantized codes")
+    assert_scales_equal(host(rsT), orsT, "requantized scales")
+    # rollout decode on the packed weight
+    if N <= 64:
+        wq, ws, _ = fb.fp8_quantize_weight_128x128(wd, transpose=False)
+        wp, _ = fb.fp8_pack_decode_weight(wq, D, C)
+        mxq, mxe, _, _ = fb.fp8_mx_quantize_1x32(xd, colwise=False)
+        mwq, mwe, _, _ = fb.fp8_mx_quantize_1x32(wd, colwise=False)
+        mwp, mwep = fb.fp8_pack_decode_weight(mwq, D, C, we=mwe)
+        for dt in (torch.float32, torch.bfloat16):
+            assert torch.equal(fb.fp8_gemm_fprop_decode(xq, xs, wp, ws, N, D, C, out_dtype=dt),
+                               fb.fp8_gemm_fprop(xq, xs, wq, ws, N, D, C, out_dtype=dt)), ("decode", dt)
+            assert torch.equal(fb.fp8_mx_gemm_fprop_decode(mxq, mxe, mwp, mwep, N, D, C, out_dtype=dt),
+                               fb.fp8_mx_gemm_fprop(mxq, mxe, mwq, mwe, N, D, C, out_dtype=dt)), ("mx decode", dt)
