@@ -86,6 +86,7 @@ _SIGS = {
                                 _p, _i64, _p],
     "fp8_mx_gemm_wgrad": [_p, _i64, _p, _i64, _p, _i64, _p, _i64, _p, _i32, _i64, _i32, _i64, _i64, _i64, _p],
     "fp8b_e4m3_encode": [_p, _p, _i64, _p, _p],
+    "fp8b_bf16_round": [_p, _i64, _p, _p],
     "fp8b_mfma_peak": [_i32, _i64, _i64, ctypes.c_uint32, _p, _p, _p],
     "fp8b_validate_gemm": [_i32, _p, _i64, _p, _i64, _p, _i64, _p, _i64, _p, _i32, _i64, _i32,
                            _i64, _i64, _i64],
@@ -797,6 +798,18 @@ def fp8b_e4m3_encode(x, s=None, out=None):
     if out.device != x.device or out.dtype != torch.uint8 or not out.is_contiguous() or out.numel() < x.numel():
         raise ValueError("out must be a contiguous uint8 tensor with one byte per element of x")
     _call("fp8b_e4m3_encode", _ptr(x), _ptr(s), x.numel(), _ptr(out), _stream(x.device))
+    return out
+
+
+def fp8b_bf16_round(x, out=None):
+    """bf16 bits (as int16) of x rounded to nearest even by the fused
+    producers' conversion."""
+    if not isinstance(x, torch.Tensor) or not x.is_cuda or x.dtype != torch.float32 or not x.is_contiguous():
+        raise ValueError("x must be a contiguous float32 GPU tensor")
+    out = _new(x.shape, torch.int16, x.device) if out is None else out
+    if out.device != x.device or out.dtype != torch.int16 or not out.is_contiguous() or out.numel() < x.numel():
+        raise ValueError("out must be a contiguous int16 tensor with one element per element of x")
+    _call("fp8b_bf16_round", _ptr(x), x.numel(), _ptr(out), _stream(x.device))
     return out
 
 

@@ -151,7 +151,7 @@ int check_offsets(const int32_t* offsets, int64_t E) {
 
 extern "C" {
 
-int fp8b_abi_version(void) { return 3; }
+int fp8b_abi_version(void) { return 4; }
 
 const char* fp8b_status_string(int status) {
     switch (status) {
@@ -719,6 +719,12 @@ int fp8b_e4m3_encode(const float* x, const float* s, int64_t n, uint8_t* out, vo
     if (n < 0) return FP8B_ESHAPE;
     if (n > 0 && (x == nullptr || out == nullptr)) return FP8B_EINVAL;
     return hip_status(launch_encode(x, s, n, out, static_cast<hipStream_t>(stream)));
+}
+
+int fp8b_bf16_round(const float* x, int64_t n, uint16_t* out, void* stream) {
+    if (n < 0) return FP8B_ESHAPE;
+    if (n > 0 && (x == nullptr || out == nullptr)) return FP8B_EINVAL;
+    return hip_status(launch_bf16_round(x, n, out, static_cast<hipStream_t>(stream)));
 }
 
 }  // extern "C"

@@ -75,6 +75,7 @@ hipError_t launch_transpose_bf16(int src, const void* in, int64_t ldi, const voi
 
 // Elementwise codec access.
 hipError_t launch_encode(const float* x, const float* s, int64_t n, uint8_t* out, hipStream_t st);
+hipError_t launch_bf16_round(const float* x, int64_t n, uint16_t* out, hipStream_t st);
 
 // Matrix-core throughput on random register operands (peak.hip): kind 0 the
 // fp8 16x16x128 MFMA, kind 1 the bf16 16x16x32 MFMA; blocks of 256 threads,

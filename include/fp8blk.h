@@ -496,6 +496,12 @@ FP8B_API int fp8_mx_gemm_fprop_decode(const uint8_t* xq, int64_t ldxq, const uin
  * zero of x[i].  If s is NULL the divisor is 1 (plain encode of x). */
 FP8B_API int fp8b_e4m3_encode(const float* x, const float* s, int64_t n, uint8_t* out, void* stream);
 
+/* out[i] = bf16 bits of x[i] rounded to nearest, ties to even, by the
+ * conversion the fused producers use for their bf16 activations (elements
+ * taken in pairs, as the kernels pack them).  x: DEVICE fp32[n]; out: DEVICE
+ * uint16[n].  Errors: FP8B_ESHAPE (n < 0), FP8B_EINVAL (NULL), FP8B_EHIP. */
+FP8B_API int fp8b_bf16_round(const float* x, int64_t n, uint16_t* out, void* stream);
+
 /* ------------------------------------------------------------------ */
 /* Measurement aid (not part of the FP8 path)                          */
 /* ------------------------------------------------------------------ */

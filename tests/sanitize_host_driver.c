@@ -9,7 +9,7 @@
 #include "fp8blk.h"
 int main(void) {
   int bad = 0;
-  if (fp8b_abi_version() != 3) bad++;
+  if (fp8b_abi_version() != 4) bad++;
   for (int s = -1; s < 8; ++s) if (!fp8b_status_string(s)) bad++;
   int64_t shapes[][3] = {{64,24576,4096},{1,3000,4099},{37,2304,301},{0,0,0},{-1,5,5},{65,4096,512},{64,1 << 20,128}};
   for (int i = 0; i < 7; ++i) (void)fp8_gemm_dgrad_split_bytes(shapes[i][0], shapes[i][1], shapes[i][2]);

@@ -34,7 +34,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_abi_version_and_status_strings():
-    assert fb.fp8b_abi_version() == 3
+    assert fb.fp8b_abi_version() == 4
     assert fb.fp8b_status_string(0) == "ok"
     assert "shape" in fb.fp8b_status_string(2)
 

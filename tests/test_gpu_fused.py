@@ -10,7 +10,9 @@ RMSNorm's per-row r.
   a width past the register-resident limit (re-read path), rows whose
   magnitudes span 2^30, and the decode/training hidden width on sampled rows;
 * both equal the unfused path: the 1x128 quantizer run on the fused kernel's
-  own bf16 output gives the same codes and scales.
+  own bf16 output gives the same codes and scales;
+* the bf16 rounding both producers use (the packed hardware conversion) on
+  every non-NaN fp32 bit pattern.
 """
 import numpy as np
 import pytest
@@ -42,6 +44,23 @@ def gate_up_views(gate: np.ndarray, up: np.ndarray):
     H[:, cols + pad:2 * cols + pad] = up
     Hd = bf16_dev(H)
     return Hd[:, :cols], Hd[:, cols + pad:2 * cols + pad]
+
+
+def test_bf16_rounding_every_fp32_pattern():
+    """The producers round their activations to bf16 with the packed
+    conversion; on every finite and infinite fp32 value it must give the
+    oracle's nearest-even bits."""
+    banner("bf16 rounding over all 2^32 fp32 patterns")
+    step = 1 << 28
+    for lo in range(-(1 << 31), 1 << 31, step):
+        banner(f"bf16 chunk {lo:#x}")
+        x = torch.arange(lo, lo + step, dtype=torch.int32, device="cuda").view(torch.float32)
+        got = fb.fp8b_bf16_round(x).cpu().numpy().view(np.uint16)
+        xs = np.arange(lo, lo + step, dtype=np.int64).astype(np.int32).view(np.float32)
+        keep = ~np.isnan(xs)
+        want = oracle.bf16_rne(xs[keep])
+        assert_bytes_equal(got[keep], want, f"bf16 rounding chunk at {lo:#x}")
+        del x
 
 
 def check_silu(gate: np.ndarray, up: np.ndarray, what: str):
