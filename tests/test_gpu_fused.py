@@ -6,8 +6,9 @@ RMSNorm's per-row r.
   is silu(g) itself, so the whole SiLU table is checked), ragged shapes with
   gate and up as views of one gate+up matrix, and the training shape
   (8192 x 12288) on sampled rows;
-* RMSNorm: bf16 and fp32 inputs and weights, two epsilons, ragged widths,
-  a width past the register-resident limit (re-read path), rows whose
+* RMSNorm: bf16 and fp32 inputs and weights, two epsilons, ragged widths
+  for every register-resident pass count (1, 2, 4 and 8 passes of 1024
+  columns), a width past that limit (re-read path), rows whose
   magnitudes span 2^30, and the decode/training hidden width on sampled rows;
 * both equal the unfused path: the 1x128 quantizer run on the fused kernel's
   own bf16 output gives the same codes and scales;
@@ -128,7 +129,7 @@ def check_rmsnorm(x: np.ndarray, w: np.ndarray, eps: float, what: str, strided: 
     assert torch.equal(q, q2) and torch.equal(s, s2), f"{what}: fused != unfused"
 
 
-@pytest.mark.parametrize("shape", [(1, 1), (3, 300), (129, 257), (64, 4096), (5, 20000)])
+@pytest.mark.parametrize("shape", [(1, 1), (3, 300), (129, 257), (7, 1500), (64, 4096), (9, 6000), (5, 20000)])
 @pytest.mark.parametrize("kind", ["bf16", "f32"])
 def test_rmsnorm_ragged(shape, kind):
     banner(f"rmsnorm {kind} {shape}")
