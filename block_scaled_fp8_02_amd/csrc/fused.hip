@@ -449,7 +449,9 @@ __device__ __forceinline__ bool silu_fast(float gf, uint32_t& bits16) {
 //   g <= -128               |silu(g)| < 2^-170, below half the least bf16
 //                           subnormal: the result is -0
 //   zeros                   +-0
-//   the rest                (|g| < 2^-120, infinities, NaN) silu_bf16
+//   the rest                (|g| < 2^-120, infinities, NaN) the checked
+//                           binary32 estimate of silu_fast, else
+//                           silu_bf16_slow
 // ---------------------------------------------------------------------
 namespace silu_lut {
 
