@@ -22,6 +22,9 @@ int main(void) {
   if (fp8_gemm_dgrad_split_noalloc(P, 4096, P, 32, P, 4096, P, 4, NULL, 0, 512, 64, 4096, 512, NULL) != 1) bad++;
   if (fp8_dequant_gemm_wgrad(P, 128, P, 256, P, 2, 0, 16, 128, 256, P, 1, 256, 0, P, 8, NULL) != 2) bad++;
   if (fp8b_mfma_peak(5, 1, 1, 0, P, NULL, NULL) != 1) bad++;
+  if (fp8b_bf16_round(P, -1, P, NULL) != 2) bad++;
+  if (fp8b_bf16_round(NULL, 8, P, NULL) != 1) bad++;
+  if (fp8b_bf16_round(NULL, 0, NULL, NULL) != 0) bad++;
   for (int64_t d = -1; d < 40; d += 13)
     for (int part = -1; part < 3; ++part) (void)fp8_decode_pack_bytes(d, 300, part);
   if (fp8_pack_decode_weight(P, 384, P, 13, 17, 300, P, P, NULL) != 3) bad++;

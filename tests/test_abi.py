@@ -158,6 +158,11 @@ def test_fused_producers_reject_bad_arguments_on_host():
     assert L.fp8_silu_mul_quantize_1x128(X + 4, 256, W, 256, 4, 256, Q, 256, S, 2, None, 0, None) == 3
     assert L.fp8_silu_mul_quantize_1x128(X, 100, W, 256, 4, 256, Q, 256, S, 2, None, 0, None) == 2
     assert L.fp8_silu_mul_quantize_1x128(X, 256, W, 256, 0, 256, Q, 256, S, 2, None, 0, None) == 0
+    # the producers' bf16 rounding (codec access): shape and pointer checks, empty call
+    assert L.fp8b_bf16_round(X, -1, Q, None) == 2
+    assert L.fp8b_bf16_round(None, 8, Q, None) == 1
+    assert L.fp8b_bf16_round(X, 8, None, None) == 1
+    assert L.fp8b_bf16_round(None, 0, None, None) == 0
 
 
 def test_dequantized_backward_rejects_bad_arguments_on_host():
