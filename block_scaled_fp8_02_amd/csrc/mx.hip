@@ -12,8 +12,28 @@
 
 namespace fp8blk {
 
+// Codes of four values of a block with exponent k.  No clamp to +-448: k is
+// the smallest exponent with max|block| <= 448 * 2^k, or the clamp at -127,
+// below which 448 * 2^-127 exceeds every block maximum, or 127, which no
+// finite maximum reaches (448 * 2^127 > FLT_MAX); so |x * 2^-k| <= 448.
 __device__ __forceinline__ uint32_t mx_encode4(const float* v, int k) {
-    return e4m3_pack4(ldexpf(v[0], -k), ldexpf(v[1], -k), ldexpf(v[2], -k), ldexpf(v[3], -k));
+    return e4m3_pack4_q(ldexpf(v[0], -k), ldexpf(v[1], -k), ldexpf(v[2], -k), ldexpf(v[3], -k));
+}
+
+// Lane i of each 16-lane row receives lane i + n of the row (DPP row shift),
+// 0 past the row's end.
+template <int N>
+__device__ __forceinline__ uint32_t row_from_above(uint32_t v) {
+    return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x100 + N, 0xF, 0xF, true);
+}
+
+// Max over the 4-lane quad of non-negative, non-NaN values (their bit
+// patterns order as the values).
+__device__ __forceinline__ float max4_quad(float v) {
+    uint32_t u = __float_as_uint(v);
+    u = max(u, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)u, 0xB1, 0xF, 0xF, true));
+    u = max(u, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)u, 0x4E, 0xF, 0xF, true));
+    return __uint_as_float(u);
 }
 
 // Tile 128 rows x 128 cols, one per block, numbered row-tile-major; thread
@@ -56,14 +76,13 @@ __global__ __launch_bounds__(256) void k_mx_quant(const T* __restrict__ x, int64
             float m = 0.0f;
 #pragma unroll
             for (int j = 0; j < 8; ++j) m = fmaxf(m, fabsf(v[p][j]));
-            m = fmaxf(m, __shfl_xor(m, 1));
-            m = fmaxf(m, __shfl_xor(m, 2));
+            m = max4_quad(m);
             const int k = mx_exponent(m);
             const int64_t r = r0 + p;
             // the row's four E8M0 bytes of this tile (lanes cg = 0, 4, 8, 12)
             // go out as one word from lane cg = 0
             const uint32_t b = (uint32_t)(c0 < cols ? k + 127 : 127);
-            const uint32_t b1 = __shfl_down(b, 4, 16), b2 = __shfl_down(b, 8, 16), b3 = __shfl_down(b, 12, 16);
+            const uint32_t b1 = row_from_above<4>(b), b2 = row_from_above<8>(b), b3 = row_from_above<12>(b);
             if (r < rows) {
                 *reinterpret_cast<uint2*>(q + r * ldq + c0) = make_uint2(mx_encode4(&v[p][0], k), mx_encode4(&v[p][4], k));
                 if (e_words) {
@@ -105,10 +124,10 @@ __global__ __launch_bounds__(256) void k_mx_quant(const T* __restrict__ x, int64
     uint32_t lo[8], hi[8];
 #pragma unroll
     for (int p = 0; p < 8; ++p) {
-        lo[p] = e4m3_pack4(ldexpf(v[p][0], -kc[0]), ldexpf(v[p][1], -kc[1]), ldexpf(v[p][2], -kc[2]),
-                           ldexpf(v[p][3], -kc[3]));
-        hi[p] = e4m3_pack4(ldexpf(v[p][4], -kc[4]), ldexpf(v[p][5], -kc[5]), ldexpf(v[p][6], -kc[6]),
-                           ldexpf(v[p][7], -kc[7]));
+        lo[p] = e4m3_pack4_q(ldexpf(v[p][0], -kc[0]), ldexpf(v[p][1], -kc[1]), ldexpf(v[p][2], -kc[2]),
+                             ldexpf(v[p][3], -kc[3]));
+        hi[p] = e4m3_pack4_q(ldexpf(v[p][4], -kc[4]), ldexpf(v[p][5], -kc[5]), ldexpf(v[p][6], -kc[6]),
+                             ldexpf(v[p][7], -kc[7]));
     }
     uint32_t tlo[8], thi[8];
     transpose8x8(lo, hi, tlo, thi);
