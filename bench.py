@@ -471,6 +471,10 @@ def main():
             kernels[n]["tflops"] / ceil["mfma_random_operands"][fmt[n]]["tflops"], 4)
     roofline["frac_measured_peak"] = round(roofline["achieved"] / pk8, 4)
     roofline["measured_peak"] = pk8
+    # the same kernel against the measured ceiling of its scale format (MFMAs
+    # plus the FP32 promotion, no memory traffic)
+    roofline["format_ceiling"] = ceil["mfma_random_operands"][fmt[dom]]["tflops"]
+    roofline["frac_format_ceiling"] = round(roofline["achieved"] / roofline["format_ceiling"], 4)
     for n, e in bf.items():
         e["frac_measured_bf16_mfma"] = round(e["tflops"] / pk16, 4)
 
