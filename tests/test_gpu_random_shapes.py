@@ -1,5 +1,5 @@
 """A seeded sweep of random small shapes through every quantizer and the
-three GEMMs, against the oracle: codes and scales bit for bit (1x128 rows,
+three GEMMs, and the fused producers, against the oracle: codes and scales bit for bit (1x128 rows,
 128x128 weight blocks with the transposed codes, the token-axis dual
 quantizer, MXFP8 in both orientations), GEMM fp32 outputs within the row-norm
 tolerance and the fp8 accumulation bound.  The accumulation bound holds for
@@ -243,3 +243,39 @@ def test_random_shape_variants(N, D, C):
                                fb.fp8_gemm_fprop(xq, xs, wq, ws, N, D, C, out_dtype=dt)), ("decode", dt)
             assert torch.equal(fb.fp8_mx_gemm_fprop_decode(mxq, mxe, mwp, mwep, N, D, C, out_dtype=dt),
                                fb.fp8_mx_gemm_fprop(mxq, mxe, mwq, mwe, N, D, C, out_dtype=dt)), ("mx decode", dt)
+
+
+def _bits(t: torch.Tensor) -> np.ndarray:
+    """bf16 device tensor -> host uint16 bits."""
+    return t.detach().to("cpu").contiguous().view(torch.int16).numpy().view(np.uint16)
+
+
+@pytest.mark.parametrize("N,D,C", SHAPES)
+def test_random_shape_fused_producers(N, D, C):
+    """RMSNorm + 1x128 (bf16 and fp32 rows, bf16 weights) on [N x C] and
+    SiLU(gate)*up + 1x128 on [N x D] (gate and up views of one matrix):
+    codes, scales, the bf16 activation and RMSNorm's r bit for bit."""
+    banner(f"random fused producers N={N} D={D} C={C}")
+    rng = np.random.default_rng(N * 7919 + D * 104729 + C)
+    X = _data(rng, (N, C))
+    w = oracle.bf16_rne((1 + 0.1 * rng.standard_normal(C)).astype(np.float32))
+    wd = torch.from_numpy(w.view(np.int16)).view(torch.bfloat16).to("cuda")
+    for x, kind in ((oracle.bf16_rne(X), "bf16"), (X, "fp32")):
+        q, s, r, y = fb.fp8_rmsnorm_quantize_1x128(dev_strided(x), wd, 1e-6, rstd=True, y=True)
+        oq, os_, orr, oy = oracle.rmsnorm_quant_1x128(x, w, 1e-6)
+        assert_scales_equal(host(r), orr, f"rmsnorm {kind} rstd")
+        assert_bytes_equal(_bits(y), oy, f"rmsnorm {kind} y")
+        assert_bytes_equal(host(q), oq, f"rmsnorm {kind} codes")
+        assert_scales_equal(host(s), os_, f"rmsnorm {kind} scales")
+    gate = oracle.bf16_rne((2.0 * rng.standard_normal((N, D))).astype(np.float32))
+    up = oracle.bf16_rne(_data(rng, (N, D)))
+    pad = (-D) % 8
+    H = np.zeros((N, 2 * (D + pad)), np.uint16)
+    H[:, :D] = gate
+    H[:, D + pad:2 * D + pad] = up
+    Hd = torch.from_numpy(H.view(np.int16)).view(torch.bfloat16).to("cuda")
+    q, s, a = fb.fp8_silu_mul_quantize_1x128(Hd[:, :D], Hd[:, D + pad:2 * D + pad], a=True)
+    oq, os_, oa = oracle.silu_mul_quant_1x128(gate, up)
+    assert_bytes_equal(_bits(a), oa, "silu*up activation")
+    assert_bytes_equal(host(q), oq, "silu*up codes")
+    assert_scales_equal(host(s), os_, "silu*up scales")
