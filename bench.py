@@ -869,7 +869,19 @@ def other_workloads(torch, fb, wl, dev, seed):
     mx["fprop_packed"] = report(time_cold(torch, lambda: fb.fp8_mx_gemm_fprop_decode(
         q_x[0], q_x[1], mp[0], mp[1], N, D, C, y=y), flush),
         N * C * 33 // 32 + D * C * 33 // 32 + N * D * 2, 2.0 * N * D * C)
-    del mp
+
+    # the MXFP8 rollout step, as decode_1x128's step_eager: the activation's
+    # row-wise copy (all FProp needs) and the FProp on the packed weight
+    xr = fb.fp8_mx_quantize_1x32(X, colwise=False)
+
+    def mx_step():
+        fb.fp8_mx_quantize_1x32(X, colwise=False, q=xr[0], e=xr[1])
+        fb.fp8_mx_gemm_fprop_decode(xr[0], xr[1], mp[0], mp[1], N, D, C, y=y)
+    mx["quant_X_rowwise"] = report(time_cold(torch, lambda: fb.fp8_mx_quantize_1x32(
+        X, colwise=False, q=xr[0], e=xr[1]), flush), N * C * 2 + N * C + N * C // 32)
+    mx["step_eager"] = report(time_cold(torch, mx_step, flush),
+                              N * C * 2 + 2 * (N * C + N * C // 32) + D * C * 33 // 32 + N * D * 2, 2.0 * N * D * C)
+    del mp, xr
     mx["dgrad"] = report(time_cold(torch, lambda: fb.fp8_mx_gemm_dgrad(q_g[0], q_g[1], q_w[2], q_w[3], N, D, C, dx=dx),
                                    flush), N * D * 33 // 32 + D * C * 33 // 32 + N * C * 2, 2.0 * N * D * C)
     Kp = 128   # the token axis (64) padded to one 128-wide block

@@ -154,10 +154,59 @@ __global__ __launch_bounds__(256) void k_mx_quant(const T* __restrict__ x, int64
     }
 }
 
+// Row-wise copy only (no transposed codes requested): no tile, no LDS.  One
+// 16-lane slot per (row, 128-column group), 8 columns a lane, so a 32-wide
+// block is one lane quad -- the rollout's few-row activations spread over
+// rows x groups slots instead of a handful of 128-row tiles.  The same
+// arithmetic per block as the tile kernel's row-wise pass.
+template <typename T>
+__global__ __launch_bounds__(256) void k_mx_quant_rows(const T* __restrict__ x, int64_t cols, int64_t ldx,
+                                                       uint8_t* __restrict__ q, int64_t ldq,
+                                                       uint8_t* __restrict__ e, int64_t lde,
+                                                       uint32_t groups_per_row, uint32_t total) {
+    const uint32_t slot = blockIdx.x * 16u + (threadIdx.x >> 4);
+    if (slot >= total) return;                       // whole 16-lane slots exit together
+    const bool e_words = e != nullptr && reinterpret_cast<uintptr_t>(e) % 4 == 0 && lde % 4 == 0;
+    const uint32_t row = slot / groups_per_row;
+    const uint32_t g = slot - row * groups_per_row;
+    const int l16 = threadIdx.x & 15;
+    const int64_t c0 = (int64_t)g * 128 + 8 * l16;
+    float v[8];
+    load8(x + (int64_t)row * ldx + c0, clamp_valid(cols - c0), v);
+    float m = 0.0f;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) m = fmaxf(m, fabsf(v[j]));
+    m = max4_quad(m);
+    const int k = mx_exponent(m);
+    const uint32_t b = (uint32_t)(c0 < cols ? k + 127 : 127);
+    const uint32_t b1 = row_from_above<4>(b), b2 = row_from_above<8>(b), b3 = row_from_above<12>(b);
+    *reinterpret_cast<uint2*>(q + (int64_t)row * ldq + c0) = make_uint2(mx_encode4(&v[0], k), mx_encode4(&v[4], k));
+    if (e == nullptr) return;
+    if (e_words) {
+        if (l16 == 0)
+            *reinterpret_cast<uint32_t*>(e + (int64_t)row * lde + 4 * (int64_t)g) = b | (b1 << 8) | (b2 << 16) | (b3 << 24);
+    } else if ((l16 & 3) == 0) {
+        e[(int64_t)row * lde + c0 / 32] = (uint8_t)b;
+    }
+}
+
 hipError_t launch_mx_quant(const void* x, bool in_bf16, int64_t rows, int64_t cols, int64_t ldx,
                            uint8_t* q, int64_t ldq, uint8_t* e, int64_t lde,
                            uint8_t* qT, int64_t ldqT, uint8_t* eT, int64_t ldeT, hipStream_t st) {
     if (rows == 0 || cols == 0) return hipSuccess;
+    if (qT == nullptr) {
+        if (q == nullptr) return hipSuccess;
+        const int64_t gpr = (cols + 127) / 128, total = rows * gpr;
+        if (total > 0xFFFFFFF0ll) return hipErrorInvalidValue;
+        const dim3 grid((unsigned)((total + 15) / 16));
+        if (in_bf16)
+            k_mx_quant_rows<uint16_t><<<grid, 256, 0, st>>>(static_cast<const uint16_t*>(x), cols, ldx, q, ldq, e, lde,
+                                                            (uint32_t)gpr, (uint32_t)total);
+        else
+            k_mx_quant_rows<float><<<grid, 256, 0, st>>>(static_cast<const float*>(x), cols, ldx, q, ldq, e, lde,
+                                                         (uint32_t)gpr, (uint32_t)total);
+        return hipGetLastError();
+    }
     const int64_t rt = (rows + 127) / 128, ct = (cols + 127) / 128;
     if (rt * ct > 0x7FFFFFFF) return hipErrorInvalidValue;
     const dim3 grid((unsigned)(rt * ct));

@@ -34,6 +34,34 @@ def test_mx_quant_ragged(shape):
     check_mx_quant(wl.f32_to_bf16_bits(x))
 
 
+@pytest.mark.parametrize("shape", [(1, 1), (3, 300), (129, 257), (64, 4096), (300, 33), (2, 24576)])
+def test_mx_quant_rowwise_only(shape):
+    """The row-wise copy alone (the rollout's activation: no transposed
+    codes) runs a kernel of its own; its codes and E8M0 bytes equal the
+    oracle's and the two-orientation kernel's, with 4-byte-aligned scale rows
+    (word stores) and with odd ones (byte stores)."""
+    banner(f"mx quant row-wise only {shape}")
+    rows, cols = shape
+    rng = np.random.default_rng(rows * 31 + cols)
+    x = (rng.standard_normal(shape) * np.exp(rng.uniform(-20, 20, shape))).astype(np.float32)
+    x[0, :min(32, cols)] = 0.0
+    for xin in (x, wl.f32_to_bf16_bits(x)):
+        xd = dev_strided(xin)
+        q, e, qT, eT = fb.fp8_mx_quantize_1x32(xd, colwise=False)
+        assert qT is None and eT is None
+        oq, oe = oracle.mx_quant_rows(xin)
+        assert_bytes_equal(host(q), oq, "mx row-wise-only codes")
+        assert_bytes_equal(host(e), oe, "mx row-wise-only scales")
+        q2, e2, _, _ = fb.fp8_mx_quantize_1x32(xd)
+        assert torch.equal(q, q2) and torch.equal(e, e2), "row-wise-only != two-orientation row-wise copy"
+        kb = -(-cols // 128) * 4
+        q3 = torch.empty((rows, -(-cols // 128) * 128), dtype=torch.uint8, device="cuda")
+        e3 = torch.empty((rows, kb + 1), dtype=torch.uint8, device="cuda")[:, :kb]
+        fb.fp8_mx_quantize_1x32(xd, colwise=False, q=q3, e=e3)
+        assert_bytes_equal(host(q3), oq, "mx row-wise-only codes (odd scale stride)")
+        assert_bytes_equal(host(e3), oe, "mx row-wise-only scales (odd scale stride)")
+
+
 @pytest.mark.parametrize("shape", [(129, 300), (64, 4096)])
 def test_mx_quant_odd_scale_strides(shape):
     """E8M0 rows whose stride is not a multiple of 4 bytes: the quantizer
