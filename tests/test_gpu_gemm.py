@@ -555,3 +555,65 @@ def test_moe_grouped_edge_segments():
         check_f32(y[a:b], ry, my, f"edge e{e} fprop")
         check_f32(dx[a:b], rdx, mdx, f"edge e{e} dgrad")
         check_f32(dw[e], rdw, mdw, f"edge e{e} wgrad")
+
+
+def _wgrad_grouped_both_outputs(gqT, gsT, xqT, xsT, offs_d, R, Dn, C):
+    """The grouped WGrad twice: bf16 output (staged through the LDS at each
+    expert boundary) and fp32 output (stored from the registers)."""
+    bf = fb.fp8_gemm_wgrad_grouped(gqT, gsT, xqT, xsT, offs_d, R, Dn, C)
+    f32 = fb.fp8_gemm_wgrad_grouped(gqT, gsT, xqT, xsT, offs_d, R, Dn, C, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    return bf, f32
+
+
+def test_moe_wgrad_bf16_matches_fp32_path(moe_full):
+    """Both MoE weight gradients at full size: the bf16 result is the fp32
+    result rounded to nearest-even, bit for bit (the arithmetic per output
+    is the same; only the way the tile leaves differs)."""
+    w, _ = moe_full
+    offs = w["offsets"]
+    E, I2, H = w["W_gu"].shape
+    I = w["inter"]
+    R = int(offs[-1])
+    offs_d = dev(offs.astype(np.int32))
+    for name, g, x, Dn, C in (("gu", w["dH"], w["X_perm"], I2, H), ("d", w["dY_d"], w["A"], H, I)):
+        banner(f"moe {name} wgrad: bf16 output against fp32 output")
+        gqT, gsT, _, _ = fb.fp8_quantize_transposed_grouped(dev(g), offs_d, rowwise=True)
+        xqT, xsT, _, _ = fb.fp8_quantize_transposed_grouped(dev(x), offs_d, rowwise=True)
+        bf, f32 = _wgrad_grouped_both_outputs(gqT, gsT, xqT, xsT, offs_d, R, Dn, C)
+        assert torch.equal(bf.view(torch.int16), f32.to(torch.bfloat16).view(torch.int16)), name
+        del bf, f32
+
+
+@pytest.mark.parametrize("seed,E,Dn,C", [(3, 200, 1024, 1024), (4, 61, 256, 768), (5, 9, 512, 256)])
+def test_moe_wgrad_many_experts_per_block(seed, E, Dn, C):
+    """Full-tile grouped WGrads with several experts per block, empty
+    experts, one-row experts and experts past a 128-row boundary: bf16
+    output equal to the fp32 output rounded, bit for bit, and the fp32
+    output within the accumulation bound of the oracle on sampled experts."""
+    banner(f"grouped wgrad, many experts per block: seed {seed} E {E} {Dn}x{C}")
+    rng = np.random.default_rng(seed)
+    counts = rng.integers(0, 300, size=E)
+    counts[rng.choice(E, size=max(1, E // 6), replace=False)] = 0
+    counts[rng.choice(E, size=max(1, E // 8), replace=False)] = 1
+    offs = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
+    R = int(offs[-1])
+    X = rng.standard_normal((R, C)).astype(np.float32)
+    dY = (rng.standard_normal((R, Dn)) * 1e-3).astype(np.float32)
+    offs_d = dev(offs)
+    xqT, xsT, _, _ = fb.fp8_quantize_transposed_grouped(dev(X), offs_d, rowwise=True)
+    gqT, gsT, _, _ = fb.fp8_quantize_transposed_grouped(dev(dY), offs_d, rowwise=True)
+    bf, f32 = _wgrad_grouped_both_outputs(gqT, gsT, xqT, xsT, offs_d, R, Dn, C)
+    assert torch.equal(bf.view(torch.int16), f32.to(torch.bfloat16).view(torch.int16))
+    dw = host(f32)
+    for e in sorted(set(rng.choice(E, size=4, replace=False).tolist()) | {int(np.argmax(counts))}):
+        a, b = int(offs[e]), int(offs[e + 1])
+        if b == a:
+            assert np.all(dw[e] == 0), f"empty expert {e}"
+            continue
+        gq, gs = oracle.quant_colwise(dY[a:b])
+        xq, xs = oracle.quant_colwise(X[a:b])
+        ref = oracle.wgrad(gq, gs, xq, xs, b - a)
+        mag = oracle.matmul_f64(np.abs(oracle.deq_rowgroups(gq, gs, b - a)),
+                                np.abs(oracle.deq_rowgroups(xq, xs, b - a)).T)
+        check_f32(dw[e], ref, mag, f"grouped wgrad e{e} ({b - a} rows)")
