@@ -557,6 +557,44 @@ def test_moe_grouped_edge_segments():
         check_f32(dw[e], rdw, mdw, f"edge e{e} wgrad")
 
 
+def test_moe_grouped_tail_boundaries():
+    """Row-grouped FProp and DGrad run an expert's whole 256-row tiles in one
+    launch and a remainder of at most 64 rows in a second one: experts ending
+    0, 1, 63, 64 and 65 rows past a whole tile, experts of fewer than 64 rows,
+    and empty ones, each against the oracle."""
+    banner("grouped GEMMs: remainders around the 64-row split")
+    rng = np.random.default_rng(12)
+    counts = np.array([64, 65, 256, 257, 320, 321, 0, 63, 576, 577, 1, 128, 0, 319], dtype=np.int64)
+    offs = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
+    E, R, H, Dn = len(counts), int(offs[-1]), 384, 384
+    X = rng.standard_normal((R, H)).astype(np.float32)
+    dY = (rng.standard_normal((R, Dn)) * 1e-3).astype(np.float32)
+    Ws = (rng.standard_normal((E, Dn, H)) * 0.02).astype(np.float32)
+    offs_d = dev(offs)
+    wq, ws, wqT = fb.fp8_quantize_weight_128x128(dev(Ws.reshape(E * Dn, H)))
+    _, _, xq, xs = fb.fp8_quantize_transposed_grouped(dev(X), offs_d, rowwise=True)
+    _, _, gq, gs = fb.fp8_quantize_transposed_grouped(dev(dY), offs_d, rowwise=True)
+    sw = (Dn // 128) * ws.stride(0)
+    y32 = fb.fp8_gemm_fprop_grouped(xq, xs, wq, Dn * wq.stride(0), ws, sw, offs_d, R, Dn, H,
+                                    out_dtype=torch.float32)
+    dx32 = fb.fp8_gemm_dgrad_grouped(gq, gs, wqT, Dn, ws, sw, offs_d, R, Dn, H, out_dtype=torch.float32)
+    ybf = fb.fp8_gemm_fprop_grouped(xq, xs, wq, Dn * wq.stride(0), ws, sw, offs_d, R, Dn, H)
+    dxbf = fb.fp8_gemm_dgrad_grouped(gq, gs, wqT, Dn, ws, sw, offs_d, R, Dn, H)
+    torch.cuda.synchronize()
+    # the bf16 outputs (staged epilogue) are the fp32 outputs (direct stores) rounded
+    assert torch.equal(ybf.view(torch.int16), y32.to(torch.bfloat16).view(torch.int16))
+    assert torch.equal(dxbf.view(torch.int16), dx32.to(torch.bfloat16).view(torch.int16))
+    y, dx = host(y32), host(dx32)
+    for e in range(E):
+        a, b = int(offs[e]), int(offs[e + 1])
+        if b == a:
+            continue
+        ry, rdx, _ = oracle_layer(X[a:b], Ws[e], dY[a:b])
+        my, mdx, _ = abs_products(X[a:b], Ws[e], dY[a:b])
+        check_f32(y[a:b], ry, my, f"tail e{e} ({b - a} rows) fprop")
+        check_f32(dx[a:b], rdx, mdx, f"tail e{e} ({b - a} rows) dgrad")
+
+
 def _wgrad_grouped_both_outputs(gqT, gsT, xqT, xsT, offs_d, R, Dn, C):
     """The grouped WGrad twice: bf16 output (staged through the LDS at each
     expert boundary) and fp32 output (stored from the registers)."""
