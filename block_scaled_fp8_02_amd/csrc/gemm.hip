@@ -51,7 +51,7 @@ constexpr int MAX_EPB = 64;
 // BI x BJ block tile, NW waves, wave tile (16*TI) x (16*TJ), NS LDS stages,
 // GM the grouping (a template argument, so that the dense and row-grouped
 // instances carry none of the expert-boundary code of GROUP_K).
-template <int BI, int BJ, int TI, int TJ, int NW, int SM, int NS, int GM>
+template <int BI, int BJ, int TI, int TJ, int NW, int SM, int NS, int GM, bool PST = false>
 __global__ __launch_bounds__(64 * NW, 1) void k_gemm(GemmArgs g) {
     constexpr int NT = 64 * NW;
     constexpr int WI = 16 * TI, WJ = 16 * TJ;
@@ -67,6 +67,14 @@ __global__ __launch_bounds__(64 * NW, 1) void k_gemm(GemmArgs g) {
     // at the end of a K step the NS-2 newest stages may still be in flight
     constexpr int INFLIGHT = (NS - 2) * (NCH + NSL);
     static_assert(INFLIGHT <= 63, "vmcnt holds at most 63");
+    // PST: a block walks tiles blockIdx.x, blockIdx.x + gridDim.x, ... (one
+    // block per compute unit; launched for contractions of a few K blocks,
+    // whose tiles are mostly output write).  The last K step of a tile copies
+    // the next tile's first K block into the idle stage and the finished tile
+    // leaves through the other stage, so the next tile's loads are in flight
+    // while this one's stores drain.  Per-output arithmetic and K order are
+    // those of the one-tile launch.
+    constexpr bool PERSIST = PST && GM == GROUP_NONE && BI == 256 && BJ == 256;
     // the bf16 output tile fits in the stage buffers for the staged epilogue
     constexpr bool STAGED_OUT = BI * BJ * 2 <= NS * STAGE;
 
@@ -89,6 +97,9 @@ __global__ __launch_bounds__(64 * NW, 1) void k_gemm(GemmArgs g) {
     const size_t sq_elem = SM == SCALE_MX ? 1 : 4;
     const size_t o_elem = g.out_f32 ? 4 : 2;
     const int64_t nbj = (g.Nn + BJ - 1) / BJ;
+    const int64_t nbi = (g.M + BI - 1) / BI;                        // dense forms
+    const int64_t ntiles = nbi * nbj;
+    int64_t vt = blockIdx.x;                                        // PERSIST: current tile
     int64_t i0, ihi, j0, kbase = 0, KB = (g.K + 127) / 128;
     int64_t e_first = 0, e_end = 1;                                 // GROUP_K: the block's experts
     if (GM == GROUP_ROWS) {
@@ -109,9 +120,8 @@ __global__ __launch_bounds__(64 * NW, 1) void k_gemm(GemmArgs g) {
         Q += e * g.q_estride;
         sQ += e * g.sq_estride * sq_elem;
     } else {
-        const int64_t nbi = (g.M + BI - 1) / BI;
         int64_t ti, tj;
-        grouped_tile(xcd_remap(blockIdx.x, nbi * nbj), nbi, nbj, 4, ti, tj);
+        grouped_tile(xcd_remap(blockIdx.x, ntiles), nbi, nbj, 4, ti, tj);
         i0 = ti * BI;
         ihi = i0 + BI < g.M ? i0 + BI : g.M;
         j0 = tj * BJ;
@@ -152,7 +162,7 @@ __global__ __launch_bounds__(64 * NW, 1) void k_gemm(GemmArgs g) {
             O += (int64_t)blockIdx.y * g.o_estride * (int64_t)o_elem;
         }
     }
-    const int64_t jhi = j0 + BJ < g.Nn ? j0 + BJ : g.Nn;
+    int64_t jhi = j0 + BJ < g.Nn ? j0 + BJ : g.Nn;
 
     // ---------------------------------------------------- DMA addressing
     // Chunk q = c*NT + tid of a stage lands at LDS byte 16*q: tile row q/8,
@@ -162,20 +172,9 @@ __global__ __launch_bounds__(64 * NW, 1) void k_gemm(GemmArgs g) {
     // clamped to its last row (they are computed but never stored).
     constexpr int NCP = BI * 8 / NT;
     static_assert(NCP * NT == BI * 8, "P rows must fill whole DMA rounds");
-    const uint8_t* pbase = g.P + i0 * g.ldp + kbase * 128;
-    const uint8_t* qbase = Q + j0 * g.ldq + kbase * 128;
+    const uint8_t* pbase;
+    const uint8_t* qbase;
     uint32_t soff[NCH];
-#pragma unroll
-    for (int c = 0; c < NCH; ++c) {
-        const int q = c * NT + tid, row = q >> 3, lch = (q & 7) ^ (row & 7);
-        if (c < NCP) {
-            const int64_t r = row < ihi - i0 ? row : ihi - i0 - 1;
-            soff[c] = (uint32_t)(r * g.ldp + lch * 16);
-        } else {
-            const int64_t r = row - BI < jhi - j0 ? row - BI : jhi - j0 - 1;
-            soff[c] = (uint32_t)(r * g.ldq + lch * 16);
-        }
-    }
 
     // ---------------------------------------------------- scale loader
     // Tile row t = s*NT + tid (s < NSL) has its scale word fetched by this
@@ -186,26 +185,54 @@ __global__ __launch_bounds__(64 * NW, 1) void k_gemm(GemmArgs g) {
     const char* sbase[NSL];                                         // wave-uniform, at K block 0
     int64_t sstep[NSL];                                             // bytes per K block
     uint32_t soffs[NSL];                                            // per lane
-#pragma unroll
-    for (int sl = 0; sl < NSL; ++sl) {
-        const int t = sl * NT + tid;
-        if (sl * NT + wave * 64 < BI) {                             // the wave holds P rows
-            int64_t r = i0 + t;
-            r = r < ihi ? r : ihi - 1;
-            sbase[sl] = static_cast<const char*>(g.sP) + (i0 * g.ldsp + (SM == SCALE_MX ? kbase * 4 : kbase)) * sq_elem;
-            soffs[sl] = (uint32_t)((r - i0) * g.ldsp * sq_elem);
-            sstep[sl] = 4;
-        } else {
-            int64_t r = j0 + (t < BI + BJ ? t - BI : 0);
-            r = r < jhi ? r : jhi - 1;
-            const int64_t rr = SM == SCALE_Q_BLOCK ? r / 128 : r;
-            const int64_t rr0 = SM == SCALE_Q_BLOCK ? j0 / 128 : j0;
-            sbase[sl] = sQ + (rr0 * g.sq_rs + (SM == SCALE_MX ? kbase * 4 : kbase * g.sq_ks)) * sq_elem;
-            soffs[sl] = (uint32_t)((rr - rr0) * g.sq_rs * sq_elem);
-            sstep[sl] = SM == SCALE_MX ? 4 : 4 * g.sq_ks;
-        }
-    }
     static_assert(BI % 64 == 0, "P and Q scale rows must not share a wave");
+    // wave-uniform scale base of slot sl for the tile at (i0_, j0_)
+    auto sbase_of = [&](int64_t i0_, int64_t j0_, int sl) -> const char* {
+        if (sl * NT + wave * 64 < BI)                               // the wave holds P rows
+            return static_cast<const char*>(g.sP) + (i0_ * g.ldsp + (SM == SCALE_MX ? kbase * 4 : kbase)) * sq_elem;
+        const int64_t rr0 = SM == SCALE_Q_BLOCK ? j0_ / 128 : j0_;
+        return sQ + (rr0 * g.sq_rs + (SM == SCALE_MX ? kbase * 4 : kbase * g.sq_ks)) * sq_elem;
+    };
+    // copy addresses of the current tile (i0, ihi, j0, jhi, kbase)
+    auto set_addr = [&]() {
+        // an opaque copy of the thread index keeps the compiler from hoisting
+        // per-lane terms out of the tile loop (live across the K loop, they
+        // would cost registers there)
+        int tx = tid;
+        asm volatile("" : "+v"(tx));
+        pbase = g.P + i0 * g.ldp + kbase * 128;
+        qbase = Q + j0 * g.ldq + kbase * 128;
+#pragma unroll
+        for (int c = 0; c < NCH; ++c) {
+            const int q = c * NT + tx, row = q >> 3, lch = (q & 7) ^ (row & 7);
+            if (c < NCP) {
+                const int64_t r = row < ihi - i0 ? row : ihi - i0 - 1;
+                soff[c] = (uint32_t)(r * g.ldp + lch * 16);
+            } else {
+                const int64_t r = row - BI < jhi - j0 ? row - BI : jhi - j0 - 1;
+                soff[c] = (uint32_t)(r * g.ldq + lch * 16);
+            }
+        }
+#pragma unroll
+        for (int sl = 0; sl < NSL; ++sl) {
+            const int t = sl * NT + tx;
+            sbase[sl] = sbase_of(i0, j0, sl);
+            if (sl * NT + wave * 64 < BI) {
+                int64_t r = i0 + t;
+                r = r < ihi ? r : ihi - 1;
+                soffs[sl] = (uint32_t)((r - i0) * g.ldsp * sq_elem);
+                sstep[sl] = 4;
+            } else {
+                int64_t r = j0 + (t < BI + BJ ? t - BI : 0);
+                r = r < jhi ? r : jhi - 1;
+                const int64_t rr = SM == SCALE_Q_BLOCK ? r / 128 : r;
+                const int64_t rr0 = SM == SCALE_Q_BLOCK ? j0 / 128 : j0;
+                soffs[sl] = (uint32_t)((rr - rr0) * g.sq_rs * sq_elem);
+                sstep[sl] = SM == SCALE_MX ? 4 : 4 * g.sq_ks;
+            }
+        }
+    };
+    set_addr();
 
     // global_load_lds_dwordx4 writes lane l's 16 bytes to LDS at m0 + 16*l
     // (global_load_lds_dword: 4 bytes at m0 + 4*l).  Both are issued from
@@ -256,24 +283,27 @@ __global__ __launch_bounds__(64 * NW, 1) void k_gemm(GemmArgs g) {
 #pragma unroll
         for (int b = 0; b < TI; ++b) acc[a][b] = v4f{0.f, 0.f, 0.f, 0.f};
 
-    if (KB > 0) {
-        // stages 0 .. NS-2 hold K blocks 0 .. NS-2 (the last block repeated
-        // where there are fewer): every thread issues the same sequence
+    auto prologue = [&]() {
+        if (KB > 0) {
+            // stages 0 .. NS-2 hold K blocks 0 .. NS-2 (the last block repeated
+            // where there are fewer): every thread issues the same sequence
 #pragma unroll
-        for (int st = 0; st < NS - 1; ++st) {
-            const int64_t kk = st < KB ? st : KB - 1;
-            FP8B_DMA_PART(kk, st, 0, NCH);
-            FP8B_DMA_SCALE(kk, st);
+            for (int st = 0; st < NS - 1; ++st) {
+                const int64_t kk = st < KB ? st : KB - 1;
+                FP8B_DMA_PART(kk, st, 0, NCH);
+                FP8B_DMA_SCALE(kk, st);
+            }
+            __builtin_amdgcn_s_waitcnt(vmcnt_imm(INFLIGHT));
         }
-        __builtin_amdgcn_s_waitcnt(vmcnt_imm(INFLIGHT));
-    }
-    __syncthreads();
+        __syncthreads();
+    };
+    prologue();
 
     const int prow_l = wi * WI + (lane & 15);                        // tile row of this lane's first P fragment
     const int qrow_l = BI + wj * WJ;                                 // tile row of this wave's first Q row
     // Direct epilogue: lane stores its 4 consecutive outputs of one row.
-    const int64_t jw = j0 + wj * WJ;
     auto store_direct = [&](char* Ob) {
+        const int64_t jw = j0 + wj * WJ;
         // an opaque copy of the lane index keeps the compiler from hoisting
         // these addresses out of the expert loop (they would stay live
         // across the K loop and push its registers into scratch)
@@ -384,6 +414,7 @@ __global__ __launch_bounds__(64 * NW, 1) void k_gemm(GemmArgs g) {
     // rows of one staged piece that fit in a single stage (whole waves)
     constexpr int RH = (STAGE / (BJ * 2)) / WI * WI;
     constexpr bool STAGED_PIECES = RH >= WI && BI % (RH > 0 ? RH : 1) == 0;
+    static_assert(!PERSIST || (NS == 2 && STAGED_PIECES), "the persistent epilogue uses one of two stages");
 
     const FragOff pfo = frag_off(prow_l, lane);                      // this lane's P fragment row
     const FragOff qfo = frag_off(qrow_l + (lane & 15), lane);        // and Q fragment row
@@ -391,6 +422,43 @@ __global__ __launch_bounds__(64 * NW, 1) void k_gemm(GemmArgs g) {
     int buf = 0;                                                     // stage of K block kb
     int nbuf = NS - 1;                                               // stage that receives block kb + NS - 1
     int64_t ecur = e_first;                                          // expert whose K blocks run (GROUP_K)
+    for (;;) {                                                       // tiles: one pass unless PERSIST
+    // PERSIST: the block's next tile, and whether its first K block is copied
+    // during this tile's last K step (both tiles whole, so that the per-lane
+    // copy offsets are the same; otherwise the next tile fills its pipeline
+    // after the epilogue, as a fresh launch would)
+    bool pf = false;
+    const uint8_t* pbase_n = pbase;
+    const uint8_t* qbase_n = qbase;
+    const char* sbase_n[NSL];
+#pragma unroll
+    for (int sl = 0; sl < NSL; ++sl) sbase_n[sl] = sbase[sl];
+    if constexpr (PERSIST) {
+        const int64_t vn = vt + (int64_t)gridDim.x;
+        if (vn < ntiles) {
+            int64_t ti, tj;
+            grouped_tile(xcd_remap(vn, ntiles), nbi, nbj, 4, ti, tj);
+            const int64_t i0n = ti * BI, j0n = tj * BJ;
+            pf = KB > 0 && ihi - i0 == BI && jhi - j0 == BJ && i0n + BI <= g.M && j0n + BJ <= g.Nn;
+            pbase_n = g.P + i0n * g.ldp;
+            qbase_n = Q + j0n * g.ldq;
+#pragma unroll
+            for (int sl = 0; sl < NSL; ++sl) sbase_n[sl] = sbase_of(i0n, j0n, sl);
+        }
+    }
+    // K block copied during step kb: kb + NS - 1, the last block again past
+    // the end (an idle stage, no branch in the loop), or with pf the next
+    // tile's block 0 in the last step
+    auto next_copy = [&](int64_t kb_) -> int64_t {
+        if (PERSIST && pf && kb_ == KB - 1) {
+            pbase = pbase_n;
+            qbase = qbase_n;
+#pragma unroll
+            for (int sl = 0; sl < NSL; ++sl) sbase[sl] = sbase_n[sl];
+            return 0;
+        }
+        return kb_ + NS - 1 < KB ? kb_ + NS - 1 : KB - 1;
+    };
     int64_t kend = GM == GROUP_K ? uniform64(ekb[0]) : KB;
     int64_t kb = 0;
     if constexpr (SM == SCALE_Q_ROW && GM != GROUP_K && TJ >= 2) {
@@ -424,7 +492,7 @@ __global__ __launch_bounds__(64 * NW, 1) void k_gemm(GemmArgs g) {
             }
         };
         for (; kb < KB; ++kb) {
-            const int64_t kn = kb + NS - 1 < KB ? kb + NS - 1 : KB - 1;
+            const int64_t kn = next_copy(kb);
             const uint8_t* base = smem + buf * STAGE;
             const uint32_t* sc = sscale[buf];
             FP8B_DMA_SCALE(kn, nbuf);
@@ -491,9 +559,7 @@ __global__ __launch_bounds__(64 * NW, 1) void k_gemm(GemmArgs g) {
     } else
     for (;;) {
     for (; kb < kend; ++kb) {
-        const int64_t kn = kb + NS - 1 < KB ? kb + NS - 1 : KB - 1;  // past the end the last block is
-                                                                     // reloaded into an idle stage:
-                                                                     // no branch in the loop
+        const int64_t kn = next_copy(kb);
         const uint8_t* base = smem + buf * STAGE;
         const uint32_t* sc = sscale[buf];
         FP8B_DMA_SCALE(kn, nbuf);
@@ -613,23 +679,54 @@ __global__ __launch_bounds__(64 * NW, 1) void k_gemm(GemmArgs g) {
     ++ecur;
     kend += uniform64(ekb[ecur - e_first]);
     }
-#undef FP8B_DMA_PART
-#undef FP8B_DMA_SCALE
-    // the tail's repeated DMAs target idle stages; let them land before the
-    // stage memory is reused or the block exits
+    // the tail's repeated DMAs target idle stages (with pf: the next tile's
+    // first block, in stage buf); let them land before the stage memory is
+    // reused or the block exits
     __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
     __syncthreads();
 
     // ---------------------------------------------------- epilogue
     if (GM == GROUP_K) O += ecur * g.o_estride * o_elem;
+    if constexpr (PERSIST) {
+        if (g.out_f32) {
+            store_direct(O);
+        } else if (pf) {                                           // stage nbuf is free, buf is taken
+            for (int r0 = 0; r0 < BI; r0 += RH) store_staged(O, smem + nbuf * STAGE, r0, RH);
+        } else {
+            store_staged(O, smem, 0, BI);                          // every stage is free
+        }
+        vt += (int64_t)gridDim.x;
+        if (vt >= ntiles) return;
+        int64_t ti, tj;
+        grouped_tile(xcd_remap(vt, ntiles), nbi, nbj, 4, ti, tj);
+        i0 = ti * BI;
+        ihi = i0 + BI < g.M ? i0 + BI : g.M;
+        j0 = tj * BJ;
+        jhi = j0 + BJ < g.Nn ? j0 + BJ : g.Nn;
+        set_addr();
+#pragma unroll
+        for (int a = 0; a < TJ; ++a)
+#pragma unroll
+            for (int b = 0; b < TI; ++b) acc[a][b] = v4f{0.f, 0.f, 0.f, 0.f};
+        if (!pf) {                                                  // fill the pipeline afresh
+            prologue();
+            buf = 0;
+            nbuf = NS - 1;
+        }
+        continue;
+    }
     if (STAGED_OUT && !g.out_f32) {
         store_staged(O, smem, 0, BI);                              // every stage is free now
         return;
     }
     store_direct(O);
+    return;
+    }
+#undef FP8B_DMA_PART
+#undef FP8B_DMA_SCALE
 }
 
-template <int BI, int BJ, int TI, int TJ, int NW, int SM, int NS, int GM>
+template <int BI, int BJ, int TI, int TJ, int NW, int SM, int NS, int GM, bool PST = false>
 static hipError_t launch_cfg(const GemmArgs& args, hipStream_t st) {
     GemmArgs a = args;
     a.epb = 1;
@@ -656,9 +753,18 @@ static hipError_t launch_cfg(const GemmArgs& args, hipStream_t st) {
         if (a.group_mode == GROUP_NONE && a.ksplit > 1) z = a.ksplit;
         if (tiles == 0 || z == 0) return hipSuccess;
         if (tiles > 0x7FFFFFFF || z > 65535) return hipErrorInvalidValue;
-        grid = dim3((unsigned)tiles, (unsigned)z, 1);
+        int64_t gx = tiles;
+        if constexpr (PST) {
+            // persistent: one block per compute unit, a multiple of the 8
+            // XCDs, so that block b and every tile it takes stay on XCD b % 8
+            static_assert(GM == GROUP_NONE && BI == 256 && BJ == 256, "persistent form of the dense tiles only");
+            if (a.ksplit > 1) return hipErrorInvalidValue;
+            const int64_t cus = (int64_t)device_cu_count() / 8 * 8;
+            if (cus >= 8 && gx > cus) gx = cus;
+        }
+        grid = dim3((unsigned)gx, (unsigned)z, 1);
     }
-    k_gemm<BI, BJ, TI, TJ, NW, SM, NS, GM><<<grid, 64 * NW, 0, st>>>(a);
+    k_gemm<BI, BJ, TI, TJ, NW, SM, NS, GM, PST><<<grid, 64 * NW, 0, st>>>(a);
     return hipGetLastError();
 }
 
@@ -687,7 +793,14 @@ static hipError_t launch_sm(const GemmArgs& a, hipStream_t st) {
     // 8 waves of 64 x 128.  Only the pairings the entry points use are
     // instantiated: row-grouped (MoE FProp, DGrad) with 128x128 weight
     // scales, K-grouped (MoE WGrad) with per-row scales on both sides.
-    if (a.group_mode == GROUP_NONE) return launch_cfg<256, 256, 4, 8, 8, SM, 2, GROUP_NONE>(a, st);
+    // Contractions of at most 4 K blocks (e.g. the rollout-batch WGrad, K =
+    // 64) are mostly output write: their tiles run persistently, each
+    // block's next tile loading while its last one's stores drain (K = 64
+    // WGrad of 24576 x 4096 measured in the notes of this change).
+    if (a.group_mode == GROUP_NONE) {
+        if ((a.K + 127) / 128 <= 4) return launch_cfg<256, 256, 4, 8, 8, SM, 2, GROUP_NONE, true>(a, st);
+        return launch_cfg<256, 256, 4, 8, 8, SM, 2, GROUP_NONE>(a, st);
+    }
     if constexpr (SM == SCALE_Q_BLOCK) {
         if (a.group_mode == GROUP_ROWS) return launch_cfg<256, 256, 4, 8, 8, SM, 2, GROUP_ROWS>(a, st);
     }
